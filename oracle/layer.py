@@ -1,0 +1,381 @@
+"""fp64 CPU oracle of one pre-LN GPT transformer layer, forward and backward.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no
+code with the HIP path and imports nothing from it; inputs come from the
+seeded generators in ``synth`` (which hold no arithmetic of the layer).
+
+What it computes
+----------------
+The tensor-parallel split of the pages (column-parallel Q/K/V projections
+with the input broadcast to every rank, row-parallel output projection whose
+per-rank partials are summed) reaches exactly the result of the unsharded
+layer (page "Megatron-LM 3D parallelism guide", §2.1 "Tensor parallelism").
+So the oracle is the plain definition of the unsharded pre-LN layer:
+
+    ln1 = LN(x)                          qkv = ln1 Wqkv^T + bqkv
+    ctx = softmax(q k^T / sqrt(d) + mask) v      (per head, fp64 softmax)
+    y1  = x + ctx Wo^T + bo
+    ln2 = LN(y1)      u = ln2 W1^T + b1     g = GeLU_tanh(u)
+    y   = y1 + g W2^T + b2
+
+and its backward by the chain rule.  The rank view (which slice of each
+tensor a given rank computes) is in ``rank_view``.
+
+Readings where the pages are silent (each one is listed in the design doc):
+pre-LN; LayerNorm with population variance and eps inside the square root;
+score scale 1/sqrt(head_dim); the mask keeps key j for query i iff
+j <= i and j lies in i's document; GeLU is the tanh form; Wqkv stacks
+separate Wq, Wk, Wv blocks, head n owning columns n*d .. n*d+d-1 of each;
+row-parallel biases are added once after the sum; no dropout.
+
+The parity of these functions is pinned in tests/test_oracle_pins.py against
+brute force, closed forms, library special cases (torch CPU fp64),
+invariants and central finite differences.  The pages print no worked
+numeric example, so no value is pinned to a printed one.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "to64", "linear", "layernorm", "layernorm_backward", "gelu_tanh", "gelu_tanh_grad",
+    "doc_starts", "attention_probabilities", "attention_forward", "attention_backward",
+    "layer_forward", "layer_backward", "vocab_ce_forward", "vocab_ce_backward",
+    "rank_view", "rel_frobenius",
+]
+
+GELU_C = math.sqrt(2.0 / math.pi)
+GELU_A = 0.044715
+
+
+def to64(t) -> np.ndarray:
+    """Any torch tensor / array-like -> float64 numpy array (exact for bf16/fp32)."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            return t.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(t, dtype=np.float64)
+
+
+def rel_frobenius(got, ref) -> float:
+    """||got - ref||_F / ||ref||_F (0 when both are zero)."""
+    got = to64(got)
+    ref = to64(ref)
+    num = float(np.linalg.norm((got - ref).ravel()))
+    den = float(np.linalg.norm(ref.ravel()))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den
+
+
+# ---------------------------------------------------------------- linear maps
+def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None) -> np.ndarray:
+    """y = x W^T + b with W stored [out, in] (nn.Linear convention).
+
+    The pages' ColumnParallelLinear / RowParallelLinear wrap exactly this map
+    (page "Megatron-LM: NVIDIA's large-model training framework", section
+    "Tensor parallelism" snippet).
+    """
+    y = x @ w.T
+    if b is not None:
+        y = y + b
+    return y
+
+
+# ------------------------------------------------------------------ LayerNorm
+def layernorm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float):
+    """Textbook LayerNorm over the last axis (Ba, Kiros & Hinton 2016).
+
+    mu = mean(x), var = mean((x-mu)^2) (population), xhat = (x-mu)/sqrt(var+eps),
+    out = gamma*xhat + beta.  The pages name a fused LayerNorm kernel
+    (page "Megatron-LM 3D parallelism guide", §4.2); under the column/row split
+    every rank sees the whole hidden vector, so the statistics are local.
+    Returns (out, mean[T], rstd[T]).
+    """
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    out = (x - mu) * rstd * gamma + beta
+    return out, mu[..., 0], rstd[..., 0]
+
+
+def layernorm_backward(dout, x, gamma, mean, rstd):
+    """Gradient of ``layernorm`` w.r.t. x, gamma, beta.
+
+    With xhat = (x-mu)*rstd and gh = dout*gamma, the Jacobian of the
+    normalisation gives dx = rstd*(gh - mean(gh) - xhat*mean(gh*xhat)).
+    dgamma = sum_T dout*xhat, dbeta = sum_T dout.
+    """
+    xhat = (x - mean[:, None]) * rstd[:, None]
+    gh = dout * gamma
+    dx = rstd[:, None] * (gh - gh.mean(axis=1, keepdims=True)
+                          - xhat * (gh * xhat).mean(axis=1, keepdims=True))
+    return dx, (dout * xhat).sum(axis=0), dout.sum(axis=0)
+
+
+# ----------------------------------------------------------------------- GeLU
+def gelu_tanh(u: np.ndarray) -> np.ndarray:
+    """GeLU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    return 0.5 * u * (1.0 + np.tanh(GELU_C * (u + GELU_A * u ** 3)))
+
+
+def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of ``gelu_tanh`` (product and chain rule, tanh' = 1 - tanh^2)."""
+    z = GELU_C * (u + GELU_A * u ** 3)
+    th = np.tanh(z)
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th ** 2) * GELU_C * (1.0 + 3.0 * GELU_A * u ** 2)
+
+
+# ------------------------------------------------------------------ attention
+def doc_starts(cu_seqlens, tokens: int) -> np.ndarray:
+    """For every packed token, the index of the first token of its document.
+
+    ``cu_seqlens`` holds the document boundaries [0, n0, n0+n1, ..., T].
+    A fixed-length micro-batch of b sequences of length s is the case
+    cu_seqlens = [0, s, 2s, ..., bs].
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    starts = np.empty(tokens, dtype=np.int64)
+    for a, b in zip(cu[:-1], cu[1:]):
+        starts[a:b] = a
+    return starts
+
+
+def _row_blocks(tokens: int, block: int):
+    for r0 in range(0, tokens, block):
+        yield r0, min(tokens, r0 + block)
+
+
+def _allowed(starts: np.ndarray, r0: int, r1: int, c0: int, c1: int) -> np.ndarray:
+    rows = np.arange(r0, r1)[:, None]
+    cols = np.arange(c0, c1)[None, :]
+    return (cols <= rows) & (cols >= starts[r0:r1, None])
+
+
+def attention_probabilities(q, k, heads: int, starts) -> np.ndarray:
+    """Full [heads, T, T] probability tensor (small inputs only, for pins)."""
+    T, h = q.shape
+    d = h // heads
+    allowed = _allowed(starts, 0, T, 0, T)
+    probs = np.zeros((heads, T, T))
+    for n in range(heads):
+        sl = slice(n * d, (n + 1) * d)
+        s = np.where(allowed, q[:, sl] @ k[:, sl].T / math.sqrt(d), -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        probs[n] = e / e.sum(axis=1, keepdims=True)
+    return probs
+
+
+def attention_forward(q, k, v, heads: int, starts, row_block: int = 512):
+    """Masked softmax attention per head, softmax in fp64.
+
+    Scores S = q_n k_n^T / sqrt(d); key j is kept for query i iff
+    starts[i] <= j <= i (causal within the document); P = softmax(S) row-wise
+    (row maximum subtracted); ctx_n = P v_n.  Also returns the natural-log
+    log-sum-exp of every score row, lse[n, i] = log sum_j exp(S_ij).
+
+    Query rows are processed in blocks of ``row_block`` only to bound memory;
+    keys outside [min start of the block, last row] carry weight exactly 0 and
+    are not materialised.  Softmax in full precision follows the pages'
+    attention_softmax_in_fp32 flag (page "Megatron-LM 3D parallelism guide",
+    §3.2); the head split follows §2.1 of the same page.
+    """
+    T, h = q.shape
+    d = h // heads
+    scale = 1.0 / math.sqrt(d)
+    ctx = np.zeros((T, h))
+    lse = np.zeros((heads, T))
+    for r0, r1 in _row_blocks(T, row_block):
+        c0, c1 = int(starts[r0:r1].min()), r1
+        allowed = _allowed(starts, r0, r1, c0, c1)
+        for n in range(heads):
+            sl = slice(n * d, (n + 1) * d)
+            s = np.where(allowed, (q[r0:r1, sl] @ k[c0:c1, sl].T) * scale, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            ctx[r0:r1, sl] = (e / l) @ v[c0:c1, sl]
+            lse[n, r0:r1] = (m + np.log(l))[:, 0]
+    return ctx, lse
+
+
+def attention_backward(q, k, v, dctx, heads: int, starts, row_block: int = 512):
+    """Gradient of ``attention_forward`` w.r.t. q, k, v.
+
+    With P the probabilities and dP = dctx_n v_n^T: dv_n = P^T dctx_n;
+    the softmax Jacobian gives dS_i = P_i * (dP_i - <P_i, dP_i>);
+    dq_n = dS k_n / sqrt(d), dk_n = dS^T q_n / sqrt(d).
+    """
+    T, h = q.shape
+    d = h // heads
+    scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((T, h))
+    dk = np.zeros((T, h))
+    dv = np.zeros((T, h))
+    for r0, r1 in _row_blocks(T, row_block):
+        c0, c1 = int(starts[r0:r1].min()), r1
+        allowed = _allowed(starts, r0, r1, c0, c1)
+        for n in range(heads):
+            sl = slice(n * d, (n + 1) * d)
+            s = np.where(allowed, (q[r0:r1, sl] @ k[c0:c1, sl].T) * scale, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            do = dctx[r0:r1, sl]
+            dv[c0:c1, sl] += p.T @ do
+            dp = do @ v[c0:c1, sl].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[r0:r1, sl] = (ds @ k[c0:c1, sl]) * scale
+            dk[c0:c1, sl] += (ds.T @ q[r0:r1, sl]) * scale
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------- whole layer
+def _params64(params: Dict) -> Dict[str, np.ndarray]:
+    return {k: to64(v) for k, v in params.items()
+            if k not in ("x", "dy", "targets", "cu_seqlens", "emb")}
+
+
+def layer_forward(params: Dict, x, heads: int, eps: float, starts) -> Dict[str, np.ndarray]:
+    """Forward of the unsharded pre-LN layer; returns every intermediate."""
+    p = _params64(params)
+    x = to64(x)
+    h = x.shape[1]
+    c: Dict[str, np.ndarray] = {"x": x}
+    c["ln1"], c["mu1"], c["rstd1"] = layernorm(x, p["ln1_g"], p["ln1_b"], eps)
+    wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
+    c["qkv"] = linear(c["ln1"], wqkv, p["bqkv"])
+    q, k, v = c["qkv"][:, :h], c["qkv"][:, h:2 * h], c["qkv"][:, 2 * h:]
+    c["ctx"], c["lse"] = attention_forward(q, k, v, heads, starts)
+    c["y1"] = x + linear(c["ctx"], p["wo"], p["bo"])
+    c["ln2"], c["mu2"], c["rstd2"] = layernorm(c["y1"], p["ln2_g"], p["ln2_b"], eps)
+    c["u"] = linear(c["ln2"], p["w1"], p["b1"])
+    c["g"] = gelu_tanh(c["u"])
+    c["y"] = c["y1"] + linear(c["g"], p["w2"], p["b2"])
+    return c
+
+
+def layer_backward(params: Dict, cache: Dict[str, np.ndarray], dy, heads: int,
+                   starts) -> Dict[str, np.ndarray]:
+    """Backward of ``layer_forward`` for upstream gradient dy (chain rule)."""
+    p = _params64(params)
+    dy = to64(dy)
+    c = cache
+    h = dy.shape[1]
+    gr: Dict[str, np.ndarray] = {}
+    # MLP: y = y1 + g W2^T + b2
+    gr["dw2"] = dy.T @ c["g"]
+    gr["db2"] = dy.sum(axis=0)
+    dg = dy @ p["w2"]
+    du = dg * gelu_tanh_grad(c["u"])
+    gr["du"] = du
+    gr["dw1"] = du.T @ c["ln2"]
+    gr["db1"] = du.sum(axis=0)
+    dln2 = du @ p["w1"]
+    gr["dln2"] = dln2
+    dy1_ln, gr["dln2_g"], gr["dln2_b"] = layernorm_backward(dln2, c["y1"], p["ln2_g"],
+                                                            c["mu2"], c["rstd2"])
+    dy1 = dy + dy1_ln
+    gr["dy1"] = dy1
+    # attention block: y1 = x + ctx Wo^T + bo
+    gr["dwo"] = dy1.T @ c["ctx"]
+    gr["dbo"] = dy1.sum(axis=0)
+    dctx = dy1 @ p["wo"]
+    gr["dctx"] = dctx
+    q, k, v = c["qkv"][:, :h], c["qkv"][:, h:2 * h], c["qkv"][:, 2 * h:]
+    dq, dk, dv = attention_backward(q, k, v, dctx, heads, starts)
+    dqkv = np.concatenate([dq, dk, dv], axis=1)
+    gr["dqkv"] = dqkv
+    gr["dwq"] = dq.T @ c["ln1"]
+    gr["dwk"] = dk.T @ c["ln1"]
+    gr["dwv"] = dv.T @ c["ln1"]
+    gr["dbqkv"] = dqkv.sum(axis=0)
+    wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
+    dln1 = dqkv @ wqkv
+    gr["dln1"] = dln1
+    dx_ln, gr["dln1_g"], gr["dln1_b"] = layernorm_backward(dln1, c["x"], p["ln1_g"],
+                                                           c["mu1"], c["rstd1"])
+    gr["dx"] = dy1 + dx_ln
+    return gr
+
+
+# ------------------------------------------------------- vocab-parallel head
+def vocab_ce_forward(y, emb, targets):
+    """Logits z = y E^T (E [V, h]); mean token cross-entropy.
+
+    loss = mean_t [ log sum_j exp(z_tj) - z_t,target_t ]  (row max subtracted
+    before exp).  The vocabulary split across ranks (VocabParallelEmbedding,
+    page "Megatron-LM: NVIDIA's large-model training framework", section
+    "Tensor parallelism") changes nothing in this definition.
+    Returns (loss, logits, lse[T]).
+    """
+    y = to64(y)
+    emb = to64(emb)
+    tg = np.asarray(targets, dtype=np.int64)
+    z = y @ emb.T
+    m = z.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    loss = float(np.mean(lse - z[np.arange(z.shape[0]), tg]))
+    return loss, z, lse
+
+
+def vocab_ce_backward(y, emb, targets, logits, lse):
+    """dz = (softmax(z) - onehot(target)) / T; dy = dz E; dE = dz^T y."""
+    y = to64(y)
+    emb = to64(emb)
+    tg = np.asarray(targets, dtype=np.int64)
+    T = logits.shape[0]
+    dz = np.exp(logits - lse[:, None])
+    dz[np.arange(T), tg] -= 1.0
+    dz /= T
+    return dz @ emb, dz.T @ y, dz
+
+
+# ----------------------------------------------------------------- rank view
+def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]],
+              params: Dict, heads: int, tp: int, r: int) -> Dict[str, np.ndarray]:
+    """The slices / partials of the unsharded result that rank r computes.
+
+    Column-parallel weights (Wq, Wk, Wv, W1) are split by output rows and
+    row-parallel ones (Wo, W2) by input columns (page "Megatron-LM 3D
+    parallelism guide", §2.1): rank r owns heads [r*a/t, (r+1)*a/t), hidden
+    columns [r*h/t, (r+1)*h/t) and FFN columns [r*f/t, (r+1)*f/t).  Its QKV
+    output is packed [q_r | k_r | v_r].  Its row-parallel partial is the
+    product of its input slice with its weight slice; the sum over ranks of
+    these partials is the unsharded product.
+    """
+    p = _params64(params)
+    h = p["wq"].shape[0]
+    f = p["w1"].shape[0]
+    hl, fl = h // tp, f // tp
+    hc = slice(r * hl, (r + 1) * hl)
+    fc = slice(r * fl, (r + 1) * fl)
+    qkv_cols = np.r_[r * hl:(r + 1) * hl, h + r * hl:h + (r + 1) * hl,
+                     2 * h + r * hl:2 * h + (r + 1) * hl]
+    v: Dict[str, np.ndarray] = {}
+    v["qkv"] = fwd["qkv"][:, qkv_cols]
+    v["ctx"] = fwd["ctx"][:, hc]
+    v["lse"] = fwd["lse"][r * (heads // tp):(r + 1) * (heads // tp)]
+    v["proj_partial"] = fwd["ctx"][:, hc] @ p["wo"][:, hc].T
+    v["u"] = fwd["u"][:, fc]
+    v["g"] = fwd["g"][:, fc]
+    v["fc2_partial"] = fwd["g"][:, fc] @ p["w2"][:, fc].T
+    if grads is not None:
+        wqkv_r = np.concatenate([p["wq"][hc], p["wk"][hc], p["wv"][hc]], axis=0)
+        v["du"] = grads["du"][:, fc]
+        v["dw2"] = grads["dw2"][:, fc]
+        v["dw1"] = grads["dw1"][fc]
+        v["db1"] = grads["db1"][fc]
+        v["fc1_dx_partial"] = grads["du"][:, fc] @ p["w1"][fc]
+        v["dctx"] = grads["dctx"][:, hc]
+        v["dwo"] = grads["dwo"][:, hc]
+        v["dqkv"] = grads["dqkv"][:, qkv_cols]
+        v["dwqkv"] = np.concatenate([grads["dwq"][hc], grads["dwk"][hc], grads["dwv"][hc]], axis=0)
+        v["dbqkv"] = grads["dbqkv"][qkv_cols]
+        v["qkv_dx_partial"] = grads["dqkv"][:, qkv_cols] @ wqkv_r
+    return v

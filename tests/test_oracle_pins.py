@@ -1,0 +1,318 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Brute force on tiny inputs, closed forms, library special cases (torch CPU
+fp64 used only as an independent pin), invariants of the pages' column/row
+split, causality and central finite differences.  Each test is chosen so
+that a plausible slip in the oracle (a dropped term, a wrong sign or index,
+a transposed operand) fails it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------- matmul
+@pytest.mark.parametrize("m,k,n", [(3, 5, 7), (17, 9, 13)])
+def test_linear_matches_triple_loop(m, k, n):
+    r = rng(1)
+    x, w, b = r.normal(size=(m, k)), r.normal(size=(n, k)), r.normal(size=n)
+    ref = np.zeros((m, n))
+    for i in range(m):
+        for j in range(n):
+            acc = b[j]
+            for kk in range(k):
+                acc += x[i, kk] * w[j, kk]
+            ref[i, j] = acc
+    got = oracle.linear(x, w, b)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ LayerNorm
+def test_layernorm_matches_torch_and_moments():
+    r = rng(2)
+    x = r.normal(size=(37, 96)) * 3 + 1.5
+    g, b = 1 + 0.1 * r.normal(size=96), 0.1 * r.normal(size=96)
+    got, mu, rstd = oracle.layernorm(x, g, b, 1e-5)
+    ref = F.layer_norm(torch.tensor(x), (96,), torch.tensor(g), torch.tensor(b), 1e-5).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # gamma = 1, beta = 0: each row has mean 0 and variance var/(var+eps)
+    y, mu, rstd = oracle.layernorm(x, np.ones(96), np.zeros(96), 1e-5)
+    var = x.var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-12
+    assert np.max(np.abs(y.var(axis=1) - var / (var + 1e-5))) < 1e-12
+    assert np.allclose(mu, x.mean(axis=1), atol=1e-13)
+    assert np.allclose(rstd, 1 / np.sqrt(var + 1e-5), rtol=1e-13)
+
+
+def test_layernorm_backward_finite_difference():
+    r = rng(3)
+    x = r.normal(size=(5, 24))
+    g, b = 1 + 0.1 * r.normal(size=24), 0.1 * r.normal(size=24)
+    dout = r.normal(size=(5, 24))
+    _, mu, rstd = oracle.layernorm(x, g, b, 1e-5)
+    dx, dg, db = oracle.layernorm_backward(dout, x, g, mu, rstd)
+
+    def L(x_, g_, b_):
+        return float((oracle.layernorm(x_, g_, b_, 1e-5)[0] * dout).sum())
+    eps = 1e-6
+    for grad, which in ((dx, 0), (dg, 1), (db, 2)):
+        v = r.normal(size=grad.shape)
+        args_p = [x, g, b]
+        args_m = [x, g, b]
+        args_p[which] = args_p[which] + eps * v
+        args_m[which] = args_m[which] - eps * v
+        fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+        an = float((grad * v).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+# ----------------------------------------------------------------------- GeLU
+def test_gelu_closed_forms_and_torch():
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.gelu_tanh(np.array([10.0]))[0] - 10.0) < 1e-12
+    assert abs(oracle.gelu_tanh(np.array([-10.0]))[0]) < 1e-12
+    u = np.linspace(-6, 6, 1001)
+    ref = F.gelu(torch.tensor(u), approximate="tanh").numpy()
+    assert np.max(np.abs(oracle.gelu_tanh(u) - ref)) < 1e-14
+    # derivative: central difference, and torch autograd as a second pin
+    eps = 1e-6
+    fd = (oracle.gelu_tanh(u + eps) - oracle.gelu_tanh(u - eps)) / (2 * eps)
+    assert np.max(np.abs(fd - oracle.gelu_tanh_grad(u))) < 1e-8
+    ut = torch.tensor(u, requires_grad=True)
+    F.gelu(ut, approximate="tanh").sum().backward()
+    assert np.max(np.abs(ut.grad.numpy() - oracle.gelu_tanh_grad(u))) < 1e-13
+    # GeLU'(0) = 1/2
+    assert abs(oracle.gelu_tanh_grad(np.array([0.0]))[0] - 0.5) < 1e-15
+
+
+# ------------------------------------------------------------------ attention
+def _qkv(T, heads, d, seed):
+    r = rng(seed)
+    return (r.normal(size=(T, heads * d)), r.normal(size=(T, heads * d)),
+            r.normal(size=(T, heads * d)))
+
+
+def test_attention_rows_sum_to_one_and_causal_zeros():
+    q, k, v = _qkv(19, 3, 8, 4)
+    starts = oracle.doc_starts([0, 7, 19], 19)
+    p = oracle.attention_probabilities(q, k, 3, starts)
+    assert np.max(np.abs(p.sum(axis=2) - 1.0)) < 1e-12
+    for i in range(19):
+        for j in range(19):
+            if j > i or j < starts[i]:
+                assert np.all(p[:, i, j] == 0.0)
+
+
+def test_attention_first_row_and_equal_keys():
+    T, H, d = 23, 2, 16
+    q, k, v = _qkv(T, H, d, 5)
+    starts = oracle.doc_starts([0, 10, 23], T)
+    ctx, _ = oracle.attention_forward(q, k, v, H, starts)
+    # the first token of a document only sees itself
+    for s in (0, 10):
+        assert np.array_equal(ctx[s], v[s])
+    # identical keys: uniform weights over the visible prefix
+    k_eq = np.tile(k[:1], (T, 1))
+    ctx2, _ = oracle.attention_forward(q, k_eq, v, H, starts)
+    for i in range(T):
+        ref = v[starts[i]:i + 1].mean(axis=0)
+        assert np.max(np.abs(ctx2[i] - ref)) < 1e-13
+
+
+def test_attention_matches_torch_sdpa_and_lse():
+    T, H, d = 70, 3, 32
+    q, k, v = _qkv(T, H, d, 6)
+    starts = np.zeros(T, dtype=np.int64)
+    ctx, lse = oracle.attention_forward(q, k, v, H, starts, row_block=16)
+    qt = torch.tensor(q).view(T, H, d).transpose(0, 1)
+    kt = torch.tensor(k).view(T, H, d).transpose(0, 1)
+    vt = torch.tensor(v).view(T, H, d).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    ref = ref.transpose(0, 1).reshape(T, H * d).numpy()
+    assert np.max(np.abs(ctx - ref)) < 1e-12
+    s = (qt @ kt.transpose(1, 2)) / math.sqrt(d)
+    s = s.masked_fill(torch.triu(torch.ones(T, T, dtype=torch.bool), 1), -math.inf)
+    assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+def test_attention_backward_matches_autograd_and_fd():
+    T, H, d = 29, 2, 16
+    q, k, v = _qkv(T, H, d, 7)
+    starts = oracle.doc_starts([0, 12, 29], T)
+    dctx = rng(8).normal(size=(T, H * d))
+    dq, dk, dv = oracle.attention_backward(q, k, v, dctx, H, starts, row_block=8)
+    # autograd through an explicit masked softmax in torch (library pin)
+    allowed = torch.tensor(oracle.attention_probabilities(q, k, H, starts)[0] > 0)
+    qt, kt, vt = (torch.tensor(a).view(T, H, d).transpose(0, 1).requires_grad_() for a in (q, k, v))
+    s = (qt @ kt.transpose(1, 2)) / math.sqrt(d)
+    s = s.masked_fill(~allowed, -math.inf)
+    out = torch.softmax(s, dim=-1) @ vt
+    out.transpose(0, 1).reshape(T, H * d).backward(torch.tensor(dctx))
+    for got, t in ((dq, qt), (dk, kt), (dv, vt)):
+        ref = t.grad.transpose(0, 1).reshape(T, H * d).numpy()
+        assert np.max(np.abs(got - ref)) < 1e-12
+    # central finite differences along random directions
+    def L(q_, k_, v_):
+        return float((oracle.attention_forward(q_, k_, v_, H, starts)[0] * dctx).sum())
+    eps = 1e-6
+    r = rng(9)
+    for which, grad in enumerate((dq, dk, dv)):
+        dirn = r.normal(size=grad.shape)
+        a_p, a_m = [q, k, v], [q, k, v]
+        a_p[which] = a_p[which] + eps * dirn
+        a_m[which] = a_m[which] - eps * dirn
+        fd = (L(*a_p) - L(*a_m)) / (2 * eps)
+        an = float((grad * dirn).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_varlen_equals_separate_documents():
+    T, H, d = 41, 2, 8
+    q, k, v = _qkv(T, H, d, 10)
+    cu = [0, 1, 15, 16, 41]
+    starts = oracle.doc_starts(cu, T)
+    ctx, lse = oracle.attention_forward(q, k, v, H, starts, row_block=7)
+    dctx = rng(11).normal(size=(T, H * d))
+    grads = oracle.attention_backward(q, k, v, dctx, H, starts, row_block=7)
+    for a, b in zip(cu[:-1], cu[1:]):
+        z = np.zeros(b - a, dtype=np.int64)
+        c1, l1 = oracle.attention_forward(q[a:b], k[a:b], v[a:b], H, z)
+        assert np.max(np.abs(ctx[a:b] - c1)) < 1e-13
+        assert np.max(np.abs(lse[:, a:b] - l1)) < 1e-13
+        g1 = oracle.attention_backward(q[a:b], k[a:b], v[a:b], dctx[a:b], H, z)
+        for full, part in zip(grads, g1):
+            assert np.max(np.abs(full[a:b] - part)) < 1e-12
+
+
+# --------------------------------------------------------------- whole layer
+def _tiny(seed=0, affine=True):
+    cfg = synth.CONFIGS["tiny_tp2"].replace(affine_random=affine, seed=seed)
+    data = synth.generate(cfg)
+    starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    return cfg, data, starts
+
+
+def test_layer_causality_bit_identical():
+    cfg, data, starts = _tiny()
+    y0 = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts)["y"]
+    i = 60
+    x = data["x"].clone()
+    x[i + 1:] += torch.randn(x[i + 1:].shape, generator=torch.Generator().manual_seed(5))
+    y1 = oracle.layer_forward(data, x, cfg.heads, cfg.eps, starts)["y"]
+    assert np.array_equal(y0[:i + 1], y1[:i + 1])
+    assert not np.allclose(y0[i + 1:], y1[i + 1:])
+
+
+PARAM_GRADS = [("x", "dx"), ("ln1_g", "dln1_g"), ("ln1_b", "dln1_b"), ("wq", "dwq"),
+               ("wk", "dwk"), ("wv", "dwv"), ("bqkv", "dbqkv"), ("wo", "dwo"), ("bo", "dbo"),
+               ("ln2_g", "dln2_g"), ("ln2_b", "dln2_b"), ("w1", "dw1"), ("b1", "db1"),
+               ("w2", "dw2"), ("b2", "db2")]
+
+
+def test_layer_gradients_finite_difference():
+    """Central differences of L = sum(dy * y) on the tiny config, in fp64."""
+    cfg, data, starts = _tiny()
+    p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
+    dy = p64["dy"]
+    cache = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
+    grads = oracle.layer_backward(p64, cache, dy, cfg.heads, starts)
+
+    def L(pp):
+        return float((oracle.layer_forward(pp, pp["x"], cfg.heads, cfg.eps, starts)["y"] * dy).sum())
+    r = rng(12)
+    eps = 1e-6
+    for pname, gname in PARAM_GRADS:
+        grad = grads[gname]
+        # one random direction plus one sampled single entry per tensor
+        dirs = [r.normal(size=grad.shape)]
+        e = np.zeros(grad.size)
+        e[int(np.argmax(np.abs(grad).ravel()))] = 1.0
+        dirs.append(e.reshape(grad.shape))
+        for dirn in dirs:
+            pp, pm = dict(p64), dict(p64)
+            pp[pname] = p64[pname] + eps * dirn
+            pm[pname] = p64[pname] - eps * dirn
+            fd = (L(pp) - L(pm)) / (2 * eps)
+            an = float((grad * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (pname, fd, an)
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_column_row_split_is_exact(tp):
+    """Sum over ranks of the row-parallel partials equals the unsharded product."""
+    cfg, data, starts = _tiny(seed=3)
+    p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
+    c = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
+    g = oracle.layer_backward(p64, c, p64["dy"], cfg.heads, starts)
+    views = [oracle.rank_view(c, g, p64, cfg.heads, tp, r) for r in range(tp)]
+    def tol(a):
+        return 1e-12 * max(1.0, np.max(np.abs(a)))
+    s = sum(v["proj_partial"] for v in views)
+    assert np.max(np.abs(s - c["ctx"] @ p64["wo"].T)) < tol(s)
+    s = sum(v["fc2_partial"] for v in views)
+    assert np.max(np.abs(s - c["g"] @ p64["w2"].T)) < tol(s)
+    s = sum(v["fc1_dx_partial"] for v in views)
+    assert np.max(np.abs(s - g["dln2"])) < tol(s)
+    s = sum(v["qkv_dx_partial"] for v in views)
+    assert np.max(np.abs(s - g["dln1"])) < tol(s)
+    # per-rank attention over the rank's local heads equals its slice
+    h, hl, al = cfg.hidden, cfg.hidden // tp, cfg.heads // tp
+    for r, v in enumerate(views):
+        qkv_r = v["qkv"]
+        ctx_r, lse_r = oracle.attention_forward(qkv_r[:, :hl], qkv_r[:, hl:2 * hl],
+                                                qkv_r[:, 2 * hl:], al, starts)
+        assert np.max(np.abs(ctx_r - v["ctx"])) < 1e-12
+        assert np.max(np.abs(lse_r - v["lse"])) < 1e-12
+    # concatenating rank slices restores the unsharded tensors
+    assert np.array_equal(np.concatenate([v["ctx"] for v in views], axis=1), c["ctx"])
+    assert np.array_equal(np.concatenate([v["u"] for v in views], axis=1), c["u"])
+    assert np.array_equal(np.concatenate([v["dw1"] for v in views], axis=0), g["dw1"])
+
+
+# ------------------------------------------------------------ vocab CE head
+def test_vocab_ce_matches_torch_and_fd():
+    r = rng(13)
+    T, h, V = 9, 16, 50
+    y, emb = r.normal(size=(T, h)), 0.3 * r.normal(size=(V, h))
+    tg = r.integers(0, V, size=T)
+    loss, z, lse = oracle.vocab_ce_forward(y, emb, tg)
+    ref = F.cross_entropy(torch.tensor(y) @ torch.tensor(emb).T, torch.tensor(tg)).item()
+    assert abs(loss - ref) < 1e-13
+    dy, demb, dz = oracle.vocab_ce_backward(y, emb, tg, z, lse)
+    assert np.max(np.abs(dz.sum(axis=1))) < 1e-15 * V
+    yt, et = torch.tensor(y, requires_grad=True), torch.tensor(emb, requires_grad=True)
+    F.cross_entropy(yt @ et.T, torch.tensor(tg)).backward()
+    assert np.max(np.abs(yt.grad.numpy() - dy)) < 1e-14
+    assert np.max(np.abs(et.grad.numpy() - demb)) < 1e-14
+    eps = 1e-6
+    for which, grad in ((0, dy), (1, demb)):
+        dirn = r.normal(size=grad.shape)
+        a_p, a_m = [y, emb], [y, emb]
+        a_p[which] = a_p[which] + eps * dirn
+        a_m[which] = a_m[which] - eps * dirn
+        fd = (oracle.vocab_ce_forward(*a_p, tg)[0] - oracle.vocab_ce_forward(*a_m, tg)[0]) / (2 * eps)
+        assert abs(fd - float((grad * dirn).sum())) < 1e-8
+
+
+def test_vocab_ce_zero_logits_golden():
+    """Zero logits over the pages' 131072-entry vocabulary: loss = ln V."""
+    gold = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    V = gold["vocab_size"]["value"]
+    T, h = 3, 4
+    loss, _, _ = oracle.vocab_ce_forward(np.ones((T, h)), np.zeros((V, h)), np.array([0, 7, V - 1]))
+    assert abs(loss - gold["zero_logit_cross_entropy"]["value"]) < 1e-12
+    assert abs(loss - 17 * math.log(2)) < 1e-12
