@@ -1,0 +1,265 @@
+/*
+ * mtp.h -- C ABI of libmtp: one tensor-parallel rank's shard of a pre-LN GPT
+ * transformer layer, forward and backward, on one AMD MI355X (gfx950).
+ *
+ * The method (page "Megatron-LM 3D parallelism guide", §2.1 "Tensor
+ * parallelism"): the Q/K/V projection weights are split by output columns
+ * across the t ranks of a tensor-parallel group and every rank receives the
+ * whole input ("column parallel", no exchange in forward); the attention
+ * output projection is split by input rows, so each rank produces a partial
+ * of the full output and the partials are summed ("row parallel").  The MLP
+ * uses the same column/row pair.  The problem is stated by hidden size,
+ * attention heads, TP size and rank, sequence length and micro-batch (page
+ * "Megatron-LM: NVIDIA large-model training framework", sections
+ * "Configuration example", "Launching training" and "GPT model definition").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - T = seq_len * micro_batch tokens; h hidden; a heads; d = h/a head
+ *    size; t = tp_size; h_l = h/t, a_l = a/t, f_l = ffn/t, V_l = vocab/t.
+ *  - Activations are token-major, row-major [T, features], element type
+ *    `desc->dtype` (fp32 or bf16).  Weights use the nn.Linear convention
+ *    W[out, in] (y = x W^T) in `desc->dtype`.  Weight and bias gradients are
+ *    fp32.  Statistics (LayerNorm mean/rstd, attention log-sum-exp,
+ *    cross-entropy max/sum) are fp32.
+ *  - Rank r's QKV output is [T, 3*h_l] = [q_r | k_r | v_r]; inside each
+ *    block head n (local) owns columns n*d .. n*d+d-1.  The caller packs the
+ *    rank's weight shard accordingly: Wqkv_r = [Wq rows r*h_l..; Wk rows
+ *    r*h_l..; Wv rows r*h_l..], shape [3*h_l, h].
+ *  - Every pointer argument is caller-owned device memory, 16-byte aligned,
+ *    contiguous with the documented shape, unless documented as a host
+ *    pointer.  The library allocates nothing and keeps no state between
+ *    calls; scratch memory is passed as `ws`/`ws_bytes`, sized by
+ *    mtp_workspace_size().
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and never synchronises.
+ *  - Return value: MTP_OK, or an error code.  Arguments are validated before
+ *    any device work is enqueued, so an error return means nothing was
+ *    launched, except MTP_ERR_HIP (a launch failed; earlier kernels of the
+ *    same call may have been enqueued).  No call aborts the process.
+ *  - T = 0 is valid: the call is a no-op except that non-accumulating
+ *    gradient outputs (dgamma/dbeta, dw, db) are set to zero.
+ */
+#ifndef MTP_H
+#define MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_VERSION 1
+
+enum mtp_status {
+    MTP_OK = 0,
+    MTP_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad rank, divisibility  */
+    MTP_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype, ...)  */
+    MTP_ERR_WORKSPACE = 3,    /* ws too small or NULL where needed                 */
+    MTP_ERR_HIP = 4           /* a HIP launch reported an error                    */
+};
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+
+/* Which of the layer's linear maps a call computes. */
+typedef enum {
+    MTP_QKV = 0,   /* column parallel: [T,h] -> [T,3h_l], bias [3h_l]            */
+    MTP_PROJ = 1,  /* row parallel:    [T,h_l] -> partial [T,h]                   */
+    MTP_FC1 = 2,   /* column parallel: [T,h] -> [T,f_l], GeLU-tanh applied         */
+    MTP_FC2 = 3,   /* row parallel:    [T,f_l] -> partial [T,h]                   */
+    MTP_VOCAB = 4  /* column parallel vocab head: [T,h] -> fp32 logits [T,V_l]   */
+} mtp_linear_kind;
+
+/* Operation ids for mtp_workspace_size(). */
+typedef enum {
+    MTP_OP_LAYERNORM_BWD = 0,
+    MTP_OP_COL_LINEAR_BWD = 1,
+    MTP_OP_ROW_LINEAR_BWD = 2,
+    MTP_OP_ATTN_BWD = 3,
+    MTP_OP_VOCAB_CE = 4
+} mtp_op;
+
+/*
+ * The problem statement of one shard.  Divisibility follows the pages
+ * (page "Megatron-LM 3D parallelism guide", §3.2: hidden size and head
+ * count must divide by the TP size, e.g. 12288/8 = 1536 per rank while a TP
+ * size of 5 is rejected).  Additionally d must be 64 or 128, f_l and V_l
+ * multiples of 8 (MTP_ERR_UNSUPPORTED otherwise).
+ */
+typedef struct {
+    int32_t hidden;       /* h                                                   */
+    int32_t heads;        /* a                                                   */
+    int32_t ffn;          /* f (MLP inner size, unsharded)                        */
+    int32_t vocab;        /* V (unsharded), 0 if the layer has no vocab head      */
+    int32_t tp_size;      /* t >= 1                                              */
+    int32_t tp_rank;      /* r in [0, t)                                         */
+    int32_t seq_len;      /* s >= 0                                              */
+    int32_t micro_batch;  /* b >= 1; T = b*s                                     */
+    int32_t dtype;        /* mtp_dtype of weights and activations                */
+    float ln_eps;         /* LayerNorm epsilon (> 0), e.g. 1e-5                   */
+} mtp_shard_desc;
+
+/* ---------------------------------------------------------------- LayerNorm
+ * y = gamma * (x - mean) * rstd + beta per token, mean and population
+ * variance over h, rstd = 1/sqrt(var + eps).  The pages name a fused
+ * LayerNorm kernel (page "Megatron-LM 3D parallelism guide", §4.2).  Under
+ * the column/row split each rank holds the whole [T,h] input, so the
+ * statistics are computed locally with no exchange.
+ *   x, y: [T,h] dtype.  gamma, beta: [h] dtype.  mean, rstd: [T] fp32 (out).
+ */
+int mtp_layernorm(const mtp_shard_desc* desc, const void* x, const void* gamma,
+                  const void* beta, void* y, float* mean, float* rstd, void* stream);
+
+/* LayerNorm backward.  dy: [T,h] gradient w.r.t. y; x, gamma, mean, rstd as
+ * saved by mtp_layernorm.  dres: nullable [T,h] residual-branch gradient that
+ * is added to dx (dx = dres + dLN/dx . dy).  dx: [T,h] dtype.  dgamma, dbeta:
+ * [h] fp32, overwritten, or incremented when accumulate != 0.  Needs
+ * ws_bytes >= mtp_workspace_size(desc, MTP_OP_LAYERNORM_BWD, 0).           */
+int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x,
+                      const void* gamma, const float* mean, const float* rstd,
+                      const void* dres, void* dx, float* dgamma, float* dbeta,
+                      int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------- column-parallel linear
+ * ColumnParallelLinear with the output left sharded (page "Megatron-LM:
+ * NVIDIA large-model training framework", section "Tensor parallelism":
+ * gather_output=False; page "Megatron-LM 3D parallelism guide", §2.1).
+ *   kind MTP_QKV:   x [T,h], w [3h_l,h], b [3h_l] nullable, y [T,3h_l];
+ *                   preact must be NULL.
+ *   kind MTP_FC1:   x [T,h], w [f_l,h], b [f_l] nullable; preact [T,f_l]
+ *                   receives u = x w^T + b and y [T,f_l] receives GeLU_tanh(u).
+ *   kind MTP_VOCAB: x [T,h], w = vocab shard [V_l,h], b [V_l] nullable,
+ *                   y = fp32 logits [T,V_l]; preact must be NULL.
+ */
+int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, const void* w,
+                       const void* b, void* y, void* preact, void* stream);
+
+/* Backward of the column-parallel linear map (pre-activation gradient in):
+ *   dy [T,out_l] is the gradient w.r.t. x w^T + b (for MTP_FC1: w.r.t. u,
+ *   i.e. GeLU' already applied, see mtp_row_linear_bwd); dtype for QKV and
+ *   FC1, dtype for VOCAB (the dlogits written by mtp_vocab_ce_bwd).
+ *   dx_partial [T,h] dtype (out): this rank's partial of the input gradient.
+ *     The input fed every rank, so the full gradient is the sum of all ranks'
+ *     partials (mtp_partial_sum).  Nullable (skipped).
+ *   dw [out_l,h] fp32, db [out_l] fp32 nullable: overwritten, or incremented
+ *     when accumulate != 0.
+ * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_COL_LINEAR_BWD, kind)
+ * when db != NULL.                                                           */
+int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, const void* x,
+                       const void* w, void* dx_partial, float* dw, float* db, int accumulate,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------- row-parallel linear
+ * RowParallelLinear with an already-sharded input (input_is_parallel=True,
+ * same snippet); the output is this rank's partial of the full product.  The
+ * pages sum the partials with an all-reduce; here mtp_partial_sum does it.
+ *   kind MTP_PROJ: x_local [T,h_l], w [h,h_l];  kind MTP_FC2: x_local
+ *   [T,f_l], w [h,f_l].  partial [T,h] dtype.  No bias: the row-parallel bias
+ *   is added once, after the sum (mtp_partial_sum).                          */
+int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local,
+                       const void* w, void* partial, void* stream);
+
+/* Backward of the row-parallel map.
+ *   dy [T,h] dtype: gradient w.r.t. the summed output (identical on ranks).
+ *   x_local, w: as in forward.
+ *   gelu_preact: nullable [T,f_l] (MTP_FC2 only).  When given, x_local was
+ *     GeLU_tanh(gelu_preact) and dx_local receives the gradient w.r.t. the
+ *     pre-activation, (dy w) * GeLU_tanh'(gelu_preact), ready for
+ *     mtp_col_linear_bwd(MTP_FC1).  Otherwise dx_local = dy w.
+ *   dx_local [T,in_l] dtype (out), nullable.
+ *   dw [h,in_l] fp32; db [h] fp32 nullable (the row-parallel bias belongs to
+ *     one rank: pass it on exactly one).  accumulate as above.
+ * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ROW_LINEAR_BWD, kind)
+ * when db != NULL.                                                           */
+int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy,
+                       const void* x_local, const void* w, const void* gelu_preact,
+                       void* dx_local, float* dw, float* db, int accumulate,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- attention
+ * Softmax attention over the rank's a_l local heads (the head split of page
+ * "Megatron-LM 3D parallelism guide", §2.1; softmax in fp32 as the
+ * attention_softmax_in_fp32 flag of §3.2 asks).  Per head n:
+ *   S = q_n k_n^T / sqrt(d); key j is visible to query i iff start(i) <= j <= i
+ *   where start(i) is the first token of i's sequence; P = softmax(S);
+ *   ctx_n = P v_n.
+ * Sequences: when cu_seqlens is NULL, the T tokens are micro_batch sequences
+ * of seq_len tokens each.  Otherwise cu_seqlens is a device int32 array of
+ * n_seqs+1 non-decreasing offsets [0, ..., T] of packed variable-length
+ * documents (block-diagonal causal mask); the library trusts its contents
+ * (it cannot read device memory before launch).
+ *   qkv [T,3h_l] dtype (layout above); ctx [T,h_l] dtype (out);
+ *   lse [a_l,T] fp32 (out): natural-log log-sum-exp of each score row.
+ */
+int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* lse,
+                 const int32_t* cu_seqlens, int32_t n_seqs, void* stream);
+
+/* Attention backward: given qkv, ctx and lse from mtp_attn_fwd and dctx
+ * [T,h_l], writes dqkv [T,3h_l] dtype = [dq | dk | dv] in the qkv layout.
+ * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ATTN_BWD, 0).           */
+int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
+                 const float* lse, const void* dctx, void* dqkv,
+                 const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* ------------------------------------------------------------ partial sum
+ * The sum that the pages perform with a tensor-parallel all-reduce (page
+ * "Megatron-LM 3D parallelism guide", §2.1: the row-split output projection's
+ * per-rank shards are summed into the complete output).  Here all partials
+ * are on one device:
+ *   out = sum_{i<n} partials[i] + bias + residual, accumulated in fp32 in
+ *   the fixed order i = 0..n-1, then bias, then residual.
+ * partials: HOST array of n_partials (1..16) device pointers, each [T,h]
+ * dtype.  bias [h] and residual [T,h] are nullable.  out [T,h] dtype (may
+ * alias residual or partials[i]).                                            */
+int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials,
+                    int32_t n_partials, const void* bias, const void* residual, void* out,
+                    void* stream);
+
+/* ------------------------------------------------- vocab-parallel CE head
+ * Cross-entropy over a vocabulary split across ranks (VocabParallelEmbedding,
+ * page "Megatron-LM: NVIDIA large-model training framework", section
+ * "Tensor parallelism"; vocab 131072 at seq 4096 in page "Megatron-LM /
+ * Megatron Core README digest", §5).  Rank r owns ids [r*V_l, (r+1)*V_l).
+ *
+ * Stats of one shard: for every token, m = max_j z_j, s = sum_j exp(z_j - m)
+ * over the shard's logits, and z_tgt = the target's logit if this shard owns
+ * the target id, else 0.  logits [T,V_l] fp32; targets [T] int32 global ids
+ * in [0, V) (checked on device: an out-of-range id yields NaN loss).
+ * m, s, z_tgt: [T] fp32 (out).                                               */
+int mtp_vocab_ce_stats(const mtp_shard_desc* desc, const float* logits,
+                       const int32_t* targets, float* m, float* s, float* z_tgt,
+                       void* stream);
+
+/* Combine the t shards' stats: M = max_r m_r, S = sum_r s_r exp(m_r - M),
+ * loss_t = log S + M - sum_r z_tgt_r; loss_mean = mean_t loss_t.
+ * m, s, z_tgt: HOST arrays of n_ranks device pointers ([T] fp32 each).
+ * M, S, loss: [T] fp32 (out); loss_mean: [1] fp32 (out, nullable).           */
+int mtp_vocab_ce_combine(const mtp_shard_desc* desc, const float* const* m,
+                         const float* const* s, const float* const* z_tgt, int32_t n_ranks,
+                         float* M, float* S, float* loss, float* loss_mean, void* stream);
+
+/* Gradient of dloss_scale * sum_t loss_t w.r.t. this shard's logits:
+ * dlogits = dloss_scale * (exp(z - M)/S - [j == target]).  For the mean
+ * loss pass dloss_scale = 1/T.  dlogits [T,V_l] dtype (out).               */
+int mtp_vocab_ce_bwd(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,
+                     const float* M, const float* S, float dloss_scale, void* dlogits,
+                     void* stream);
+
+/* ------------------------------------------------------------- utilities */
+/* Bytes of `ws` that operation `op` needs for this shard; `kind` selects
+ * the linear map for MTP_OP_COL_LINEAR_BWD / MTP_OP_ROW_LINEAR_BWD.
+ * Returns 0 when none is needed, and 0 for an invalid desc.                 */
+size_t mtp_workspace_size(const mtp_shard_desc* desc, int op, int kind);
+
+/* Static string for a status code. */
+const char* mtp_status_string(int status);
+
+/* MTP_VERSION of the built library. */
+int mtp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTP_H */

@@ -1,0 +1,348 @@
+// C ABI of libmtp (declared in include/mtp.h): argument validation, then
+// dispatch to the kernels.  Validation completes before anything is
+// enqueued; no entry point allocates memory or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "mtp.h"
+
+namespace {
+
+using mtp::GemmDesc;
+
+struct Shard {
+  int64_t T;
+  int h, a, d, t, r, hl, al, fl;
+  int64_t V, Vl;
+  bool bf16;
+  int esize;
+  float eps;
+};
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned(p); }
+
+int check_desc(const mtp_shard_desc* desc, Shard* s) {
+  if (!desc) return MTP_ERR_INVALID_ARG;
+  const mtp_shard_desc& d = *desc;
+  if (d.hidden <= 0 || d.heads <= 0 || d.ffn < 0 || d.vocab < 0 || d.tp_size < 1 ||
+      d.tp_rank < 0 || d.tp_rank >= d.tp_size || d.seq_len < 0 || d.micro_batch < 1)
+    return MTP_ERR_INVALID_ARG;
+  if (!(d.ln_eps > 0.0f) || !isfinite(d.ln_eps)) return MTP_ERR_INVALID_ARG;
+  if (d.dtype != MTP_F32 && d.dtype != MTP_BF16) return MTP_ERR_UNSUPPORTED;
+  if (d.hidden % d.heads != 0) return MTP_ERR_INVALID_ARG;
+  // hidden and heads must split evenly over the TP ranks; so must the FFN
+  // and the vocabulary.
+  if (d.heads % d.tp_size != 0 || d.hidden % d.tp_size != 0) return MTP_ERR_INVALID_ARG;
+  if (d.ffn % d.tp_size != 0 || d.vocab % d.tp_size != 0) return MTP_ERR_INVALID_ARG;
+  const int hd = d.hidden / d.heads;
+  if (hd != 64 && hd != 128) return MTP_ERR_UNSUPPORTED;
+  if ((d.ffn / d.tp_size) % 8 != 0 || (d.vocab / d.tp_size) % 8 != 0) return MTP_ERR_UNSUPPORTED;
+  if (d.hidden > 16384) return MTP_ERR_UNSUPPORTED;
+  const int64_t T = static_cast<int64_t>(d.seq_len) * d.micro_batch;
+  if (T > (static_cast<int64_t>(1) << 30)) return MTP_ERR_UNSUPPORTED;
+  s->T = T;
+  s->h = d.hidden; s->a = d.heads; s->d = hd; s->t = d.tp_size; s->r = d.tp_rank;
+  s->hl = d.hidden / d.tp_size; s->al = d.heads / d.tp_size; s->fl = d.ffn / d.tp_size;
+  s->V = d.vocab; s->Vl = d.vocab / d.tp_size;
+  s->bf16 = d.dtype == MTP_BF16;
+  s->esize = s->bf16 ? 2 : 4;
+  s->eps = d.ln_eps;
+  return MTP_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MTP_OK : MTP_ERR_HIP; }
+
+hipError_t gemm(const Shard& s, const GemmDesc& g, hipStream_t st) {
+  return s.bf16 ? mtp::gemm_bf16(g, st) : mtp::gemm_f32(g, st);
+}
+
+// Output width of a column-parallel kind, 0 for anything else.
+int64_t col_out(const Shard& s, int kind) {
+  switch (kind) {
+    case MTP_QKV: return 3LL * s.hl;
+    case MTP_FC1: return s.fl;
+    case MTP_VOCAB: return s.Vl;
+    default: return 0;
+  }
+}
+// Input width of a row-parallel kind, 0 for anything else.
+int64_t row_in(const Shard& s, int kind) {
+  switch (kind) {
+    case MTP_PROJ: return s.hl;
+    case MTP_FC2: return s.fl;
+    default: return 0;
+  }
+}
+
+int tile_override() { return -1; }
+
+}  // namespace
+
+extern "C" {
+
+int mtp_version(void) { return MTP_VERSION; }
+
+const char* mtp_status_string(int status) {
+  switch (status) {
+    case MTP_OK: return "MTP_OK";
+    case MTP_ERR_INVALID_ARG: return "MTP_ERR_INVALID_ARG: invalid argument";
+    case MTP_ERR_UNSUPPORTED: return "MTP_ERR_UNSUPPORTED: valid but unsupported shape or dtype";
+    case MTP_ERR_WORKSPACE: return "MTP_ERR_WORKSPACE: workspace missing or too small";
+    case MTP_ERR_HIP: return "MTP_ERR_HIP: a HIP launch failed";
+    default: return "unknown mtp status";
+  }
+}
+
+size_t mtp_workspace_size(const mtp_shard_desc* desc, int op, int kind) {
+  Shard s;
+  if (check_desc(desc, &s) != MTP_OK) return 0;
+  switch (op) {
+    case MTP_OP_LAYERNORM_BWD: return mtp::layernorm_bwd_ws_bytes(s.T, s.h);
+    case MTP_OP_COL_LINEAR_BWD: {
+      const int64_t n = col_out(s, kind);
+      return n > 0 ? mtp::column_sum_ws_bytes(s.T, n) : 0;
+    }
+    case MTP_OP_ROW_LINEAR_BWD:
+      return row_in(s, kind) > 0 ? mtp::column_sum_ws_bytes(s.T, s.h) : 0;
+    case MTP_OP_ATTN_BWD: return static_cast<size_t>(s.al) * s.T * sizeof(float);
+    default: return 0;
+  }
+}
+
+int mtp_layernorm(const mtp_shard_desc* desc, const void* x, const void* gamma, const void* beta,
+                  void* y, float* mean, float* rstd, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(beta) || !ok_ptr(y) || !ok_ptr(mean) || !ok_ptr(rstd))
+    return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::layernorm_fwd(s.bf16, x, gamma, beta, y, mean, rstd, s.T, s.h, s.eps,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x, const void* gamma,
+                      const float* mean, const float* rstd, const void* dres, void* dx,
+                      float* dgamma, float* dbeta, int accumulate, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(mean) || !ok_ptr(rstd) ||
+      !ok_opt(dres) || !ok_ptr(dx) || !ok_ptr(dgamma) || !ok_ptr(dbeta))
+    return MTP_ERR_INVALID_ARG;
+  const size_t need = mtp::layernorm_bwd_ws_bytes(s.T, s.h);
+  if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  return hip_status(mtp::layernorm_bwd(s.bf16, dy, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
+                                       accumulate != 0, s.T, s.h, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, const void* w,
+                       const void* b, void* y, void* preact, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  const int64_t n = col_out(s, kind);
+  if (n <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(x) || !ok_ptr(w) || !ok_opt(b) || !ok_ptr(y)) return MTP_ERR_INVALID_ARG;
+  if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
+  GemmDesc g{};
+  g.A = x; g.lda = s.h; g.a_kmajor = true;
+  g.B = w; g.ldb = s.h; g.b_kmajor = true;
+  g.M = static_cast<int>(s.T); g.N = static_cast<int>(n); g.K = s.h;
+  g.C = y; g.ldc = n; g.bias = b;
+  g.aux = preact; g.ld_aux = n;
+  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : kind == MTP_VOCAB ? mtp::kEpiF32 : mtp::kEpiStore;
+  g.tile = tile_override();
+  return hip_status(gemm(s, g, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, const void* x,
+                       const void* w, void* dx_partial, float* dw, float* db, int accumulate,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  const int64_t n = col_out(s, kind);
+  if (n <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(w) || !ok_opt(dx_partial) || !ok_ptr(dw) || !ok_opt(db))
+    return MTP_ERR_INVALID_ARG;
+  if (db) {
+    const size_t need = mtp::column_sum_ws_bytes(s.T, n);
+    if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  }
+  hipStream_t str = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (dx_partial) {
+    GemmDesc g{};
+    g.A = dy; g.lda = n; g.a_kmajor = true;
+    g.B = w; g.ldb = s.h; g.b_kmajor = false;
+    g.M = static_cast<int>(s.T); g.N = s.h; g.K = static_cast<int>(n);
+    g.C = dx_partial; g.ldc = s.h; g.epi = mtp::kEpiStore; g.tile = tile_override();
+    e = gemm(s, g, str);
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
+  {
+    GemmDesc g{};
+    g.A = dy; g.lda = n; g.a_kmajor = false;
+    g.B = x; g.ldb = s.h; g.b_kmajor = false;
+    g.M = static_cast<int>(n); g.N = s.h; g.K = static_cast<int>(s.T);
+    g.C = dw; g.ldc = s.h; g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
+    g.tile = tile_override();
+    e = gemm(s, g, str);
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
+  if (db) e = mtp::column_sum(s.bf16, dy, s.T, n, db, accumulate != 0, ws, str);
+  return hip_status(e);
+}
+
+int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local, const void* w,
+                       void* partial, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  const int64_t k = row_in(s, kind);
+  if (k <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(x_local) || !ok_ptr(w) || !ok_ptr(partial)) return MTP_ERR_INVALID_ARG;
+  GemmDesc g{};
+  g.A = x_local; g.lda = k; g.a_kmajor = true;
+  g.B = w; g.ldb = k; g.b_kmajor = true;
+  g.M = static_cast<int>(s.T); g.N = s.h; g.K = static_cast<int>(k);
+  g.C = partial; g.ldc = s.h; g.epi = mtp::kEpiStore; g.tile = tile_override();
+  return hip_status(gemm(s, g, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, const void* x_local,
+                       const void* w, const void* gelu_preact, void* dx_local, float* dw,
+                       float* db, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  const int64_t k = row_in(s, kind);
+  if (k <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(dy) || !ok_ptr(x_local) || !ok_ptr(w) || !ok_opt(dx_local) || !ok_ptr(dw) ||
+      !ok_opt(db) || !ok_opt(gelu_preact))
+    return MTP_ERR_INVALID_ARG;
+  if (gelu_preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
+  if (db) {
+    const size_t need = mtp::column_sum_ws_bytes(s.T, s.h);
+    if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  }
+  hipStream_t str = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (dx_local) {
+    GemmDesc g{};
+    g.A = dy; g.lda = s.h; g.a_kmajor = true;
+    g.B = w; g.ldb = k; g.b_kmajor = false;
+    g.M = static_cast<int>(s.T); g.N = static_cast<int>(k); g.K = s.h;
+    g.C = dx_local; g.ldc = k;
+    g.aux = const_cast<void*>(gelu_preact); g.ld_aux = k;
+    g.epi = gelu_preact ? mtp::kEpiDGelu : mtp::kEpiStore;
+    g.tile = tile_override();
+    e = gemm(s, g, str);
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
+  {
+    GemmDesc g{};
+    g.A = dy; g.lda = s.h; g.a_kmajor = false;
+    g.B = x_local; g.ldb = k; g.b_kmajor = false;
+    g.M = s.h; g.N = static_cast<int>(k); g.K = static_cast<int>(s.T);
+    g.C = dw; g.ldc = k; g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
+    g.tile = tile_override();
+    e = gemm(s, g, str);
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
+  if (db) e = mtp::column_sum(s.bf16, dy, s.T, s.h, db, accumulate != 0, ws, str);
+  return hip_status(e);
+}
+
+int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* lse,
+                 const int32_t* cu_seqlens, int32_t n_seqs, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
+  if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  mtp::AttnDesc a{};
+  a.qkv = qkv; a.ctx = ctx; a.lse = lse;
+  a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  return hip_status(mtp::attn_fwd(s.bf16, a, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, const float* lse,
+                 const void* dctx, void* dqkv, const int32_t* cu_seqlens, int32_t n_seqs,
+                 void* ws, size_t ws_bytes, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
+    return MTP_ERR_INVALID_ARG;
+  if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float);
+  if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  mtp::AttnDesc a{};
+  a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
+  a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
+  a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials, int32_t n_partials,
+                    const void* bias, const void* residual, void* out, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!partials || n_partials < 1 || n_partials > mtp::kMaxPartials) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_partials; ++i)
+    if (!ok_ptr(partials[i])) return MTP_ERR_INVALID_ARG;
+  if (!ok_opt(bias) || !ok_opt(residual) || !ok_ptr(out)) return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::partial_sum(s.bf16, partials, n_partials, bias, residual, out, s.T, s.h,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int mtp_vocab_ce_stats(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,
+                       float* m, float* sm, float* z_tgt, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (s.Vl <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(logits) || !ok_ptr(targets) || !ok_ptr(m) || !ok_ptr(sm) || !ok_ptr(z_tgt))
+    return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::ce_stats(logits, targets, m, sm, z_tgt, s.T, s.Vl, s.r * s.Vl, s.V,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int mtp_vocab_ce_combine(const mtp_shard_desc* desc, const float* const* m, const float* const* sm,
+                         const float* const* z_tgt, int32_t n_ranks, float* M, float* S,
+                         float* loss, float* loss_mean, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!m || !sm || !z_tgt || n_ranks < 1 || n_ranks > mtp::kMaxPartials) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_ranks; ++i)
+    if (!ok_ptr(m[i]) || !ok_ptr(sm[i]) || !ok_ptr(z_tgt[i])) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(M) || !ok_ptr(S) || !ok_ptr(loss) || !ok_opt(loss_mean)) return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::ce_combine(m, sm, z_tgt, n_ranks, M, S, loss, loss_mean, s.T,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int mtp_vocab_ce_bwd(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,
+                     const float* M, const float* S, float dloss_scale, void* dlogits,
+                     void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (s.Vl <= 0) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(logits) || !ok_ptr(targets) || !ok_ptr(M) || !ok_ptr(S) || !ok_ptr(dlogits))
+    return MTP_ERR_INVALID_ARG;
+  if (!isfinite(dloss_scale)) return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::ce_bwd(s.bf16, logits, targets, M, S, dloss_scale, dlogits, s.T, s.Vl,
+                                s.r * s.Vl, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

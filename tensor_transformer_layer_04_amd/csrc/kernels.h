@@ -1,0 +1,77 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+// Host-side only declarations; every launcher enqueues on `stream` and
+// returns hipGetLastError() after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+// ------------------------------------------------------------------ GEMM
+// C[M,N] = sum_k A(m,k) B(n,k), fp32 accumulate, then an epilogue.
+//   A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B(n,k) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+enum Epilogue : int {
+  kEpiStore = 0,    // C = acc (+ bias[n])                     C in elem type
+  kEpiGelu = 1,     // aux = acc + bias (u); C = GeLU_tanh(u)   C, aux elem type
+  kEpiDGelu = 2,    // C = acc * GeLU_tanh'(aux)               C, aux elem type
+  kEpiF32 = 3,      // C = acc (+ bias[n])                     C fp32
+  kEpiF32Acc = 4,   // C += acc                                C fp32
+};
+
+struct GemmDesc {
+  const void* A; int64_t lda; bool a_kmajor;
+  const void* B; int64_t ldb; bool b_kmajor;
+  int M, N, K;
+  void* C; int64_t ldc;
+  const void* bias;    // [N] elem type, nullable
+  void* aux; int64_t ld_aux;
+  int epi;
+  int tile;            // tile-shape override for tuning (-1: heuristic)
+};
+
+hipError_t gemm_bf16(const GemmDesc& g, hipStream_t stream);
+hipError_t gemm_f32(const GemmDesc& g, hipStream_t stream);
+
+// Column sums of a [rows, cols] matrix into fp32 out[cols] (= or +=).
+// ws must hold column_sum_ws_bytes(rows, cols) bytes.
+size_t column_sum_ws_bytes(int64_t rows, int64_t cols);
+hipError_t column_sum(bool bf16, const void* x, int64_t rows, int64_t cols, float* out,
+                      bool accumulate, void* ws, hipStream_t stream);
+
+// ------------------------------------------------------------- row-wise
+hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void* beta, void* y,
+                         float* mean, float* rstd, int64_t T, int h, float eps,
+                         hipStream_t stream);
+size_t layernorm_bwd_ws_bytes(int64_t T, int h);
+hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* gamma,
+                         const float* mean, const float* rstd, const void* dres, void* dx,
+                         float* dgamma, float* dbeta, bool accumulate, int64_t T, int h,
+                         void* ws, hipStream_t stream);
+constexpr int kMaxPartials = 16;
+hipError_t partial_sum(bool bf16, const void* const* partials, int n, const void* bias,
+                       const void* residual, void* out, int64_t T, int h, hipStream_t stream);
+hipError_t zero_f32(float* p, int64_t n, hipStream_t stream);
+
+// ------------------------------------------------------------- attention
+struct AttnDesc {
+  const void* qkv; void* ctx; float* lse;
+  const void* dctx; void* dqkv; float* delta;  // backward
+  const int32_t* cu_seqlens; int n_seqs;        // nullable -> fixed seq_len
+  int64_t T; int seq_len; int heads; int head_dim;
+};
+hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t stream);
+hipError_t attn_bwd(bool bf16, const AttnDesc& a, hipStream_t stream);
+
+// ------------------------------------------------------------ vocab CE
+hipError_t ce_stats(const float* logits, const int32_t* targets, float* m, float* s, float* zt,
+                    int64_t T, int64_t V_l, int64_t v0, int64_t V, hipStream_t stream);
+hipError_t ce_combine(const float* const* m, const float* const* s, const float* const* zt, int n,
+                      float* M, float* S, float* loss, float* loss_mean, int64_t T,
+                      hipStream_t stream);
+hipError_t ce_bwd(bool bf16, const float* logits, const int32_t* targets, const float* M,
+                  const float* S, float scale, void* dlogits, int64_t T, int64_t V_l, int64_t v0,
+                  hipStream_t stream);
+
+}  // namespace mtp

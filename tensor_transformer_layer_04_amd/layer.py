@@ -1,0 +1,259 @@
+"""Tensor-parallel pre-LN transformer layer shards on one GPU.
+
+``TPLayer`` sequences the libmtp calls for one or more rank shards of a
+Megatron-style layer (page "Megatron-LM 3D parallelism guide", §2.1: the
+Q/K/V and FC1 weights split by output columns, the output projection and
+FC2 by input rows, per-rank partials summed).  All ranks' shards run one
+after another on the same device and ``mtp_partial_sum`` stands in for the
+tensor-parallel all-reduce.  Torch provides device memory and the stream;
+every step of the layer runs in libmtp's kernels.
+
+Forward (per step):
+    ln1 = LN(x)                                   (replicated, computed once)
+    per rank r: qkv_r = ln1 Wqkv_r^T + bqkv_r;  ctx_r, lse_r = attn(qkv_r)
+                p_r = ctx_r Wo_r^T                (partial)
+    y1 = sum_r p_r + bo + x
+    ln2 = LN(y1)
+    per rank r: u_r = ln2 W1_r^T + b1_r; g_r = GeLU(u_r); q_r = g_r W2_r^T
+    y = sum_r q_r + b2 + y1
+Backward mirrors it; the input gradient of each column-parallel map is the
+sum of the ranks' partials (the input reached every rank).
+
+Ranks that are not computed in this process can contribute their partials
+through ``external`` buffers (e.g. precomputed by an earlier run), which is
+how one rank's shard is timed with the full t-way sums charged to it.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import mtp
+
+
+def desc_for(cfg, rank: int) -> mtp.mtp_shard_desc:
+    """The C descriptor of rank ``rank`` for a workload config."""
+    T = cfg.tokens
+    seq_len, mb = (T, 1) if cfg.varlen_tokens else (cfg.seq_len, cfg.micro_batch)
+    return mtp.make_desc(cfg.hidden, cfg.heads, cfg.ffn, cfg.tp, rank, seq_len, mb,
+                         mtp.MTP_F32 if cfg.dtype == "f32" else mtp.MTP_BF16,
+                         vocab=cfg.vocab, ln_eps=cfg.eps)
+
+
+def pack_rank_weights(full: Dict[str, torch.Tensor], cfg, rank: int,
+                      device="cuda") -> Dict[str, torch.Tensor]:
+    """Slice the unsharded weights into rank ``rank``'s shard.
+
+    Column-parallel maps keep the rank's output rows (Wqkv_r stacks the
+    rank's rows of Wq, Wk and Wv, so its output is [q_r | k_r | v_r]);
+    row-parallel maps keep the rank's input columns.  Replicated tensors
+    (LayerNorm affine, row-parallel biases) are copied as they are.
+    """
+    h, f, t = cfg.hidden, cfg.ffn, cfg.tp
+    hl, fl = h // t, f // t
+    hs = slice(rank * hl, (rank + 1) * hl)
+    fs = slice(rank * fl, (rank + 1) * fl)
+
+    def dev(x):
+        return x.to(device).contiguous()
+    w = {
+        "wqkv": dev(torch.cat([full["wq"][hs], full["wk"][hs], full["wv"][hs]], 0)),
+        "bqkv": dev(torch.cat([full["bqkv"][:h][hs], full["bqkv"][h:2 * h][hs],
+                               full["bqkv"][2 * h:][hs]], 0)),
+        "wo": dev(full["wo"][:, hs]),
+        "w1": dev(full["w1"][fs]),
+        "b1": dev(full["b1"][fs]),
+        "w2": dev(full["w2"][:, fs]),
+    }
+    if cfg.vocab:
+        vl = cfg.vocab // t
+        w["emb"] = dev(full["emb"][rank * vl:(rank + 1) * vl])
+    return w
+
+
+def replicated_params(full: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch.Tensor]:
+    return {k: full[k].to(device).contiguous() for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "bo", "b2")}
+
+
+class TPLayer:
+    """One pre-LN layer, ``ranks`` of its ``cfg.tp`` shards computed here."""
+
+    def __init__(self, cfg, full: Dict[str, torch.Tensor], ranks: Optional[Sequence[int]] = None,
+                 device="cuda", cu_seqlens: Optional[torch.Tensor] = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.ranks = list(range(cfg.tp)) if ranks is None else list(ranks)
+        self.dt = cfg.torch_dtype
+        self.T = cfg.tokens
+        self.descs = {r: desc_for(cfg, r) for r in range(cfg.tp)}
+        self.d0 = self.descs[self.ranks[0]]
+        self.w = {r: pack_rank_weights(full, cfg, r, device) for r in self.ranks}
+        self.rep = replicated_params(full, device)
+        self.cu = None
+        self.n_seqs = 0
+        if cu_seqlens is not None and cfg.varlen_tokens:
+            self.cu = cu_seqlens.to(device=self.device, dtype=torch.int32).contiguous()
+            self.n_seqs = self.cu.numel() - 1
+        self._alloc()
+
+    # ------------------------------------------------------------ buffers
+    def _alloc(self):
+        cfg, T, dt, dev = self.cfg, self.T, self.dt, self.device
+        h, t = cfg.hidden, cfg.tp
+        hl, al, fl = h // t, cfg.heads // t, cfg.ffn // t
+        E = lambda *s, d=dt: torch.empty(*s, dtype=d, device=dev)
+        self.ln1, self.y1, self.ln2, self.y = E(T, h), E(T, h), E(T, h), E(T, h)
+        self.mu1, self.rs1, self.mu2, self.rs2 = (E(T, d=torch.float32) for _ in range(4))
+        self.a: Dict[int, Dict[str, torch.Tensor]] = {}
+        for r in self.ranks:
+            self.a[r] = {
+                "qkv": E(T, 3 * hl), "ctx": E(T, hl), "lse": E(al, T, d=torch.float32),
+                "p": E(T, h), "u": E(T, fl), "g": E(T, fl), "q": E(T, h),
+                # backward
+                "du": E(T, fl), "dln2": E(T, h), "dctx": E(T, hl), "dqkv": E(T, 3 * hl),
+                "dln1": E(T, h),
+            }
+        self.dy1, self.dx, self.dln2_sum, self.dln1_sum = E(T, h), E(T, h), E(T, h), E(T, h)
+        f32 = torch.float32
+        self.grads: Dict[int, Dict[str, torch.Tensor]] = {}
+        for r in self.ranks:
+            self.grads[r] = {
+                "dwqkv": E(3 * hl, h, d=f32), "dbqkv": E(3 * hl, d=f32), "dwo": E(h, hl, d=f32),
+                "dw1": E(fl, h, d=f32), "db1": E(fl, d=f32), "dw2": E(h, fl, d=f32),
+            }
+        self.rgrads = {k: E(h, d=f32) for k in ("dln1_g", "dln1_b", "dln2_g", "dln2_b", "dbo", "db2")}
+        d = self.d0
+        ws = max(
+            mtp.mtp_workspace_size(d, mtp.MTP_OP_LAYERNORM_BWD),
+            mtp.mtp_workspace_size(d, mtp.MTP_OP_COL_LINEAR_BWD, mtp.MTP_QKV),
+            mtp.mtp_workspace_size(d, mtp.MTP_OP_COL_LINEAR_BWD, mtp.MTP_FC1),
+            mtp.mtp_workspace_size(d, mtp.MTP_OP_ROW_LINEAR_BWD, mtp.MTP_PROJ),
+            mtp.mtp_workspace_size(d, mtp.MTP_OP_ATTN_BWD),
+            256)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ws_bytes = ws
+        self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
+
+    # ------------------------------------------------------------ forward
+    def forward(self, x: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
+        """Forward of the computed ranks; returns y (valid when every rank's
+        partials are available, computed or external)."""
+        ext = external or {}
+        d0, rep = self.d0, self.rep
+        self.x = x
+        mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+        for r in self.ranks:
+            d, w, a = self.descs[r], self.w[r], self.a[r]
+            mtp.mtp_col_linear_fwd(d, mtp.MTP_QKV, self.ln1, w["wqkv"], w["bqkv"], a["qkv"], None)
+            mtp.mtp_attn_fwd(d, a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
+            mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
+        parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
+        mtp.mtp_partial_sum(d0, parts, rep["bo"], x, self.y1)
+        mtp.mtp_layernorm(d0, self.y1, rep["ln2_g"], rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+        for r in self.ranks:
+            d, w, a = self.descs[r], self.w[r], self.a[r]
+            mtp.mtp_col_linear_fwd(d, mtp.MTP_FC1, self.ln2, w["w1"], w["b1"], a["g"], a["u"])
+            mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, a["g"], w["w2"], a["q"])
+        parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
+        mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
+        return self.y
+
+    # ----------------------------------------------------------- backward
+    def backward(self, dy: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
+        ext = external or {}
+        d0, rep, ws, wsb = self.d0, self.rep, self.ws, self.ws_bytes
+        for r in self.ranks:
+            d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
+            db2 = self.rgrads["db2"] if r == self.owns_bias else None
+            mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], g["dw2"],
+                                   db2, 0, ws, wsb)
+            mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], g["dw1"],
+                                   g["db1"], 0, ws, wsb)
+        parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
+        mtp.mtp_partial_sum(d0, parts, None, None, self.dln2_sum)
+        mtp.mtp_layernorm_bwd(d0, self.dln2_sum, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
+                              self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws, wsb)
+        for r in self.ranks:
+            d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
+            dbo = self.rgrads["dbo"] if r == self.owns_bias else None
+            mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None, a["dctx"],
+                                   g["dwo"], dbo, 0, ws, wsb)
+            mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
+                             self.n_seqs, ws, wsb)
+            mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
+                                   g["dwqkv"], g["dbqkv"], 0, ws, wsb)
+        parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
+        mtp.mtp_partial_sum(d0, parts, None, None, self.dln1_sum)
+        mtp.mtp_layernorm_bwd(d0, self.dln1_sum, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                              self.dy1, self.dx, self.rgrads["dln1_g"], self.rgrads["dln1_b"], 0,
+                              ws, wsb)
+        return self.dx
+
+    def partials(self) -> Dict[str, List[torch.Tensor]]:
+        """This object's partial outputs, to be passed as ``external`` to a
+        layer that computes the remaining ranks."""
+        return {
+            "proj": [self.a[r]["p"].clone() for r in self.ranks],
+            "fc2": [self.a[r]["q"].clone() for r in self.ranks],
+            "fc1_dx": [self.a[r]["dln2"].clone() for r in self.ranks],
+            "qkv_dx": [self.a[r]["dln1"].clone() for r in self.ranks],
+        }
+
+
+class VocabHead:
+    """Vocab-parallel output head with cross-entropy from per-shard stats.
+
+    Rank r holds rows [r*V/t, (r+1)*V/t) of the output embedding
+    (VocabParallelEmbedding, page "Megatron-LM: NVIDIA large-model training
+    framework", section "Tensor parallelism").  Each shard computes its fp32
+    logits, their max / sum-exp / target logit; the combine gives the loss
+    per token; the backward writes dlogits and the shard's partial of dy.
+    """
+
+    def __init__(self, cfg, full: Dict[str, torch.Tensor], ranks: Optional[Sequence[int]] = None,
+                 device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.ranks = list(range(cfg.tp)) if ranks is None else list(ranks)
+        self.descs = {r: desc_for(cfg, r) for r in range(cfg.tp)}
+        self.d0 = self.descs[self.ranks[0]]
+        T, h, vl = cfg.tokens, cfg.hidden, cfg.vocab // cfg.tp
+        vl_rows = slice(0, 0)
+        self.emb = {r: full["emb"][r * vl:(r + 1) * vl].to(device).contiguous() for r in self.ranks}
+        self.targets = full["targets"].to(device=device, dtype=torch.int32).contiguous()
+        f32, dt = torch.float32, cfg.torch_dtype
+        E = lambda *s, d=dt: torch.empty(*s, dtype=d, device=self.device)
+        self.logits = {r: E(T, vl, d=f32) for r in self.ranks}
+        self.stats = {r: (E(T, d=f32), E(T, d=f32), E(T, d=f32)) for r in self.ranks}
+        self.dlogits = {r: E(T, vl) for r in self.ranks}
+        self.dy_part = {r: E(T, h) for r in self.ranks}
+        self.demb = {r: E(vl, h, d=f32) for r in self.ranks}
+        self.M, self.S, self.loss = E(T, d=f32), E(T, d=f32), E(T, d=f32)
+        self.loss_mean = E(1, d=f32)
+        self.dy = E(T, h)
+        del vl_rows
+
+    def forward(self, y: torch.Tensor, external_stats: Sequence = ()):
+        self.y = y
+        for r in self.ranks:
+            d = self.descs[r]
+            mtp.mtp_col_linear_fwd(d, mtp.MTP_VOCAB, y, self.emb[r], None, self.logits[r], None)
+            m, s, z = self.stats[r]
+            mtp.mtp_vocab_ce_stats(d, self.logits[r], self.targets, m, s, z)
+        stats = [self.stats[r] for r in self.ranks] + list(external_stats)
+        mtp.mtp_vocab_ce_combine(self.d0, [s[0] for s in stats], [s[1] for s in stats],
+                                 [s[2] for s in stats], self.M, self.S, self.loss, self.loss_mean)
+        return self.loss_mean
+
+    def backward(self, external_dy: Sequence[torch.Tensor] = ()):
+        T = self.cfg.tokens
+        for r in self.ranks:
+            d = self.descs[r]
+            mtp.mtp_vocab_ce_bwd(d, self.logits[r], self.targets, self.M, self.S,
+                                 1.0 / max(T, 1), self.dlogits[r])
+            mtp.mtp_col_linear_bwd(d, mtp.MTP_VOCAB, self.dlogits[r], self.y, self.emb[r],
+                                   self.dy_part[r], self.demb[r], None, 0, None, 0)
+        parts = [self.dy_part[r] for r in self.ranks] + list(external_dy)
+        mtp.mtp_partial_sum(self.d0, parts, None, None, self.dy)
+        return self.dy

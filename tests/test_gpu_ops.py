@@ -1,0 +1,301 @@
+"""Per-entry-point parity of libmtp against the fp64 oracle (GPU).
+
+Shapes are chosen to leave ragged tails against every tile size the
+kernels use (tokens, output features and reduction lengths that are not
+multiples of 32/64/128/256), plus the degenerate cases: a single token,
+no tokens at all, length-1 and empty documents, the maximum number of
+partials.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL, check, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _m():
+    from tensor_transformer_layer_04_amd import mtp
+    return mtp
+
+
+def rnd(shape, dtype, seed, std=1.0):
+    t = torch.randn(*shape, generator=torch.Generator().manual_seed(seed)) * std
+    return t.to(DT[dtype])
+
+
+def dev(t):
+    return t.cuda().contiguous()
+
+
+def host(t):
+    return t.detach().float().cpu()
+
+
+def desc(mtp, h, a, f, tp, r, T, dtype, vocab=0):
+    return mtp.make_desc(h, a, f, tp, r, T, 1, mtp.MTP_BF16 if dtype == "bf16" else mtp.MTP_F32,
+                         vocab=vocab)
+
+
+def ws_for(mtp, d, op, kind=0):
+    n = max(mtp.mtp_workspace_size(d, op, kind), 256)
+    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+
+
+# ---------------------------------------------------------------- linear
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_column_and_row_linear(dtype, T):
+    require_gpu()
+    mtp = _m()
+    h, a, f = 256, 4, 800          # h_l = 64, f_l = 200 at tp 4
+    tp, r = 4, 1
+    hl, fl = h // tp, f // tp
+    d = desc(mtp, h, a, f, tp, r, T, dtype)
+    tol = TOL[dtype]
+    x = rnd((T, h), dtype, 1)
+    wq = rnd((3 * hl, h), dtype, 2, 0.05)
+    bq = rnd((3 * hl,), dtype, 3, 0.1)
+    w1 = rnd((fl, h), dtype, 4, 0.05)
+    b1 = rnd((fl,), dtype, 5, 0.1)
+    wo = rnd((h, hl), dtype, 6, 0.05)
+    w2 = rnd((h, fl), dtype, 7, 0.05)
+    rep = {}
+    # column-parallel QKV forward
+    y = torch.empty(T, 3 * hl, dtype=DT[dtype], device="cuda")
+    mtp.mtp_col_linear_fwd(d, mtp.MTP_QKV, dev(x), dev(wq), dev(bq), y, None)
+    X, WQ, BQ = (oracle.to64(t) for t in (x, wq, bq))
+    check("qkv", host(y), oracle.linear(X, WQ, BQ), tol, rep)
+    # FC1 with fused GeLU
+    g = torch.empty(T, fl, dtype=DT[dtype], device="cuda")
+    u = torch.empty_like(g)
+    mtp.mtp_col_linear_fwd(d, mtp.MTP_FC1, dev(x), dev(w1), dev(b1), g, u)
+    U = oracle.linear(X, oracle.to64(w1), oracle.to64(b1))
+    check("fc1_u", host(u), U, tol, rep)
+    check("fc1_g", host(g), oracle.gelu_tanh(U), tol, rep)
+    # row-parallel forward (PROJ and FC2)
+    xl = rnd((T, hl), dtype, 8)
+    p = torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, dev(xl), dev(wo), p)
+    check("proj", host(p), oracle.linear(oracle.to64(xl), oracle.to64(wo)), tol, rep)
+    mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, g, dev(w2), p)
+    G = oracle.to64(g.cpu())
+    check("fc2", host(p), oracle.linear(G, oracle.to64(w2)), tol, rep)
+    # column-parallel backward: dx partial, dW, db; then accumulate
+    dy = rnd((T, 3 * hl), dtype, 9)
+    dx = torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    dw = torch.empty(3 * hl, h, dtype=torch.float32, device="cuda")
+    db = torch.empty(3 * hl, dtype=torch.float32, device="cuda")
+    ws, wsb = ws_for(mtp, d, mtp.MTP_OP_COL_LINEAR_BWD, mtp.MTP_QKV)
+    mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, dev(dy), dev(x), dev(wq), dx, dw, db, 0, ws, wsb)
+    DY = oracle.to64(dy)
+    check("col_dx", host(dx), DY @ WQ, tol, rep)
+    check("col_dw", host(dw), DY.T @ X, tol, rep)
+    check("col_db", host(db), DY.sum(0), tol, rep)
+    mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, dev(dy), dev(x), dev(wq), None, dw, db, 1, ws, wsb)
+    check("col_dw_acc", host(dw), 2 * (DY.T @ X), tol, rep)
+    check("col_db_acc", host(db), 2 * DY.sum(0), tol, rep)
+    # row-parallel backward with the GeLU derivative fused
+    dyr = rnd((T, h), dtype, 10)
+    du = torch.empty(T, fl, dtype=DT[dtype], device="cuda")
+    dw2 = torch.empty(h, fl, dtype=torch.float32, device="cuda")
+    db2 = torch.empty(h, dtype=torch.float32, device="cuda")
+    ws, wsb = ws_for(mtp, d, mtp.MTP_OP_ROW_LINEAR_BWD, mtp.MTP_FC2)
+    mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dev(dyr), g, dev(w2), u, du, dw2, db2, 0, ws, wsb)
+    DYR, UU = oracle.to64(dyr), oracle.to64(u.cpu())
+    check("row_du", host(du), (DYR @ oracle.to64(w2)) * oracle.gelu_tanh_grad(UU), tol, rep)
+    check("row_dw", host(dw2), DYR.T @ G, tol, rep)
+    check("row_db", host(db2), DYR.sum(0), tol, rep)
+    log(f"linear {dtype} T={T}: " + ", ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+def test_vocab_linear_fp32_logits():
+    require_gpu()
+    mtp = _m()
+    T, h, V, tp = 77, 256, 2 * 520, 2
+    d = desc(mtp, h, 2, 0, tp, 1, T, "bf16", vocab=V)
+    x, e = rnd((T, h), "bf16", 11), rnd((V // tp, h), "bf16", 12, 0.05)
+    z = torch.empty(T, V // tp, dtype=torch.float32, device="cuda")
+    mtp.mtp_col_linear_fwd(d, mtp.MTP_VOCAB, dev(x), dev(e), None, z, None)
+    rep = {}
+    check("logits", host(z), oracle.linear(oracle.to64(x), oracle.to64(e)), TOL["bf16"], rep)
+
+
+# ------------------------------------------------------------- LayerNorm
+@pytest.mark.parametrize("dtype,h,T", [("bf16", 192, 53), ("f32", 256, 7), ("bf16", 12288, 9),
+                                       ("bf16", 4096, 1)])
+def test_layernorm_fwd_bwd(dtype, h, T):
+    require_gpu()
+    mtp = _m()
+    d = desc(mtp, h, h // 64, 0, 1, 0, T, dtype)
+    x = rnd((T, h), dtype, 20, 2.0)
+    gm = (1 + 0.1 * torch.randn(h, generator=torch.Generator().manual_seed(21))).to(DT[dtype])
+    bt = rnd((h,), dtype, 22, 0.1)
+    y = torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    mu = torch.empty(T, dtype=torch.float32, device="cuda")
+    rs = torch.empty_like(mu)
+    mtp.mtp_layernorm(d, dev(x), dev(gm), dev(bt), y, mu, rs)
+    X, GM, BT = (oracle.to64(t) for t in (x, gm, bt))
+    ref, rmu, rrs = oracle.layernorm(X, GM, BT, 1e-5)
+    tol = TOL[dtype]
+    rep = {}
+    check("ln_y", host(y), ref, tol, rep)
+    check("ln_mu", host(mu), rmu, tol, rep)
+    check("ln_rstd", host(rs), rrs, tol, rep)
+    dy = rnd((T, h), dtype, 23)
+    dres = rnd((T, h), dtype, 24)
+    dx = torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    dg = torch.empty(h, dtype=torch.float32, device="cuda")
+    dbt = torch.empty_like(dg)
+    ws, wsb = ws_for(mtp, d, mtp.MTP_OP_LAYERNORM_BWD)
+    mtp.mtp_layernorm_bwd(d, dev(dy), dev(x), dev(gm), mu, rs, dev(dres), dx, dg, dbt, 0, ws, wsb)
+    rdx, rdg, rdb = oracle.layernorm_backward(oracle.to64(dy), X, GM, rmu, rrs)
+    check("ln_dx", host(dx), rdx + oracle.to64(dres), tol, rep)
+    check("ln_dgamma", host(dg), rdg, tol, rep)
+    check("ln_dbeta", host(dbt), rdb, tol, rep)
+    log(f"layernorm {dtype} h={h} T={T}: " + ", ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+# ------------------------------------------------------------- attention
+ATTN_CASES = [
+    # dtype, heads(local), d, T, cu_seqlens (None = one causal sequence)
+    ("bf16", 2, 128, 77, None),
+    ("bf16", 3, 64, 200, None),
+    ("bf16", 2, 128, 300, [0, 1, 2, 130, 130, 131, 300]),
+    ("bf16", 1, 128, 520, [0, 129, 257, 520]),
+    ("bf16", 2, 64, 1, None),
+    ("f32", 2, 64, 128, None),
+    ("f32", 1, 128, 90, [0, 40, 41, 90]),
+]
+
+
+@pytest.mark.parametrize("dtype,al,D,T,cu", ATTN_CASES)
+def test_attention_fwd_bwd(dtype, al, D, T, cu):
+    require_gpu()
+    mtp = _m()
+    h = al * D
+    d = desc(mtp, h, al, 0, 1, 0, T, dtype)
+    qkv = rnd((T, 3 * h), dtype, 30)
+    dctx = rnd((T, h), dtype, 31)
+    cu_t = None
+    n = 0
+    cu_list = cu if cu is not None else [0, T]
+    if cu is not None:
+        cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        n = len(cu) - 1
+    ctx = torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    lse = torch.empty(al, T, dtype=torch.float32, device="cuda")
+    mtp.mtp_attn_fwd(d, dev(qkv), ctx, lse, cu_t, n)
+    dqkv = torch.empty(T, 3 * h, dtype=DT[dtype], device="cuda")
+    ws, wsb = ws_for(mtp, d, mtp.MTP_OP_ATTN_BWD)
+    mtp.mtp_attn_bwd(d, dev(qkv), ctx, lse, dev(dctx), dqkv, cu_t, n, ws, wsb)
+    torch.cuda.synchronize()
+    Q = oracle.to64(qkv)
+    starts = oracle.doc_starts(cu_list, T)
+    rctx, rlse = oracle.attention_forward(Q[:, :h], Q[:, h:2 * h], Q[:, 2 * h:], al, starts)
+    dq, dk, dv = oracle.attention_backward(Q[:, :h], Q[:, h:2 * h], Q[:, 2 * h:],
+                                           oracle.to64(dctx), al, starts)
+    tol = TOL[dtype]
+    rep = {}
+    check("ctx", host(ctx), rctx, tol, rep)
+    check("lse", host(lse), rlse, tol, rep)
+    got = host(dqkv)
+    # with one visible key per query (T = 1) dq and dk are exactly zero; their
+    # error is then measured against the scale of dv
+    floor = 1e-3 * float(np.linalg.norm(dv))
+    check("dq", got[:, :h], dq, tol, rep, floor)
+    check("dk", got[:, h:2 * h], dk, tol, rep, floor)
+    check("dv", got[:, 2 * h:], dv, tol, rep)
+    log(f"attention {dtype} al={al} D={D} T={T} cu={cu}: " +
+        ", ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
+# ------------------------------------------------------------ partial sum
+@pytest.mark.parametrize("n", [1, 2, 16])
+def test_partial_sum(n):
+    require_gpu()
+    mtp = _m()
+    T, h = 45, 256
+    d = desc(mtp, h, 2, 0, 1, 0, T, "bf16")
+    parts = [rnd((T, h), "bf16", 40 + i) for i in range(n)]
+    bias, res = rnd((h,), "bf16", 60), rnd((T, h), "bf16", 61)
+    out = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_partial_sum(d, [dev(p) for p in parts], dev(bias), dev(res), out)
+    ref = sum(oracle.to64(p) for p in parts) + oracle.to64(bias) + oracle.to64(res)
+    rep = {}
+    check("sum", host(out), ref, TOL["bf16"], rep)
+    # without bias / residual, in place over the first partial
+    p0 = dev(parts[0])
+    mtp.mtp_partial_sum(d, [p0] + [dev(p) for p in parts[1:]], None, None, p0)
+    check("sum_inplace", host(p0), sum(oracle.to64(p) for p in parts), TOL["bf16"], rep)
+
+
+# --------------------------------------------------------------- vocab CE
+def test_vocab_ce_pieces():
+    require_gpu()
+    mtp = _m()
+    T, h, V, tp = 33, 256, 4 * 136, 4
+    vl = V // tp
+    z = torch.randn(T, V, generator=torch.Generator().manual_seed(70)) * 3
+    tg = torch.randint(0, V, (T,), generator=torch.Generator().manual_seed(71), dtype=torch.int32)
+    tgd = dev(tg)
+    stats, logits = [], []
+    for r in range(tp):
+        d = desc(mtp, h, 4, 0, tp, r, T, "bf16", vocab=V)
+        zr = dev(z[:, r * vl:(r + 1) * vl])
+        m, s, zt = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(3))
+        mtp.mtp_vocab_ce_stats(d, zr, tgd, m, s, zt)
+        stats.append((m, s, zt))
+        logits.append(zr)
+    d0 = desc(mtp, h, 4, 0, tp, 0, T, "bf16", vocab=V)
+    M, S, loss = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(3))
+    lm = torch.empty(1, dtype=torch.float32, device="cuda")
+    mtp.mtp_vocab_ce_combine(d0, [s[0] for s in stats], [s[1] for s in stats],
+                             [s[2] for s in stats], M, S, loss, lm)
+    Z = oracle.to64(z)
+    tgn = tg.numpy().astype(np.int64)
+    # the oracle's CE with y = Z and E = identity reproduces logits Z exactly
+    ref_loss, _, lse = oracle.vocab_ce_forward(Z, np.eye(V), tgn)
+    per_tok = lse - Z[np.arange(T), tgn]
+    rep = {}
+    check("loss_tokens", host(loss), per_tok, 1e-5, rep)
+    assert abs(float(lm.item()) - ref_loss) <= 1e-5 * abs(ref_loss)
+    _, _, dz = oracle.vocab_ce_backward(Z, np.eye(V), tgn, Z, lse)
+    for r in range(tp):
+        d = desc(mtp, h, 4, 0, tp, r, T, "bf16", vocab=V)
+        dl = torch.empty(T, vl, dtype=torch.bfloat16, device="cuda")
+        mtp.mtp_vocab_ce_bwd(d, logits[r], tgd, M, S, 1.0 / T, dl)
+        check(f"dlogits{r}", host(dl), dz[:, r * vl:(r + 1) * vl], TOL["bf16"], rep)
+
+
+# ----------------------------------------------------------- degenerate
+def test_zero_tokens_writes_zero_gradients():
+    require_gpu()
+    mtp = _m()
+    h, f = 128, 64
+    d = desc(mtp, h, 1, f, 1, 0, 0, "bf16")
+    e = torch.empty(0, h, dtype=torch.bfloat16, device="cuda")
+    e_f = torch.empty(0, f, dtype=torch.bfloat16, device="cuda")
+    w1 = dev(rnd((f, h), "bf16", 80))
+    dw = torch.full((f, h), 7.0, device="cuda")
+    db = torch.full((f,), 7.0, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    # zero-size tensors have no storage; pass a valid aligned dummy address
+    dummy = torch.empty(64, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, dummy, dummy, w1, dummy, dw, db, 0, ws, 256)
+    dg = torch.full((h,), 7.0, device="cuda")
+    dbt = torch.full((h,), 7.0, device="cuda")
+    stat = torch.empty(64, dtype=torch.float32, device="cuda")
+    mtp.mtp_layernorm_bwd(d, dummy, dummy, dummy, stat, stat, None, dummy, dg, dbt, 0, ws, 256)
+    lse = torch.empty(64, dtype=torch.float32, device="cuda")
+    mtp.mtp_attn_fwd(d, dummy, dummy, lse)
+    torch.cuda.synchronize()
+    assert float(dw.abs().max()) == 0.0 and float(db.abs().max()) == 0.0
+    assert float(dg.abs().max()) == 0.0 and float(dbt.abs().max()) == 0.0
+    del e, e_f
