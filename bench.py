@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark: one tensor-parallel rank's shard of a pre-LN GPT layer,
+forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 7b_tp2]
+
+One step is the whole shard path on one batch: LayerNorm, the column-parallel
+QKV GEMM, causal attention over the rank's heads, the row-parallel output
+projection, the t-way partial sum (the other ranks' partials are resident
+inputs, precomputed once), the second LayerNorm, the FC1/GeLU and FC2 pair,
+their partial sum, and the mirror-image backward with every weight and bias
+gradient.  Inputs are resident in HBM before the timed region.  The timed
+region is bracketed by torch.cuda.synchronize() and HIP events on the
+stream the kernels run on.
+
+Printed: one JSON line with the achieved model TFLOP/s (causal attention
+counted as s(s+1)/2 pairs), the fraction of the bf16 dense MFMA peak,
+tokens/s, the roofline of the dominant kernel (measured with HIP events
+around its launches inside the timed region) and the fp64 CPU oracle timed
+on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TP-shard layer fwd+bwd TFLOP/s, % bf16 MFMA peak, tokens/s on 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# Calls that launch the dominant kernel (the weight-gradient GEMM family).
+DOMINANT_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
+
+
+def seq_pairs(cu) -> int:
+    """Number of (query, visible key) pairs: sum over sequences of L(L+1)/2."""
+    return sum((b - a) * (b - a + 1) // 2 for a, b in zip(cu[:-1], cu[1:]))
+
+
+def shard_flops(cfg, cu) -> dict:
+    """Model FLOPs of one rank shard, forward + backward (3x forward)."""
+    T, h, t = cfg.tokens, cfg.hidden, cfg.tp
+    hl, fl, al, d = h // t, cfg.ffn // t, cfg.heads // t, cfg.head_dim
+    gemm_fwd = 2 * T * (3 * h * hl + hl * h + 2 * h * fl)
+    attn_fwd = 4 * d * al * seq_pairs(cu)
+    vocab_fwd = 2 * T * h * (cfg.vocab // t) if cfg.vocab else 0
+    return {
+        "total": 3 * (gemm_fwd + attn_fwd + vocab_fwd),
+        "gemm": 3 * gemm_fwd, "attn": 3 * attn_fwd, "vocab": 3 * vocab_fwd,
+        # per-call flops of the weight-gradient GEMMs (M*N*K*2)
+        "wgrad": {"fc2_wgrad": 2 * h * fl * T, "fc1_wgrad": 2 * fl * h * T,
+                  "proj_wgrad": 2 * h * hl * T, "qkv_wgrad": 2 * 3 * hl * h * T},
+    }
+
+
+def source_digest() -> str:
+    p = os.path.join(ROOT, "tensor_transformer_layer_04_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("gemm_source_sha") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, data) -> dict:
+    """The fp64 oracle (as it stands) on the host: one unsharded fwd+bwd."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:  # pragma: no cover
+        threads = 0
+    threads = threads or len(os.sched_getaffinity(0))
+    p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens", "targets")}
+    starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    t0 = time.perf_counter()
+    c = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
+    oracle.layer_backward(p64, c, p64["dy"], cfg.heads, starts)
+    dt = time.perf_counter() - t0
+    full = cfg.replace(tp=1)
+    fl = shard_flops(full, data["cu_seqlens"].tolist())["total"]
+    del np
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "tokens_per_s": round(cfg.tokens / dt, 1),
+            "sample": f"one unsharded fp64 forward+backward of the {cfg.name} layer "
+                      f"({cfg.tokens} tokens, all {cfg.tp} shards' work; "
+                      f"{fl / 1e9:.0f} model GFLOP), numpy/OpenBLAS"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="7b_tp2")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: every rank shard of the layer runs on the same "
+              "device and the tensor-parallel sum is an on-device kernel, so there is no "
+              f"multi-GPU run (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from tensor_transformer_layer_04_amd.layer import TPLayer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU (no GPU visible)", file=sys.stderr)
+        return 1
+    cfg = synth.get_config(args.config)
+    if cfg.vocab:
+        print("bench.py times layer configs without the vocab head", file=sys.stderr)
+        return 2
+    data = synth.generate(cfg)
+    cu = data["cu_seqlens"].tolist()
+    dev = "cuda"
+    x = data["x"].to(dev)
+    dy = data["dy"].to(dev)
+
+    ext = None
+    if cfg.tp > 1:
+        # The other ranks' partials of this very step, computed once and kept
+        # resident: the timed shard's t-way sums read them as inputs.
+        full = TPLayer(cfg, data, device=dev, cu_seqlens=data["cu_seqlens"])
+        full.forward(x)
+        full.backward(dy)
+        parts = full.partials()
+        ext = {k: [v[i] for i, r in enumerate(full.ranks) if r != args.rank] for k, v in parts.items()}
+        del full
+        torch.cuda.synchronize()
+    L = TPLayer(cfg, data, ranks=[args.rank], device=dev, cu_seqlens=data["cu_seqlens"])
+
+    def step():
+        L.forward(x, ext)
+        L.backward(dy, ext)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    L.probe = {t: [] for t in DOMINANT_TAGS}
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    probes = L.probe
+    L.probe = None
+
+    fl = shard_flops(cfg, cu)
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    # dominant kernel: the weight-gradient GEMM, 4 launches per step
+    dom_ms = sum(a.elapsed_time(b) for t in DOMINANT_TAGS for a, b in probes[t])
+    dom_launches = sum(len(probes[t]) for t in DOMINANT_TAGS)
+    dom_flops = sum(fl["wgrad"][t] * len(probes[t]) for t in DOMINANT_TAGS)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    kernel = "gemm_bf16_kernel<256,128,2,2,false,false,kEpiF32> (weight gradient)"
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded x, dy ~ N(0,1), weights ~ N(0,0.02), biases 0, LN gamma 1",
+        "config": {
+            "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard fwd+bwd",
+            "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn, "tp": cfg.tp,
+            "rank": args.rank, "seq_len": cfg.seq_len, "micro_batch": cfg.micro_batch,
+            "tokens": cfg.tokens, "global_batch": cfg.micro_batch, "parallelism": f"tp{cfg.tp}-shard",
+        },
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),
+        "model_gflop_per_step": round(fl["total"] / 1e9, 2),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": {
+            "kernel": kernel,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(kernel),
+            "launches_per_step": dom_launches // max(args.steps, 1),
+            "avg_launch_us": round(1e3 * dom_ms / max(dom_launches, 1), 2),
+            "share_of_step": round(dom_ms / (ms * args.steps), 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, data)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -142,8 +142,9 @@ int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, cons
  *   dx_partial [T,h] dtype (out): this rank's partial of the input gradient.
  *     The input fed every rank, so the full gradient is the sum of all ranks'
  *     partials (mtp_partial_sum).  Nullable (skipped).
- *   dw [out_l,h] fp32, db [out_l] fp32 nullable: overwritten, or incremented
- *     when accumulate != 0.
+ *   dw [out_l,h] fp32, db [out_l] fp32, both nullable (skipped): overwritten,
+ *     or incremented when accumulate != 0.  Each of dx_partial, dw, db is an
+ *     independent product, so one map's backward may be split over calls.
  * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_COL_LINEAR_BWD, kind)
  * when db != NULL.                                                           */
 int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, const void* x,
@@ -168,8 +169,8 @@ int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local
  *     pre-activation, (dy w) * GeLU_tanh'(gelu_preact), ready for
  *     mtp_col_linear_bwd(MTP_FC1).  Otherwise dx_local = dy w.
  *   dx_local [T,in_l] dtype (out), nullable.
- *   dw [h,in_l] fp32; db [h] fp32 nullable (the row-parallel bias belongs to
- *     one rank: pass it on exactly one).  accumulate as above.
+ *   dw [h,in_l] fp32 nullable; db [h] fp32 nullable (the row-parallel bias
+ *     belongs to one rank: pass it on exactly one).  accumulate as above.
  * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ROW_LINEAR_BWD, kind)
  * when db != NULL.                                                           */
 int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy,

@@ -168,7 +168,7 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
   if (st != MTP_OK) return st;
   const int64_t n = col_out(s, kind);
   if (n <= 0) return MTP_ERR_INVALID_ARG;
-  if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(w) || !ok_opt(dx_partial) || !ok_ptr(dw) || !ok_opt(db))
+  if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(w) || !ok_opt(dx_partial) || !ok_opt(dw) || !ok_opt(db))
     return MTP_ERR_INVALID_ARG;
   if (db) {
     const size_t need = mtp::column_sum_ws_bytes(s.T, n);
@@ -185,7 +185,7 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
-  {
+  if (dw) {
     GemmDesc g{};
     g.A = dy; g.lda = n; g.a_kmajor = false;
     g.B = x; g.ldb = s.h; g.b_kmajor = false;
@@ -223,7 +223,7 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
   if (st != MTP_OK) return st;
   const int64_t k = row_in(s, kind);
   if (k <= 0) return MTP_ERR_INVALID_ARG;
-  if (!ok_ptr(dy) || !ok_ptr(x_local) || !ok_ptr(w) || !ok_opt(dx_local) || !ok_ptr(dw) ||
+  if (!ok_ptr(dy) || !ok_ptr(x_local) || !ok_ptr(w) || !ok_opt(dx_local) || !ok_opt(dw) ||
       !ok_opt(db) || !ok_opt(gelu_preact))
     return MTP_ERR_INVALID_ARG;
   if (gelu_preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
@@ -245,7 +245,7 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
-  {
+  if (dw) {
     GemmDesc g{};
     g.A = dy; g.lda = s.h; g.a_kmajor = false;
     g.B = x_local; g.ldb = k; g.b_kmajor = false;

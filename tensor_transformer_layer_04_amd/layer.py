@@ -25,6 +25,7 @@ how one rank's shard is timed with the full t-way sums charged to it.
 """
 from __future__ import annotations
 
+import contextlib
 from typing import Dict, List, Optional, Sequence
 
 import torch
@@ -134,6 +135,22 @@ class TPLayer:
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
         self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
+        # Optional timing probe: {tag: [(start_event, end_event), ...]} for the
+        # tags present as keys; events are recorded on the current stream.
+        self.probe: Optional[Dict[str, list]] = None
+
+    @contextlib.contextmanager
+    def _timed(self, tag: str):
+        pr = self.probe
+        if pr is None or tag not in pr:
+            yield
+            return
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        pr[tag].append((a, b))
 
     # ------------------------------------------------------------ forward
     def forward(self, x: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
@@ -142,52 +159,88 @@ class TPLayer:
         ext = external or {}
         d0, rep = self.d0, self.rep
         self.x = x
-        mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+        T = self._timed
+        with T("ln1"):
+            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
-            mtp.mtp_col_linear_fwd(d, mtp.MTP_QKV, self.ln1, w["wqkv"], w["bqkv"], a["qkv"], None)
-            mtp.mtp_attn_fwd(d, a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
-            mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
+            with T("qkv_fwd"):
+                mtp.mtp_col_linear_fwd(d, mtp.MTP_QKV, self.ln1, w["wqkv"], w["bqkv"], a["qkv"],
+                                       None)
+            with T("attn_fwd"):
+                mtp.mtp_attn_fwd(d, a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
+            with T("proj_fwd"):
+                mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
-        mtp.mtp_partial_sum(d0, parts, rep["bo"], x, self.y1)
-        mtp.mtp_layernorm(d0, self.y1, rep["ln2_g"], rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+        with T("sum_proj"):
+            mtp.mtp_partial_sum(d0, parts, rep["bo"], x, self.y1)
+        with T("ln2"):
+            mtp.mtp_layernorm(d0, self.y1, rep["ln2_g"], rep["ln2_b"], self.ln2, self.mu2, self.rs2)
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
-            mtp.mtp_col_linear_fwd(d, mtp.MTP_FC1, self.ln2, w["w1"], w["b1"], a["g"], a["u"])
-            mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, a["g"], w["w2"], a["q"])
+            with T("fc1_fwd"):
+                mtp.mtp_col_linear_fwd(d, mtp.MTP_FC1, self.ln2, w["w1"], w["b1"], a["g"], a["u"])
+            with T("fc2_fwd"):
+                mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, a["g"], w["w2"], a["q"])
         parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
-        mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
+        with T("sum_fc2"):
+            mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
         return self.y
 
     # ----------------------------------------------------------- backward
     def backward(self, dy: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
         ext = external or {}
         d0, rep, ws, wsb = self.d0, self.rep, self.ws, self.ws_bytes
+        T = self._timed
+        # Each linear map's backward is issued as two calls: the data gradient
+        # (with the bias gradient) and the weight gradient.
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
             db2 = self.rgrads["db2"] if r == self.owns_bias else None
-            mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], g["dw2"],
-                                   db2, 0, ws, wsb)
-            mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], g["dw1"],
-                                   g["db1"], 0, ws, wsb)
+            with T("fc2_dgrad"):
+                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], None,
+                                       db2, 0, ws, wsb)
+            with T("fc2_wgrad"):
+                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, g["dw2"],
+                                       None, 0, ws, wsb)
+            with T("fc1_dgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
+                                       g["db1"], 0, ws, wsb)
+            with T("fc1_wgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
+                                       None, 0, ws, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
-        mtp.mtp_partial_sum(d0, parts, None, None, self.dln2_sum)
-        mtp.mtp_layernorm_bwd(d0, self.dln2_sum, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
-                              self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws, wsb)
+        with T("sum_fc1_dx"):
+            mtp.mtp_partial_sum(d0, parts, None, None, self.dln2_sum)
+        with T("ln2_bwd"):
+            mtp.mtp_layernorm_bwd(d0, self.dln2_sum, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
+                                  self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws,
+                                  wsb)
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
             dbo = self.rgrads["dbo"] if r == self.owns_bias else None
-            mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None, a["dctx"],
-                                   g["dwo"], dbo, 0, ws, wsb)
-            mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
-                             self.n_seqs, ws, wsb)
-            mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
-                                   g["dwqkv"], g["dbqkv"], 0, ws, wsb)
+            with T("proj_dgrad"):
+                mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
+                                       a["dctx"], None, dbo, 0, ws, wsb)
+            with T("proj_wgrad"):
+                mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None, None,
+                                       g["dwo"], None, 0, ws, wsb)
+            with T("attn_bwd"):
+                mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
+                                 self.n_seqs, ws, wsb)
+            with T("qkv_dgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
+                                       None, g["dbqkv"], 0, ws, wsb)
+            with T("qkv_wgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
+                                       g["dwqkv"], None, 0, ws, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
-        mtp.mtp_partial_sum(d0, parts, None, None, self.dln1_sum)
-        mtp.mtp_layernorm_bwd(d0, self.dln1_sum, self.x, rep["ln1_g"], self.mu1, self.rs1,
-                              self.dy1, self.dx, self.rgrads["dln1_g"], self.rgrads["dln1_b"], 0,
-                              ws, wsb)
+        with T("sum_qkv_dx"):
+            mtp.mtp_partial_sum(d0, parts, None, None, self.dln1_sum)
+        with T("ln1_bwd"):
+            mtp.mtp_layernorm_bwd(d0, self.dln1_sum, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                                  self.dy1, self.dx, self.rgrads["dln1_g"], self.rgrads["dln1_b"],
+                                  0, ws, wsb)
         return self.dx
 
     def partials(self) -> Dict[str, List[torch.Tensor]]:
