@@ -184,7 +184,7 @@ def main(argv=None) -> int:
     dom_launches = sum(len(probes[t]) for t in DOMINANT_TAGS)
     dom_flops = sum(fl["wgrad"][t] * len(probes[t]) for t in DOMINANT_TAGS)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    kernel = "gemm_bf16_kernel<256,128,2,2,false,false,kEpiF32> (weight gradient)"
+    kernel = "gemm_bf16_kernel, weight-gradient layout (m-major A, n-major B, fp32 C)"
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),

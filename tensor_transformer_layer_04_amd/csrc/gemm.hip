@@ -6,13 +6,32 @@
 //   forward  y  = x W^T : A = x  [M,K] k-major,  B = W [N,K] k-major
 //   dgrad    dx = dy W  : A = dy [M,K] k-major,  B = W [K,N] n-major
 //   wgrad    dW = dy^T x: A = dy [K,M] m-major,  B = x [K,N] n-major
-// Every operand is staged into LDS with 8 consecutive k values per 16-byte
-// chunk, which is what one lane feeds to v_mfma_f32_32x32x16_bf16.  k-major
-// operands are copied chunk by chunk; m/n-major operands are read as 8x8
-// element blocks (8 k-rows of 8 contiguous m), transposed in registers and
-// written as 8 k-contiguous chunks.  LDS rows hold 64 k values (8 chunks);
-// chunk c of row r lives at slot c ^ (r & 7), so the 32 rows read by the
-// lanes of one MFMA operand fetch hit distinct banks.
+//
+// bf16 kernel design (gfx950):
+//  * One workgroup computes a BM x BN tile of C with WGM x WGN waves; each
+//    wave owns a (BM/WGM) x (BN/WGN) sub-tile of 32x32 blocks computed with
+//    v_mfma_f32_32x32x16_bf16.
+//  * Operand tiles of 64 k are copied from HBM straight into LDS by
+//    buffer_load_dwordx4 ... lds (no VGPR round trip), double-buffered: the
+//    next k-tile streams in while the current one feeds the MFMAs.  Every
+//    16-byte chunk that lies outside the matrix (ragged M, N or K) gets a
+//    buffer offset past the resource's num_records, which the hardware
+//    returns as zeros, so no edge needs a separate code path.
+//  * k-major operands are stored as rows of 64 k (128 B, 8 chunks); chunk c
+//    of row r sits at slot c ^ ((r >> 1) & 7), so the 16 rows read in one
+//    LDS cycle by an MFMA operand load hit distinct banks.  A lane's MFMA operand (8
+//    consecutive k of one row) is one ds_read_b128.
+//  * m/n-major operands are stored as 64 k-rows of the tile's m range; the
+//    MFMA operand (8 consecutive k of one m) is gathered by two
+//    ds_read_b64_tr_b16, which transpose 4x16 blocks across each group of 16
+//    lanes: lane i of a group receives element j from the address supplied
+//    by lane 4j + i/4, at sub-element i%4.  64-byte segments of a k-row are
+//    XOR-swizzled by k so the 8 k-rows of one transpose read spread over
+//    the banks.
+//  * The MFMA is issued as D = B_frag * A_frag so that each lane ends with 4
+//    consecutive n of one row m (8- or 16-byte stores in the epilogue).
+//  * Tiles are ordered so that the workgroups of one XCD (dispatched
+//    round-robin over the 8 XCDs) share operand panels in their L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,8 +39,13 @@ namespace mtp {
 namespace {
 
 constexpr int kBK = 64;
-constexpr int kChunks = kBK / 8;
 constexpr int kGroupM = 8;
+constexpr uint32_t kOOB = 0x80000000u;  // past every num_records: the load returns 0
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct GemmParams {
   const bf16_t* A; int64_t lda;
@@ -31,10 +55,16 @@ struct GemmParams {
   const void* bias;
   void* aux; int64_t ld_aux;
   int tiles_m, tiles_n;
+  uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31)
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kChunks + (chunk ^ (row & 7));
+__device__ __forceinline__ lds_void* to_lds(const void* p) {
+  return (lds_void*)const_cast<void*>(p);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           static_cast<int>(kRsrcWord3));
 }
 
 // Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids
@@ -54,71 +84,76 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsz;
 }
 
-// Global -> register -> LDS staging of one operand tile of R rows x 64 k.
-template <int R, int NT, bool KMAJOR> struct TileLoader;
+// Chunk swizzle of a k-major row (8 chunks of 16 B).  A ds_read_b128 is
+// served 16 lanes (256 B, all 64 banks) per cycle; the 16 rows those lanes
+// read are 2 per 256 B of LDS, so row pairs share a slot pattern and the 8
+// pairs get distinct chunk slots.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
-template <int R, int NT> struct TileLoader<R, NT, true> {
-  static constexpr int kPer = R * kChunks / NT;
-  static_assert(R * kChunks % NT == 0, "tile/threads mismatch");
-  uint4 r[kPer];
-  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int row0, int rmax,
-                                       int k0, int K, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      const int row = c >> 3, kc = c & 7;
-      const int grow = row0 + row, gk = k0 + kc * 8;
-      if (grow < rmax && gk < K)
-        r[i] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(grow) * ld + gk);
-      else
-        r[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint4* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * NT;
-      lds[swz(c >> 3, c & 7)] = r[i];
-    }
-  }
-};
+// 64-byte segment swizzle of an m/n-major k-row holding R elements (R/32
+// segments): the 8 k-rows {16t+0..3, 16t+8..11} (or +4) touched by one
+// transpose read map to 8 distinct segments when R >= 256.
+template <int R>
+__device__ __forceinline__ int swz_m(int chunk, int k) {
+  constexpr int kSegs = R / 32;
+  const int f = ((k & 3) | (((k >> 3) & 1) << 2)) & (kSegs - 1);
+  return chunk ^ (f << 2);
+}
 
-template <int R, int NT> struct TileLoader<R, NT, false> {
-  // R 8x8 blocks (8 k-blocks x R/8 row-blocks); thread tid takes blocks
-  // tid, tid+NT, ...
-  static constexpr int kBlocks = (R + NT - 1) / NT;
-  uint4 r[kBlocks * 8];
-  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int row0, int rmax,
-                                       int k0, int K, int tid) {
+// Issue the copy of one operand tile (R rows of the tile's m or n range x
+// 64 k) into one LDS stage.  The stage is R*128 bytes, written 1 KB per
+// instruction (64 lanes x 16 B, lane-contiguous); wave w issues
+// instructions w*kPer .. w*kPer+kPer-1.
+template <int R, int NW, bool KMAJ>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, char* stage, int wave,
+                                           int lane, int row0, int rmax, int k0, int K,
+                                           uint32_t ld_bytes) {
+  constexpr int kInstr = R / 8;
+  constexpr int kPer = kInstr / NW;
+  static_assert(kInstr % NW == 0, "tile rows must split over the waves");
 #pragma unroll
-    for (int bi = 0; bi < kBlocks; ++bi) {
-      const int b = tid + bi * NT;
-      const int rb = b % (R / 8), kb = b / (R / 8);
-      const int gr = row0 + rb * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + kb * 8 + j;
-        if (b < R && gr < rmax && gk < K)
-          r[bi * 8 + j] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(gk) * ld + gr);
-        else
-          r[bi * 8 + j] = make_uint4(0, 0, 0, 0);
-      }
+  for (int i = 0; i < kPer; ++i) {
+    const int j = wave * kPer + i;
+    const int q = j * 64 + lane;
+    uint32_t off;
+    if (KMAJ) {
+      const int row = q >> 3;
+      const int lc = (q & 7) ^ swz_k(row);
+      const int gr = row0 + row, gk = k0 + lc * 8;
+      off = (gr < rmax && gk < K) ? static_cast<uint32_t>(gr) * ld_bytes + gk * 2 : kOOB;
+    } else {
+      constexpr int kCpr = R / 8;  // 16-byte chunks per k-row
+      const int kr = q / kCpr;
+      const int lc = swz_m<R>(q % kCpr, kr);
+      const int gk = k0 + kr, gm = row0 + lc * 8;
+      off = (gk < K && gm < rmax) ? static_cast<uint32_t>(gk) * ld_bytes + gm * 2 : kOOB;
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(stage + j * 1024), 16, off, 0, 0, 0);
   }
-  __device__ __forceinline__ void store(uint4* lds, int tid) const {
-#pragma unroll
-    for (int bi = 0; bi < kBlocks; ++bi) {
-      const int b = tid + bi * NT;
-      if (b < R) {
-        const int rb = b % (R / 8), kb = b / (R / 8);
-        uint4 t[8];
-        transpose8x8_bf16(&r[bi * 8], t);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) lds[swz(rb * 8 + c, kb)] = t[c];
-      }
-    }
-  }
-};
+}
+
+// MFMA operand (8 consecutive k of one row) from a k-major LDS tile.
+__device__ __forceinline__ bf16x8 frag_k(const char* t, int row, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + row * 128 + ((c ^ swz_k(row)) << 4));
+}
+
+__device__ __forceinline__ v4i16 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<char*>(p));
+}
+
+// MFMA operand from an m/n-major LDS tile of R columns: lane l gets
+// rows rb + l%32, k = 16*kk + 8*(l/32) + 0..7.
+template <int R>
+__device__ __forceinline__ bf16x8 frag_m(const char* t, int rb, int kk, int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  const int k = kk * 16 + (G >> 1) * 8 + (s >> 2);
+  const int m = rb + (G & 1) * 16 + (s & 3) * 4;
+  const int c = m >> 3, w = (m & 7) * 2;
+  const v4i16 lo = tr_read(t + k * (R * 2) + (swz_m<R>(c, k) << 4) + w);
+  const v4i16 hi = tr_read(t + (k + 4) * (R * 2) + (swz_m<R>(c, k + 4) << 4) + w);
+  const v4i16 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 template <int EPI, typename ElemT>
 __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, float v[4]) {
@@ -156,28 +191,31 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
   }
 }
 
-// One workgroup computes a BM x BN tile with WGM x WGN waves; each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks.  The MFMA is issued
-// as D = B_frag * A_frag so that each lane ends with 4 consecutive n of one
-// row m (8- or 16-byte stores in the epilogue).
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+__global__ void __launch_bounds__(WGM * WGN * 64, (WGM * WGN + 3) / 4)
 gemm_bf16_kernel(GemmParams p) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
-  __shared__ uint4 lds_a[2][BM * kChunks];
-  __shared__ uint4 lds_b[2][BN * kChunks];
+  // Two stages per operand, as separate objects so the compiler can tell
+  // the stage being filled from the stage being read.
+  __shared__ __attribute__((aligned(1024))) char lds_a0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) char lds_a1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) char lds_b0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) char lds_b1[BN * 128];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   int tm, tn;
   tile_coords(p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  TileLoader<BM, NT, AK> la;
-  TileLoader<BN, NT, BKM> lb;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
+  const uint32_t lda_b = static_cast<uint32_t>(p.lda) * 2, ldb_b = static_cast<uint32_t>(p.ldb) * 2;
+
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -186,44 +224,88 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = (p.K + kBK - 1) / kBK;
-  la.load(p.A, p.lda, m0, p.M, 0, p.K, tid);
-  lb.load(p.B, p.ldb, n0, p.N, 0, p.K, tid);
-  la.store(lds_a[0], tid);
-  lb.store(lds_b[0], tid);
-  __syncthreads();
-
   const int lrow = lane & 31, lk = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(p.A, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid);
-      lb.load(p.B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid);
-    }
+  auto issue = [&](char* sa, char* sb, int k0) {
+    issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
+    issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
+  };
+  // Operand fragments of one k-step (16 k): FM A blocks and FN B blocks.
+  struct Frags { bf16x8 a[FM], b[FN]; };
+  auto load_frags = [&](const char* ta, const char* tb, int kk, Frags& f) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i)
+      f.a[i] = AK ? frag_k(ta, wm * WTM + i * 32 + lrow, kk * 2 + lk)
+                  : frag_m<BM>(ta, wm * WTM + i * 32, kk, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint4 t = lds_a[cur][swz(wm * WTM + i * 32 + lrow, kk * 2 + lk)];
-        af[i] = __builtin_bit_cast(bf16x8, t);
+    for (int j = 0; j < FN; ++j)
+      f.b[j] = BKM ? frag_k(tb, wn * WTN + j * 32 + lrow, kk * 2 + lk)
+                   : frag_m<BN>(tb, wn * WTN + j * 32, kk, lane);
+  };
+  // LDS reads per k-step (transpose reads come in pairs).
+  constexpr int kReads = FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
+  constexpr int kPerMfma = (kReads + FM * FN - 1) / (FM * FN);
+  // MFMAs of one k-step with the fragment reads of the next step spread
+  // between them, so LDS latency hides behind the matrix pipeline.
+  auto step = [&](const Frags& f, bool prefetch, const char* ta, const char* tb, int kk,
+                  Frags& nf) {
+    if (prefetch) load_frags(ta, tb, kk, nf);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    if (prefetch) {
+#ifdef MTP_READS_FIRST
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+#else
+#pragma unroll
+      for (int t = 0; t < FM * FN; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, kPerMfma, 0);   // then LDS reads
       }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint4 t = lds_b[cur][swz(wn * WTN + j * 32 + lrow, kk * 2 + lk)];
-        bfr[j] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+#endif
     }
-    if (kt + 1 < nk) {
-      la.store(lds_a[cur ^ 1], tid);
-      lb.store(lds_b[cur ^ 1], tid);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto stage_ready = [&]() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  // Pipeline over k-tiles (stage s holds tile kt):
+  //   steps 0..2 of tile kt, each prefetching the next step's fragments;
+  //   wait for the next tile's copy and for every wave to finish reading
+  //   stage s (all of tile kt's fragments are in registers by now);
+  //   refill stage s with tile kt+2; step 3 of tile kt, prefetching step 0
+  //   of tile kt+1 from the other stage.
+  // The barrier thus sits before the last k-step, whose MFMAs cover the
+  // first fragment reads of the next tile.  The tile count is rounded up to
+  // even so that the two stages alternate in a branch-free loop: tiles past
+  // K (and copies issued for them) are all-zero loads that add nothing.
+  const int nk = ((p.K + kBK - 1) / kBK + 1) & ~1;
+  Frags f0, f1;
+  auto tile = [&](char* ca, char* cb, char* na, char* nb, int kt) {
+    step(f0, true, ca, cb, 1, f1);
+    step(f1, true, ca, cb, 2, f0);
+    step(f0, true, ca, cb, 3, f1);
+    stage_ready();
+    issue(ca, cb, (kt + 2) * kBK);
+    step(f1, true, na, nb, 0, f0);
+  };
+  if (nk > 0) {
+    issue(lds_a0, lds_b0, 0);
+    issue(lds_a1, lds_b1, kBK);
+    // Only tile 0 is needed now: tile 1's copies may stay in flight.
+    constexpr int kTileInstr = (BM / 8 + BN / 8) / NW;
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
+    __syncthreads();
+    load_frags(lds_a0, lds_b0, 0, f0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      tile(lds_a0, lds_b0, lds_a1, lds_b1, kt);
+      tile(lds_a1, lds_b1, lds_a0, lds_b0, kt + 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
 
   // Epilogue: lane holds m = lrow, n = 8*g + 4*lk + c for acc element 4*g + c.
@@ -257,22 +339,34 @@ hipError_t launch_bf16(const GemmParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shapes compiled in (BM x BN, 2x2 waves).
-enum TileShape : int { kTile256x128 = 0, kTile128x128 = 1, kTile128x256 = 2, kNumTiles = 3 };
+// Tile shapes compiled in.
+enum TileShape : int {
+  kTile256x256 = 0,  // 8 waves (2x4), 128 KB LDS
+  kTile256x128 = 1,  // 8 waves (4x2), 96 KB LDS
+  kTile128x256 = 2,  // 8 waves (2x4), 96 KB LDS
+  kTile128x128 = 3,  // 4 waves (2x2), 64 KB LDS
+  kTile256x256w4 = 4,  // 4 waves (2x2), one per SIMD, 128 KB LDS
+  kNumTiles = 5
+};
 
 int pick_tile(int M, int N) {
-  // Fewest full-chip waves of tiles, weighting the smaller tile as slower
-  // per flop (it re-reads operands twice as often from LDS and L2).
+#ifdef MTP_FORCE_TILE
+  if (MTP_FORCE_TILE >= 0) return MTP_FORCE_TILE;
+#endif
+  // Fewest full-chip waves of tiles, weighting smaller tiles as slower per
+  // flop (they re-read operands more often from LDS and L2).
   constexpr int kCUs = 256;
-  const int bm[kNumTiles] = {256, 128, 128};
-  const int bn[kNumTiles] = {128, 128, 256};
-  const double eff[kNumTiles] = {1.0, 0.8, 1.0};
+  const int bm[kNumTiles] = {256, 256, 128, 128, 256};
+  const int bn[kNumTiles] = {256, 128, 256, 128, 256};
+  const int per_cu[kNumTiles] = {1, 1, 1, 2, 1};
+  const double eff[kNumTiles] = {1.0, 0.9, 0.9, 0.75, 0.99};
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
     const long tiles = static_cast<long>((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
-    const long waves = (tiles + kCUs - 1) / kCUs;
-    const double cost = static_cast<double>(waves) * bm[t] * bn[t] / eff[t];
+    const long slots = static_cast<long>(kCUs) * per_cu[t];
+    const long waves = (tiles + slots - 1) / slots;
+    const double cost = static_cast<double>(waves) * per_cu[t] * bm[t] * bn[t] / eff[t];
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t; }
   }
   return best;
@@ -281,9 +375,11 @@ int pick_tile(int M, int N) {
 template <bool AK, bool BKM, int EPI>
 hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
+    case kTile256x128: return launch_bf16<256, 128, 4, 2, AK, BKM, EPI>(p, s);
+    case kTile128x256: return launch_bf16<128, 256, 2, 4, AK, BKM, EPI>(p, s);
     case kTile128x128: return launch_bf16<128, 128, 2, 2, AK, BKM, EPI>(p, s);
-    case kTile128x256: return launch_bf16<128, 256, 2, 2, AK, BKM, EPI>(p, s);
-    default: return launch_bf16<256, 128, 2, 2, AK, BKM, EPI>(p, s);
+    case kTile256x256w4: return launch_bf16<256, 256, 2, 2, AK, BKM, EPI>(p, s);
+    default: return launch_bf16<256, 256, 2, 4, AK, BKM, EPI>(p, s);
   }
 }
 
@@ -348,6 +444,15 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Bytes spanned by an operand stored with leading dimension ld: rows x ld
+// elements for the leading axis, the last row only up to its used width.
+int64_t operand_bytes(bool kmajor, int rows, int K, int64_t ld) {
+  const int64_t outer = kmajor ? rows : K;
+  const int64_t inner = kmajor ? K : rows;
+  if (outer == 0 || inner == 0) return 0;
+  return ((outer - 1) * ld + inner) * 2;
+}
+
 GemmParams to_params(const GemmDesc& g) {
   GemmParams p{};
   p.A = static_cast<const bf16_t*>(g.A); p.lda = g.lda;
@@ -366,7 +471,17 @@ GemmParams to_params(const GemmDesc& g) {
 //   wgrad   (m-major, n-major):  F32, F32Acc
 hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  const GemmParams p = to_params(g);
+  GemmParams p = to_params(g);
+  // Buffer offsets are 32-bit and the edge handling needs every valid byte
+  // offset below kOOB; the 16-byte chunks need 8-aligned rows.
+  const int64_t ab = operand_bytes(g.a_kmajor, g.M, g.K, g.lda);
+  const int64_t bb = operand_bytes(g.b_kmajor, g.N, g.K, g.ldb);
+  if (ab >= static_cast<int64_t>(kOOB) || bb >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;
+  if ((g.lda & 7) || (g.ldb & 7) || (g.a_kmajor ? (g.K & 7) : (g.M & 7)) ||
+      (g.b_kmajor ? (g.K & 7) : (g.N & 7)) || (g.N & 3))
+    return hipErrorInvalidValue;
+  p.a_bytes = static_cast<uint32_t>(ab);
+  p.b_bytes = static_cast<uint32_t>(bb);
   const int tile = (g.tile >= 0 && g.tile < kNumTiles) ? g.tile : pick_tile(g.M, g.N);
   if (g.a_kmajor && g.b_kmajor) {
     switch (g.epi) {

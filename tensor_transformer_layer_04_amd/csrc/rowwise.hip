@@ -152,15 +152,29 @@ layernorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ x,
   }
 }
 
-// out[c] (=|+=) sum_{b < nparts} part[b*cols + c], b ascending.
-__global__ void __launch_bounds__(256)
+// out[c] (=|+=) sum_{b < nparts} part[b*cols + c].  A workgroup owns 16
+// columns (64-byte rows of the partial matrix) and 16 part lanes: lane ty
+// sums parts ty, ty+16, ... in ascending order, then lane sums are added in
+// ty order, so the result does not depend on scheduling.
+constexpr int kRedCols = 16;
+constexpr int kRedLanes = 16;
+__global__ void __launch_bounds__(kRedCols * kRedLanes)
 reduce_parts_kernel(const float* __restrict__ part, int nparts, int64_t cols,
                     float* __restrict__ out, int accumulate) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float red[kRedLanes][kRedCols];
+  const int tx = threadIdx.x % kRedCols, ty = threadIdx.x / kRedCols;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCols + tx;
   float s = 0.0f;
-  for (int b = 0; b < nparts; ++b) s += part[b * cols + c];
-  out[c] = accumulate ? out[c] + s : s;
+  if (c < cols)
+    for (int b = ty; b < nparts; b += kRedLanes) s += part[static_cast<int64_t>(b) * cols + c];
+  red[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && c < cols) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRedLanes; ++i) t += red[i][tx];
+    out[c] = accumulate ? out[c] + t : t;
+  }
 }
 
 // --------------------------------------------------------------- col sums
@@ -430,10 +444,10 @@ hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* g
     if (bf16) ln_bwd_nc<bf16_t>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T, h, rpb, parts, s);
     else ln_bwd_nc<float>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T, h, rpb, parts, s);
   }
-  const dim3 g((h + 255) / 256);
-  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(256), 0, s, pg, T > 0 ? parts : 0,
+  const dim3 g((h + kRedCols - 1) / kRedCols);
+  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pg, T > 0 ? parts : 0,
                      static_cast<int64_t>(h), dgamma, accumulate ? 1 : 0);
-  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(256), 0, s, pb, T > 0 ? parts : 0,
+  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pb, T > 0 ? parts : 0,
                      static_cast<int64_t>(h), dbeta, accumulate ? 1 : 0);
   return hipGetLastError();
 }
@@ -456,7 +470,8 @@ hipError_t column_sum(bool bf16, const void* x, int64_t rows, int64_t cols, floa
       hipLaunchKernelGGL(colsum_part_kernel<float>, g, dim3(256), 0, s, cptr<float>(x), rows,
                          cols, rpb, part);
   }
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part,
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((cols + kRedCols - 1) / kRedCols),
+                     dim3(kRedCols * kRedLanes), 0, s, part,
                      static_cast<int>(rows > 0 ? parts : 0), cols, out, accumulate ? 1 : 0);
   return hipGetLastError();
 }
