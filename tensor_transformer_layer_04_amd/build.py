@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmtp.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "gemm.hip", "attention.hip", "rowwise.hip"]
+SOURCES = ["abi.hip", "gemm.hip", "attention.hip", "attention_fwd.hip", "attention_bwd.hip",
+           "rowwise.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

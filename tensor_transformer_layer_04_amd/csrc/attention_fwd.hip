@@ -1,0 +1,313 @@
+// Attention forward for bf16 shards on CDNA4 MFMA.
+//
+// Per local head n: S = q_n k_n^T / sqrt(d), key j visible to query i iff
+// start(i) <= j <= i, P = softmax(S) in fp32 (online, base 2), ctx_n = P v_n,
+// lse = natural-log log-sum-exp of each score row.  The head split needs no
+// exchange between ranks and the softmax runs in fp32 (page "Megatron-LM 3D
+// parallelism guide", §2.1 and the attention_softmax_in_fp32 flag of §3.2).
+//
+// Work decomposition (one workgroup = 4 waves, 64 queries of one head):
+//  * waves (g, h) for query group g in {0,1} (32 queries) and key half h in
+//    {0,1}: every 64-key tile is split between the two key halves, so two
+//    waves share each query group and the chip holds 2 waves per SIMD even
+//    when T x heads / 32 is only 4 waves per CU.  The halves keep separate
+//    online-softmax states and are merged exactly at the end.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 puts one query per lane (16
+//    keys each, the other 16 in lane ^ 32), so row max and row sum are
+//    in-lane plus one exchange.  P^T then feeds O^T += V^T P^T straight from
+//    registers; its contraction order is the key order the lane holds
+//    ({4g..4g+3, 8+4g..8+4g+3} per 16 keys), and V^T is gathered from the
+//    natural [key][d] tile in that order with ds_read_b64_tr_b16.
+//  * K and V tiles go HBM -> LDS with buffer_load ... lds, double-buffered;
+//    keys outside [0, T) read as zeros (buffer offset past num_records).
+//  * Scores stay in log2 units: p = exp2(s * scale * log2(e) - m) is one FMA
+//    and one v_exp_f32.  O is rescaled only when some lane's max grew.
+//  * Block ids are ordered so that block b and block b + ceil(nb/2) (placed
+//    on the same CU by the in-order dispatcher when the grid is two blocks
+//    per CU) take the longest and the shortest remaining causal row blocks.
+#include "common.h"
+#include "kernels.h"
+#include "lds_dma.h"
+
+namespace mtp {
+namespace {
+
+constexpr int kFQ = 64;  // queries per workgroup
+constexpr int kFK = 64;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct FwdParams {
+  const bf16_t* qkv;
+  int ld;  // elements per token row of qkv (3 * hl)
+  bf16_t* ctx;
+  int hl;
+  float* lse;
+  const int32_t* cu;
+  int n_seqs;
+  int T, seq_len, heads, nqb;
+  float scale_log2;
+  uint32_t qkv_bytes;
+};
+
+__device__ __forceinline__ int seq_start(const FwdParams& p, int i) {
+  if (!p.cu) return (i / p.seq_len) * p.seq_len;
+  int lo = 0, hi = p.n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return p.cu[lo];
+}
+
+// K tile: row = key, D*2 bytes; 16-byte chunk c of row r at c ^ swz_key(r).
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// V tile: row = key, D*2 bytes; 64-byte segment s of row r at s ^ swz_val(r).
+template <int D>
+__device__ __forceinline__ int swz_val(int r) {
+  return r & (D / 32 - 1);
+}
+
+// Copy keys [k0, k0+64) of one head's K (V) columns into an LDS tile.
+template <int D, bool VAL>
+__device__ __forceinline__ void issue_kv(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int lane,
+                                         int k0, int T, int col0, uint32_t ld_bytes) {
+  constexpr int kCpr = D / 8;                 // chunks per key row
+  constexpr int kInstr = kFK * kCpr / 64;     // 1 KB copies per tile
+  constexpr int kPer = kInstr / 4;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = wave * kPer + i;
+    const int q = j * 64 + lane;
+    const int row = q / kCpr, pc = q % kCpr;
+    const int lc = VAL ? (((pc >> 2) ^ swz_val<D>(row)) << 2) | (pc & 3) : pc ^ swz_key<D>(row);
+    const int key = k0 + row;
+    const uint32_t off = (key >= 0 && key < T)
+                             ? static_cast<uint32_t>(key) * ld_bytes + (col0 + lc * 8) * 2
+                             : kOOB;
+    copy16_to_lds(rs, tile + j * 1024, off);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
+  constexpr int KS = D / 16;  // k-steps of S over d
+  constexpr int DB = D / 32;  // 32-wide d blocks of O
+  constexpr int kTileBytes = kFK * D * 2;
+  __shared__ __attribute__((aligned(1024))) char sk0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sk1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sv0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sv1[kTileBytes];
+
+  const int T = p.T;
+  const int nb = gridDim.x, half = (nb + 1) / 2;
+  const int b = blockIdx.x;
+  const int item = b < half ? b : nb - 1 - (b - half);
+  const int head = item % p.heads;
+  const int qblk = p.nqb - 1 - item / p.heads;
+  const int q0 = qblk * kFQ;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qg = wave & 1, kh = wave >> 1;
+  const int lq = lane & 31, g = lane >> 5;
+  const int qa = q0 + qg * 32;            // first query of this wave
+  const int qi = qa + lq;                 // this lane's query
+  const bool qvalid = qi < T;
+  const int qstart = seq_start(p, min(qi, T - 1));
+  const int wq_last = min(qa + 31, T - 1);
+  const int w_start_lo = seq_start(p, min(qa, T - 1));
+  const int w_start_hi = seq_start(p, wq_last);
+  const int kv_lo = seq_start(p, min(q0, T - 1));
+  const int kv_hi = min(T, q0 + kFQ);
+  const int nt = (((kv_hi - kv_lo + kFK - 1) / kFK) + 1) & ~1;
+
+  const uint32_t ld_bytes = static_cast<uint32_t>(p.ld) * 2;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.qkv, p.qkv_bytes);
+  const int kcol = p.hl + head * D, vcol = 2 * p.hl + head * D;
+
+  // Q^T fragments (B operand of S^T): lane holds d = 16 s + 8 g .. +7 of
+  // query qi.
+  bf16x8 qf[KS];
+  {
+    const bf16_t* qrow = p.qkv + static_cast<int64_t>(qvalid ? qi : 0) * p.ld + head * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * g)
+                             : make_uint4(0, 0, 0, 0);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+
+  auto issue = [&](char* tk, char* tv, int k0) {
+    issue_kv<D, false>(rs, tk, wave, lane, k0, T, kcol, ld_bytes);
+    issue_kv<D, true>(rs, tv, wave, lane, k0, T, vcol, ld_bytes);
+  };
+
+  auto compute = [&](const char* tk, const char* tv, int j0) {
+    const int ja = j0 + kh * 32;  // first key of this wave's half
+    // Wave-uniform: skip when no (query, key) pair of the half is visible.
+    if (qa >= T || ja > wq_last || ja + 31 < w_start_lo) return;
+    f32x16 sacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+    const int krow = kh * 32 + lq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = 2 * s + g;
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+          tk + krow * (D * 2) + ((c ^ swz_key<D>(krow)) << 4));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+    }
+    const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = ja + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (!(qvalid && j <= qi && j >= qstart)) sacc[e] = -INFINITY;
+      }
+    }
+    float mt = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * p.scale_log2;
+    const float m_new = fmaxf(m, mt);
+    if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+      const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      m = m_new;
+    }
+    const float nm = m == -INFINITY ? 0.0f : -m;
+    uint32_t pk[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e], p.scale_log2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], p.scale_log2, nm));
+      l += p0 + p1;
+      pk[e >> 1] = pack_bf2(p0, p1);
+    }
+    // O^T += V^T P^T over the half's 32 keys, 16 per k-step.
+    const int G = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
+      const int r1 = kh * 32 + 16 * t + 4 * (G >> 1) + (s16 >> 2);
+      const int r2 = r1 + 8;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const int col = 32 * d + 16 * (G & 1) + 4 * (s16 & 3);
+        const int seg = col >> 5, within = (col & 31) * 2;
+        const v4i16 lo = tr_read(tv + r1 * (D * 2) + ((seg ^ swz_val<D>(r1)) << 6) + within);
+        const v4i16 hi = tr_read(tv + r2 * (D * 2) + ((seg ^ swz_val<D>(r2)) << 6) + within);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16x8(lo, hi), pb, o[d], 0, 0, 0);
+      }
+    }
+  };
+
+  auto stage_ready = [&]() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  issue(sk0, sv0, kv_lo);
+  issue(sk1, sv1, kv_lo + kFK);
+  {
+    constexpr int kTileInstr = 2 * (kFK * (D / 8) / 64) / 4;
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
+    __syncthreads();
+  }
+  for (int t = 0; t < nt; t += 2) {
+    const int j0 = kv_lo + t * kFK;
+    compute(sk0, sv0, j0);
+    stage_ready();
+    issue(sk0, sv0, j0 + 2 * kFK);
+    compute(sk1, sv1, j0 + kFK);
+    stage_ready();
+    issue(sk1, sv1, j0 + 3 * kFK);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Merge the two key halves of each query group.  The half-1 wave parks
+  // m, l and O in LDS (tile buffers are free now); the half-0 wave combines.
+  l += __shfl_xor(l, 32, kWave);
+  float* park_o = reinterpret_cast<float*>(qg == 0 ? sk0 : sk1);
+  float* park_ml = reinterpret_cast<float*>(sv0) + qg * 128;
+  if (kh == 1) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) park_o[(d * 16 + e) * 64 + lane] = o[d][e];
+    park_ml[lane] = m;
+    park_ml[64 + lane] = l;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = park_ml[lane], l1 = park_ml[64 + lane];
+    const float mf = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mf);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mf);
+    const float lt = l * a0 + l1 * a1;
+    if (qvalid) {
+      const float inv = 1.0f / lt;
+      bf16_t* out = p.ctx + static_cast<int64_t>(qi) * p.hl + head * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * a + c;
+            v[c] = (o[d][e] * a0 + park_o[(d * 16 + e) * 64 + lane] * a1) * inv;
+          }
+          store4(out + 32 * d + 8 * a + 4 * g, v);
+        }
+      if (g == 0)
+        p.lse[static_cast<int64_t>(head) * T + qi] = (mf + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
+  FwdParams p{};
+  p.qkv = static_cast<const bf16_t*>(a.qkv);
+  p.ld = 3 * a.heads * a.head_dim;
+  p.ctx = static_cast<bf16_t*>(a.ctx);
+  p.hl = a.heads * a.head_dim;
+  p.lse = a.lse;
+  p.cu = a.cu_seqlens;
+  p.n_seqs = a.n_seqs;
+  p.T = static_cast<int>(a.T);
+  p.seq_len = a.seq_len;
+  p.heads = a.heads;
+  p.nqb = static_cast<int>((a.T + kFQ - 1) / kFQ);
+  p.scale_log2 = kLog2e / sqrtf(static_cast<float>(a.head_dim));
+  const int64_t bytes = a.T * p.ld * 2;
+  if (bytes >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;
+  p.qkv_bytes = static_cast<uint32_t>(bytes);
+  const dim3 grid(static_cast<unsigned>(p.nqb * a.heads));
+  if (a.head_dim == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, p);
+  else if (a.head_dim == 64) hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mtp

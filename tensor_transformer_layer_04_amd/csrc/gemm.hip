@@ -34,18 +34,13 @@
 //    round-robin over the 8 XCDs) share operand panels in their L2.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace mtp {
 namespace {
 
 constexpr int kBK = 64;
 constexpr int kGroupM = 8;
-constexpr uint32_t kOOB = 0x80000000u;  // past every num_records: the load returns 0
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct GemmParams {
   const bf16_t* A; int64_t lda;
@@ -57,15 +52,6 @@ struct GemmParams {
   int tiles_m, tiles_n;
   uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31)
 };
-
-__device__ __forceinline__ lds_void* to_lds(const void* p) {
-  return (lds_void*)const_cast<void*>(p);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           static_cast<int>(kRsrcWord3));
-}
 
 // Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids
 // are dispatched round-robin over the 8 XCDs; the first step gives every XCD
@@ -128,17 +114,13 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, char* stag
       const int gk = k0 + kr, gm = row0 + lc * 8;
       off = (gk < K && gm < rmax) ? static_cast<uint32_t>(gk) * ld_bytes + gm * 2 : kOOB;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(stage + j * 1024), 16, off, 0, 0, 0);
+    copy16_to_lds(rs, stage + j * 1024, off);
   }
 }
 
 // MFMA operand (8 consecutive k of one row) from a k-major LDS tile.
 __device__ __forceinline__ bf16x8 frag_k(const char* t, int row, int c) {
   return *reinterpret_cast<const bf16x8*>(t + row * 128 + ((c ^ swz_k(row)) << 4));
-}
-
-__device__ __forceinline__ v4i16 tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<char*>(p));
 }
 
 // MFMA operand from an m/n-major LDS tile of R columns: lane l gets
@@ -151,8 +133,7 @@ __device__ __forceinline__ bf16x8 frag_m(const char* t, int rb, int kk, int lane
   const int c = m >> 3, w = (m & 7) * 2;
   const v4i16 lo = tr_read(t + k * (R * 2) + (swz_m<R>(c, k) << 4) + w);
   const v4i16 hi = tr_read(t + (k + 4) * (R * 2) + (swz_m<R>(c, k + 4) << 4) + w);
-  const v4i16 v[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, v);
+  return cat_bf16x8(lo, hi);
 }
 
 template <int EPI, typename ElemT>

@@ -62,6 +62,8 @@ struct AttnDesc {
   int64_t T; int seq_len; int heads; int head_dim;
 };
 hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t stream);
+hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t stream);
+hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t stream);
 hipError_t attn_bwd(bool bf16, const AttnDesc& a, hipStream_t stream);
 
 // ------------------------------------------------------------ vocab CE
