@@ -78,11 +78,14 @@ __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
 // 64-byte segment swizzle of an m/n-major k-row holding R elements (R/32
 // segments): the 8 k-rows {16t+0..3, 16t+8..11} (or +4) touched by one
-// transpose read map to 8 distinct segments when R >= 256.
+// transpose read map to 8 distinct segments when R >= 256.  The XOR stays
+// inside aligned groups of kP segments, kP the largest power of two that
+// divides the segment count, so every swizzled chunk stays in the row.
 template <int R>
 __device__ __forceinline__ int swz_m(int chunk, int k) {
   constexpr int kSegs = R / 32;
-  const int f = ((k & 3) | (((k >> 3) & 1) << 2)) & (kSegs - 1);
+  constexpr int kP = kSegs & -kSegs;
+  const int f = ((k & 3) | (((k >> 3) & 1) << 2)) & (kP - 1);
   return chunk ^ (f << 2);
 }
 
@@ -327,27 +330,37 @@ enum TileShape : int {
   kTile128x256 = 2,  // 8 waves (2x4), 96 KB LDS
   kTile128x128 = 3,  // 4 waves (2x2), 64 KB LDS
   kTile256x256w4 = 4,  // 4 waves (2x2), one per SIMD, 128 KB LDS
-  kNumTiles = 5
+  kTile256x192 = 5,  // 8 waves (4x2), 112 KB LDS
+  kTile192x256 = 6,  // 8 waves (2x4), 112 KB LDS
+  kNumTiles = 7
 };
 
 int pick_tile(int M, int N) {
 #ifdef MTP_FORCE_TILE
   if (MTP_FORCE_TILE >= 0) return MTP_FORCE_TILE;
 #endif
-  // Fewest full-chip waves of tiles, weighting smaller tiles as slower per
-  // flop (they re-read operands more often from LDS and L2).
+  // Cost = rounds of tiles over the 256 CUs x tile area / relative
+  // efficiency (measured on the 7B shard shapes).  128x128 tiles run two
+  // per CU, or one per CU (at lower efficiency) when they fit in one round.
   constexpr int kCUs = 256;
-  const int bm[kNumTiles] = {256, 256, 128, 128, 256};
-  const int bn[kNumTiles] = {256, 128, 256, 128, 256};
-  const int per_cu[kNumTiles] = {1, 1, 1, 2, 1};
-  const double eff[kNumTiles] = {1.0, 0.9, 0.9, 0.75, 0.99};
+  const int bm[kNumTiles] = {256, 256, 128, 128, 256, 256, 192};
+  const int bn[kNumTiles] = {256, 128, 256, 128, 256, 192, 256};
+  const int per_cu[kNumTiles] = {1, 1, 1, 2, 1, 1, 1};
+  const double eff[kNumTiles] = {1.0, 0.9, 0.92, 0.87, 0.0, 0.96, 0.96};
+  constexpr double kEffAlone128 = 0.78;
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
+    if (eff[t] <= 0.0) continue;
     const long tiles = static_cast<long>((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
-    const long slots = static_cast<long>(kCUs) * per_cu[t];
-    const long waves = (tiles + slots - 1) / slots;
-    const double cost = static_cast<double>(waves) * per_cu[t] * bm[t] * bn[t] / eff[t];
+    const double area = static_cast<double>(bm[t]) * bn[t];
+    double cost;
+    if (per_cu[t] == 2 && tiles <= kCUs) {
+      cost = area / kEffAlone128;
+    } else {
+      const long slots = static_cast<long>(kCUs) * per_cu[t];
+      cost = static_cast<double>((tiles + slots - 1) / slots) * per_cu[t] * area / eff[t];
+    }
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t; }
   }
   return best;
@@ -360,6 +373,8 @@ hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
     case kTile128x256: return launch_bf16<128, 256, 2, 4, AK, BKM, EPI>(p, s);
     case kTile128x128: return launch_bf16<128, 128, 2, 2, AK, BKM, EPI>(p, s);
     case kTile256x256w4: return launch_bf16<256, 256, 2, 2, AK, BKM, EPI>(p, s);
+    case kTile256x192: return launch_bf16<256, 192, 4, 2, AK, BKM, EPI>(p, s);
+    case kTile192x256: return launch_bf16<192, 256, 2, 4, AK, BKM, EPI>(p, s);
     default: return launch_bf16<256, 256, 2, 4, AK, BKM, EPI>(p, s);
   }
 }

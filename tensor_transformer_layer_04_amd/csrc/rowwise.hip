@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kRowThreads = 256;
 constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kMaxRegChunks = 8;  // rows are cached in registers: h <= 8*8*256
+constexpr int kMaxRowChunks = 2048;  // rows of up to 16384 elements
 
 template <typename T> __host__ __device__ __forceinline__ const T* cptr(const void* p) {
   return static_cast<const T*>(p);
@@ -31,124 +31,276 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ----------------------------------------------------------- LayerNorm fwd
-// One workgroup per token row.  Two passes over the register-cached row:
-// mean, then the centred second moment (population variance).
+// One wave per token row, four rows per workgroup; lane l owns 8-element
+// chunks l, l+64, ...  Two passes over the register-cached row (NC chunks
+// per lane; NC = 0 re-reads the row for rows wider than 4096): mean, then
+// the centred second moment (population variance), by wave shuffles.
 template <typename T, int NC>
-__global__ void __launch_bounds__(kRowThreads)
+__global__ void __launch_bounds__(256)
 layernorm_fwd_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                      const T* __restrict__ beta, T* __restrict__ y, float* __restrict__ mean,
-                     float* __restrict__ rstd, int h, float eps) {
-  __shared__ float red[kRowWaves];
-  const int64_t row = blockIdx.x;
+                     float* __restrict__ rstd, int64_t T_rows, int h, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
   const int nchunk = h / 8;
   const T* xr = x + row * h;
-  float v[NC][8];
+  constexpr int kC = NC > 0 ? NC : 1;
+  float v[kC][8];
+  const int iters = NC > 0 ? NC : (nchunk + 63) / 64;
   float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + i * kRowThreads;
+  for (int i = 0; i < iters; ++i) {
+    const int c = lane + i * 64;
     if (c < nchunk) {
-      load8(xr + c * 8, v[i]);
+      float t[8];
+      load8(xr + c * 8, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[i][e];
+      for (int e = 0; e < 8; ++e) {
+        s += t[e];
+        if (NC > 0) v[i][e] = t[e];
+      }
     }
   }
-  const float mu = block_sum(s, red) / h;
+  const float mu = warp_sum(s) / h;
   float q = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + i * kRowThreads;
+  for (int i = 0; i < iters; ++i) {
+    const int c = lane + i * 64;
     if (c < nchunk) {
+      float t[8];
+      if (NC > 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { const float d = v[i][e] - mu; q += d * d; }
+        for (int e = 0; e < 8; ++e) t[e] = v[i][e];
+      } else {
+        load8(xr + c * 8, t);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float d = t[e] - mu; q += d * d; }
     }
   }
-  const float rs = rsqrtf(block_sum(q, red) / h + eps);
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + i * kRowThreads;
+  const float rs = rsqrtf(warp_sum(q) / h + eps);
+  for (int i = 0; i < iters; ++i) {
+    const int c = lane + i * 64;
     if (c < nchunk) {
-      float g[8], b[8], o[8];
+      float t[8], g[8], b[8], o[8];
+      if (NC > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = v[i][e];
+      } else {
+        load8(xr + c * 8, t);
+      }
       load8(gamma + c * 8, g);
       load8(beta + c * 8, b);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rs * g[e] + b[e];
+      for (int e = 0; e < 8; ++e) o[e] = (t[e] - mu) * rs * g[e] + b[e];
       store8(y + row * h + c * 8, o);
     }
   }
-  if (threadIdx.x == 0) { mean[row] = mu; rstd[row] = rs; }
+  if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
 }
 
 // ----------------------------------------------------------- LayerNorm bwd
-// Workgroup b handles rows [b*rpb, (b+1)*rpb).  Per row:
+// Row pass: one wave per token row, four rows per workgroup, the two row
+// means by wave shuffles only (no barrier):
 //   xhat = (x-mu)*rstd, gh = dy*gamma,
 //   dx = rstd*(gh - mean(gh) - xhat*mean(gh*xhat)) (+ dres).
-// Column partial sums of dy*xhat and dy over the workgroup's rows go to ws;
-// reduce_parts_kernel adds the partials in workgroup order.
+// Lane l owns 8-element chunks l, l+64, ...  With NC > 0 the row's xhat and
+// gh stay in registers (NC chunks per lane); NC = 0 re-reads x and dy for
+// the second pass (rows wider than 4096).
 template <typename T, int NC>
-__global__ void __launch_bounds__(kRowThreads)
-layernorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ x,
-                     const T* __restrict__ gamma, const float* __restrict__ mean,
-                     const float* __restrict__ rstd, const T* __restrict__ dres,
-                     T* __restrict__ dx, float* __restrict__ part_g, float* __restrict__ part_b,
-                     int64_t T_rows, int h, int rpb) {
-  __shared__ float red[kRowWaves];
+__global__ void __launch_bounds__(256)
+layernorm_bwd_rows_kernel(const T* __restrict__ dy, const T* __restrict__ x,
+                          const T* __restrict__ gamma, const float* __restrict__ mean,
+                          const float* __restrict__ rstd, const T* __restrict__ dres,
+                          T* __restrict__ dx, int64_t T_rows, int h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
   const int nchunk = h / 8;
-  float accg[NC][8], accb[NC][8];
+  const float mu = mean[row], rs = rstd[row];
+  const T* xr = x + row * h;
+  const T* dr = dy + row * h;
+  constexpr int kC = NC > 0 ? NC : 1;
+  float xh[kC][8], gh[kC][8];
+  float s1 = 0.0f, s2 = 0.0f;
+  const int iters = NC > 0 ? NC : (nchunk + 63) / 64;
+  for (int i = 0; i < iters; ++i) {
+    const int c = lane + i * 64;
+    if (c < nchunk) {
+      float xv[8], dv[8], gv[8];
+      load8(xr + c * 8, xv);
+      load8(dr + c * 8, dv);
+      load8(gamma + c * 8, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = (xv[e] - mu) * rs, g = dv[e] * gv[e];
+        s1 += g;
+        s2 += g * a;
+        if (NC > 0) { xh[i][e] = a; gh[i][e] = g; }
+      }
+    }
+  }
+  const float m1 = warp_sum(s1) / h, m2 = warp_sum(s2) / h;
+  for (int i = 0; i < iters; ++i) {
+    const int c = lane + i * 64;
+    if (c < nchunk) {
+      float a[8], g[8], o[8];
+      if (NC > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] = xh[i][e]; g[e] = gh[i][e]; }
+      } else {
+        float xv[8], dv[8], gv[8];
+        load8(xr + c * 8, xv);
+        load8(dr + c * 8, dv);
+        load8(gamma + c * 8, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] = (xv[e] - mu) * rs; g[e] = dv[e] * gv[e]; }
+      }
+      if (dres) {
+        load8(dres + row * h + c * 8, o);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += rs * (g[e] - m1 - a[e] * m2);
+      store8(dx + row * h + c * 8, o);
+    }
+  }
+}
+
+// bf16 rows whose width is a multiple of 512 (NC = h/512 chunks per lane):
+// the same arithmetic with every load of the row issued before any use and
+// the raw bf16 words kept in registers (4 VGPRs per 8 elements).
+__device__ __forceinline__ float bfw(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? hi_bf(w) : lo_bf(w);
+}
+
+template <int NC>
+__global__ void __launch_bounds__(256)
+layernorm_fwd_bf16_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+                          const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
+                          float* __restrict__ mean, float* __restrict__ rstd, int64_t T_rows,
+                          int h, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * h);
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) v[i] = xr[lane + 64 * i];
+  float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < NC; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { accg[i][e] = 0.0f; accb[i][e] = 0.0f; }
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
-  const int64_t r1 = min(T_rows, r0 + rpb);
-  for (int64_t row = r0; row < r1; ++row) {
-    const float mu = mean[row], rs = rstd[row];
-    float xh[NC][8], gh[NC][8];
-    float s1 = 0.0f, s2 = 0.0f;
+    for (int e = 0; e < 8; ++e) s += bfw(v[i], e);
+  const float mu = warp_sum(s) / h;
+  float q = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = threadIdx.x + i * kRowThreads;
-      if (c < nchunk) {
-        float xv[8], dv[8], gv[8];
-        load8(x + row * h + c * 8, xv);
-        load8(dy + row * h + c * 8, dv);
-        load8(gamma + c * 8, gv);
+  for (int i = 0; i < NC; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xh[i][e] = (xv[e] - mu) * rs;
-          gh[i][e] = dv[e] * gv[e];
-          s1 += gh[i][e];
-          s2 += gh[i][e] * xh[i][e];
-          accg[i][e] += dv[e] * xh[i][e];
-          accb[i][e] += dv[e];
-        }
-      }
+    for (int e = 0; e < 8; ++e) { const float d = bfw(v[i], e) - mu; q += d * d; }
+  const float rs = rsqrtf(warp_sum(q) / h + eps);
+  const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+  const uint4* br = reinterpret_cast<const uint4*>(beta);
+  uint4* yr = reinterpret_cast<uint4*>(y + row * h);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint4 g = gr[lane + 64 * i], b = br[lane + 64 * i];
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bfw(v[i], e) - mu) * rs * bfw(g, e) + bfw(b, e);
+    yr[lane + 64 * i] = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]),
+                                   pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
+  }
+  if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+}
+
+template <int NC>
+__global__ void __launch_bounds__(256)
+layernorm_bwd_rows_bf16_kernel(const bf16_t* __restrict__ dy, const bf16_t* __restrict__ x,
+                               const bf16_t* __restrict__ gamma, const float* __restrict__ mean,
+                               const float* __restrict__ rstd, const bf16_t* __restrict__ dres,
+                               bf16_t* __restrict__ dx, int64_t T_rows, int h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
+  const float mu = mean[row], rs = rstd[row];
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * h);
+  const uint4* dr = reinterpret_cast<const uint4*>(dy + row * h);
+  const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+  uint4 xv[NC], dv[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) { xv[i] = xr[lane + 64 * i]; dv[i] = dr[lane + 64 * i]; }
+  float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint4 g = gr[lane + 64 * i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = (bfw(xv[i], e) - mu) * rs, gh = bfw(dv[i], e) * bfw(g, e);
+      s1 += gh;
+      s2 += gh * a;
     }
-    const float m1 = block_sum(s1, red) / h;
-    const float m2 = block_sum(s2, red) / h;
+  }
+  const float m1 = warp_sum(s1) / h, m2 = warp_sum(s2) / h;
+  const uint4* rr = reinterpret_cast<const uint4*>(dres + row * h);
+  uint4* outr = reinterpret_cast<uint4*>(dx + row * h);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c = threadIdx.x + i * kRowThreads;
-      if (c < nchunk) {
-        float o[8];
-        if (dres) load8(dres + row * h + c * 8, o);
-        else {
+  for (int i = 0; i < NC; ++i) {
+    const uint4 g = gr[lane + 64 * i];
+    const uint4 rv = dres ? rr[lane + 64 * i] : make_uint4(0, 0, 0, 0);
+    float o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-        }
+    for (int e = 0; e < 8; ++e) {
+      const float a = (bfw(xv[i], e) - mu) * rs, gh = bfw(dv[i], e) * bfw(g, e);
+      o[e] = bfw(rv, e) + rs * (gh - m1 - a * m2);
+    }
+    outr[lane + 64 * i] = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]),
+                                     pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
+  }
+}
+
+// Column pass: part_g[p][c] = sum over the rows of part p of dy*xhat,
+// part_b[p][c] = sum of dy (rows ascending within a thread, the four row
+// lanes added in order).  Workgroup (bx, by): columns [512 bx, 512 bx + 512),
+// rows [by*rpb, (by+1)*rpb); 64 threads x 8 columns x 4 row lanes.
+template <typename T>
+__global__ void __launch_bounds__(256)
+layernorm_bwd_cols_kernel(const T* __restrict__ dy, const T* __restrict__ x,
+                          const float* __restrict__ mean, const float* __restrict__ rstd,
+                          int64_t rows, int h, int rpb, float* __restrict__ part_g,
+                          float* __restrict__ part_b) {
+  __shared__ float red[2][4][512];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 512 + tx * 8;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rpb;
+  const int64_t r1 = min(rows, r0 + rpb);
+  float ag[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ab[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c < h) {
+#pragma unroll 8
+    for (int64_t r = r0 + ty; r < r1; r += 4) {
+      const float mu = mean[r], rs = rstd[r];
+      float xv[8], dv[8];
+      load8(x + r * h + c, xv);
+      load8(dy + r * h + c, dv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += rs * (gh[i][e] - m1 - xh[i][e] * m2);
-        store8(dx + row * h + c * 8, o);
+      for (int e = 0; e < 8; ++e) {
+        ag[e] += dv[e] * ((xv[e] - mu) * rs);
+        ab[e] += dv[e];
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = threadIdx.x + i * kRowThreads;
-    if (c < nchunk) {
-      store8(part_g + static_cast<int64_t>(blockIdx.x) * h + c * 8, accg[i]);
-      store8(part_b + static_cast<int64_t>(blockIdx.x) * h + c * 8, accb[i]);
-    }
+  for (int e = 0; e < 8; ++e) { red[0][ty][tx * 8 + e] = ag[e]; red[1][ty][tx * 8 + e] = ab[e]; }
+  __syncthreads();
+  if (ty < 2 && c < h) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o[e] = red[ty][0][tx * 8 + e] + red[ty][1][tx * 8 + e] + red[ty][2][tx * 8 + e] +
+             red[ty][3][tx * 8 + e];
+    store8((ty == 0 ? part_g : part_b) + static_cast<int64_t>(blockIdx.y) * h + c, o);
   }
 }
 
@@ -159,8 +311,12 @@ layernorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ x,
 constexpr int kRedCols = 16;
 constexpr int kRedLanes = 16;
 __global__ void __launch_bounds__(kRedCols * kRedLanes)
-reduce_parts_kernel(const float* __restrict__ part, int nparts, int64_t cols,
-                    float* __restrict__ out, int accumulate) {
+reduce_parts_kernel(const float* __restrict__ part0, float* __restrict__ out0,
+                    const float* __restrict__ part1, float* __restrict__ out1, int nparts,
+                    int64_t cols, int accumulate) {
+  // blockIdx.y selects one of two independent (part, out) pairs.
+  const float* part = blockIdx.y == 0 ? part0 : part1;
+  float* out = blockIdx.y == 0 ? out0 : out1;
   __shared__ float red[kRedLanes][kRedCols];
   const int tx = threadIdx.x % kRedCols, ty = threadIdx.x / kRedCols;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCols + tx;
@@ -191,6 +347,7 @@ colsum_part_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, int rpb,
   const int64_t r1 = min(rows, r0 + rpb);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c < cols) {
+#pragma unroll 8
     for (int64_t r = r0 + ty; r < r1; r += 4) {
       float v[8];
       load8(x + r * cols + c, v);
@@ -353,13 +510,7 @@ int grid_for(int64_t nvec) {
   return static_cast<int>(b < 8192 ? (b > 0 ? b : 1) : 8192);
 }
 
-int ln_bwd_parts(int64_t T) {
-  int64_t parts = (T + 7) / 8;
-  if (parts > 512) parts = 512;
-  return static_cast<int>(parts);
-}
-
-constexpr int kColRowsPerPart = 64;
+constexpr int kColRowsPerPart = 32;
 
 int64_t colsum_parts(int64_t rows) {
   int64_t p = (rows + kColRowsPerPart - 1) / kColRowsPerPart;
@@ -367,52 +518,70 @@ int64_t colsum_parts(int64_t rows) {
 }
 
 // ---------------------------------------------------------------- launchers
-// Register chunks per thread for a row of h elements (8 per chunk).
-int reg_chunks(int h) {
-  const int per = (h / 8 + kRowThreads - 1) / kRowThreads;
-  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 6 ? 6 : 8;
-}
 
-template <typename T, int NC>
-void launch_ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
-                   float* rstd, int64_t T_rows, int h, float eps, hipStream_t s) {
-  hipLaunchKernelGGL((layernorm_fwd_kernel<T, NC>), dim3(T_rows), dim3(kRowThreads), 0, s,
-                     cptr<T>(x), cptr<T>(gamma), cptr<T>(beta), static_cast<T*>(y), mean, rstd,
-                     h, eps);
+template <typename T>
+void ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+            float* rstd, int64_t T_rows, int h, float eps, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T_rows + 3) / 4));
+  const int per_lane = (h / 8 + 63) / 64;
+  if (sizeof(T) == 2 && h % 512 == 0 && per_lane <= 16) {
+#define MTP_LN_FWD16(NC)                                                                     \
+  hipLaunchKernelGGL((layernorm_fwd_bf16_kernel<NC>), grid, dim3(256), 0, s, cptr<bf16_t>(x), \
+                     cptr<bf16_t>(gamma), cptr<bf16_t>(beta), static_cast<bf16_t*>(y), mean, \
+                     rstd, T_rows, h, eps)
+    switch (per_lane) {
+      case 1: MTP_LN_FWD16(1); return;
+      case 2: MTP_LN_FWD16(2); return;
+      case 4: MTP_LN_FWD16(4); return;
+      case 8: MTP_LN_FWD16(8); return;
+      case 16: MTP_LN_FWD16(16); return;
+      default: break;
+    }
+#undef MTP_LN_FWD16
+  }
+#define MTP_LN_FWD(NC)                                                                       \
+  hipLaunchKernelGGL((layernorm_fwd_kernel<T, NC>), grid, dim3(256), 0, s, cptr<T>(x),          \
+                     cptr<T>(gamma), cptr<T>(beta), static_cast<T*>(y), mean, rstd, T_rows, h, \
+                     eps)
+  if (per_lane <= 1) MTP_LN_FWD(1);
+  else if (per_lane <= 2) MTP_LN_FWD(2);
+  else if (per_lane <= 4) MTP_LN_FWD(4);
+  else if (per_lane <= 8) MTP_LN_FWD(8);
+  else MTP_LN_FWD(0);
+#undef MTP_LN_FWD
 }
 
 template <typename T>
-void ln_fwd_nc(const void* x, const void* gamma, const void* beta, void* y, float* mean,
-               float* rstd, int64_t T_rows, int h, float eps, hipStream_t s) {
-  switch (reg_chunks(h)) {
-    case 1: launch_ln_fwd<T, 1>(x, gamma, beta, y, mean, rstd, T_rows, h, eps, s); break;
-    case 2: launch_ln_fwd<T, 2>(x, gamma, beta, y, mean, rstd, T_rows, h, eps, s); break;
-    case 4: launch_ln_fwd<T, 4>(x, gamma, beta, y, mean, rstd, T_rows, h, eps, s); break;
-    case 6: launch_ln_fwd<T, 6>(x, gamma, beta, y, mean, rstd, T_rows, h, eps, s); break;
-    default: launch_ln_fwd<T, 8>(x, gamma, beta, y, mean, rstd, T_rows, h, eps, s); break;
+void ln_bwd_rows(const void* dy, const void* x, const void* gamma, const float* mean,
+                 const float* rstd, const void* dres, void* dx, int64_t T_rows, int h,
+                 hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T_rows + 3) / 4));
+  const int per_lane = (h / 8 + 63) / 64;
+  if (sizeof(T) == 2 && h % 512 == 0 && per_lane <= 16) {
+#define MTP_LN_BWD16(NC)                                                                      \
+  hipLaunchKernelGGL((layernorm_bwd_rows_bf16_kernel<NC>), grid, dim3(256), 0, s,               \
+                     cptr<bf16_t>(dy), cptr<bf16_t>(x), cptr<bf16_t>(gamma), mean, rstd,       \
+                     cptr<bf16_t>(dres), static_cast<bf16_t*>(dx), T_rows, h)
+    switch (per_lane) {
+      case 1: MTP_LN_BWD16(1); return;
+      case 2: MTP_LN_BWD16(2); return;
+      case 4: MTP_LN_BWD16(4); return;
+      case 8: MTP_LN_BWD16(8); return;
+      case 16: MTP_LN_BWD16(16); return;
+      default: break;
+    }
+#undef MTP_LN_BWD16
   }
-}
-
-template <typename T, int NC>
-void launch_ln_bwd(const void* dy, const void* x, const void* gamma, const float* mean,
-                   const float* rstd, const void* dres, void* dx, float* pg, float* pb,
-                   int64_t T_rows, int h, int rpb, int parts, hipStream_t s) {
-  hipLaunchKernelGGL((layernorm_bwd_kernel<T, NC>), dim3(parts), dim3(kRowThreads), 0, s,
-                     cptr<T>(dy), cptr<T>(x), cptr<T>(gamma), mean, rstd, cptr<T>(dres),
-                     static_cast<T*>(dx), pg, pb, T_rows, h, rpb);
-}
-
-template <typename T>
-void ln_bwd_nc(const void* dy, const void* x, const void* gamma, const float* mean,
-               const float* rstd, const void* dres, void* dx, float* pg, float* pb,
-               int64_t T_rows, int h, int rpb, int parts, hipStream_t s) {
-  switch (reg_chunks(h)) {
-    case 1: launch_ln_bwd<T, 1>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T_rows, h, rpb, parts, s); break;
-    case 2: launch_ln_bwd<T, 2>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T_rows, h, rpb, parts, s); break;
-    case 4: launch_ln_bwd<T, 4>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T_rows, h, rpb, parts, s); break;
-    case 6: launch_ln_bwd<T, 6>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T_rows, h, rpb, parts, s); break;
-    default: launch_ln_bwd<T, 8>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T_rows, h, rpb, parts, s); break;
-  }
+#define MTP_LN_BWD_ROWS(NC)                                                                  \
+  hipLaunchKernelGGL((layernorm_bwd_rows_kernel<T, NC>), grid, dim3(256), 0, s, cptr<T>(dy),  \
+                     cptr<T>(x), cptr<T>(gamma), mean, rstd, cptr<T>(dres),                 \
+                     static_cast<T*>(dx), T_rows, h)
+  if (per_lane <= 1) MTP_LN_BWD_ROWS(1);
+  else if (per_lane <= 2) MTP_LN_BWD_ROWS(2);
+  else if (per_lane <= 4) MTP_LN_BWD_ROWS(4);
+  else if (per_lane <= 8) MTP_LN_BWD_ROWS(8);
+  else MTP_LN_BWD_ROWS(0);
+#undef MTP_LN_BWD_ROWS
 }
 
 }  // namespace
@@ -421,34 +590,40 @@ hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void
                          float* mean, float* rstd, int64_t T, int h, float eps,
                          hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (h / 8 > kRowThreads * kMaxRegChunks) return hipErrorInvalidValue;
-  if (bf16) ln_fwd_nc<bf16_t>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
-  else ln_fwd_nc<float>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
+  if (h / 8 > kMaxRowChunks) return hipErrorInvalidValue;
+  if (bf16) ln_fwd<bf16_t>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
+  else ln_fwd<float>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
   return hipGetLastError();
 }
 
 size_t layernorm_bwd_ws_bytes(int64_t T, int h) {
-  return static_cast<size_t>(ln_bwd_parts(T)) * h * 2 * sizeof(float);
+  return static_cast<size_t>(colsum_parts(T)) * h * 2 * sizeof(float);
 }
 
 hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* gamma,
                          const float* mean, const float* rstd, const void* dres, void* dx,
                          float* dgamma, float* dbeta, bool accumulate, int64_t T, int h,
                          void* ws, hipStream_t s) {
-  if (h / 8 > kRowThreads * kMaxRegChunks) return hipErrorInvalidValue;
-  const int parts = ln_bwd_parts(T);
+  if (h / 8 > kMaxRowChunks) return hipErrorInvalidValue;
+  const int64_t parts = colsum_parts(T);
   float* pg = static_cast<float*>(ws);
-  float* pb = pg + static_cast<int64_t>(parts) * h;
+  float* pb = pg + parts * h;
   if (T > 0) {
+    if (bf16) ln_bwd_rows<bf16_t>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
+    else ln_bwd_rows<float>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
     const int rpb = static_cast<int>((T + parts - 1) / parts);
-    if (bf16) ln_bwd_nc<bf16_t>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T, h, rpb, parts, s);
-    else ln_bwd_nc<float>(dy, x, gamma, mean, rstd, dres, dx, pg, pb, T, h, rpb, parts, s);
+    const dim3 g((h + 511) / 512, static_cast<unsigned>(parts));
+    if (bf16)
+      hipLaunchKernelGGL(layernorm_bwd_cols_kernel<bf16_t>, g, dim3(256), 0, s, cptr<bf16_t>(dy),
+                         cptr<bf16_t>(x), mean, rstd, T, h, rpb, pg, pb);
+    else
+      hipLaunchKernelGGL(layernorm_bwd_cols_kernel<float>, g, dim3(256), 0, s, cptr<float>(dy),
+                         cptr<float>(x), mean, rstd, T, h, rpb, pg, pb);
   }
-  const dim3 g((h + kRedCols - 1) / kRedCols);
-  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pg, T > 0 ? parts : 0,
-                     static_cast<int64_t>(h), dgamma, accumulate ? 1 : 0);
-  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pb, T > 0 ? parts : 0,
-                     static_cast<int64_t>(h), dbeta, accumulate ? 1 : 0);
+  const dim3 g((h + kRedCols - 1) / kRedCols, 2);
+  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
+                     dbeta, static_cast<int>(T > 0 ? parts : 0), static_cast<int64_t>(h),
+                     accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -470,9 +645,9 @@ hipError_t column_sum(bool bf16, const void* x, int64_t rows, int64_t cols, floa
       hipLaunchKernelGGL(colsum_part_kernel<float>, g, dim3(256), 0, s, cptr<float>(x), rows,
                          cols, rpb, part);
   }
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((cols + kRedCols - 1) / kRedCols),
-                     dim3(kRedCols * kRedLanes), 0, s, part,
-                     static_cast<int>(rows > 0 ? parts : 0), cols, out, accumulate ? 1 : 0);
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((cols + kRedCols - 1) / kRedCols, 1),
+                     dim3(kRedCols * kRedLanes), 0, s, part, out, part, out,
+                     static_cast<int>(rows > 0 ? parts : 0), cols, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
