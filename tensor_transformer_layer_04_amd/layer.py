@@ -81,7 +81,7 @@ class TPLayer:
     """One pre-LN layer, ``ranks`` of its ``cfg.tp`` shards computed here."""
 
     def __init__(self, cfg, full: Dict[str, torch.Tensor], ranks: Optional[Sequence[int]] = None,
-                 device="cuda", cu_seqlens: Optional[torch.Tensor] = None):
+                 device="cuda", cu_seqlens: Optional[torch.Tensor] = None, overlap: bool = True):
         self.cfg = cfg
         self.device = torch.device(device)
         self.ranks = list(range(cfg.tp)) if ranks is None else list(ranks)
@@ -96,6 +96,10 @@ class TPLayer:
         if cu_seqlens is not None and cfg.varlen_tokens:
             self.cu = cu_seqlens.to(device=self.device, dtype=torch.int32).contiguous()
             self.n_seqs = self.cu.numel() - 1
+        # Weight and bias gradients are off the backward's critical path: with
+        # ``overlap`` they run on a second stream (default priority) next to
+        # the data gradients, joined back before backward() returns.
+        self.side = torch.cuda.Stream(device=self.device) if overlap else None
         self._alloc()
 
     # ------------------------------------------------------------ buffers
@@ -134,22 +138,25 @@ class TPLayer:
             256)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
+        # the side stream gets a workspace of its own
+        self.ws_side = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
         # Optional timing probe: {tag: [(start_event, end_event), ...]} for the
         # tags present as keys; events are recorded on the current stream.
         self.probe: Optional[Dict[str, list]] = None
 
     @contextlib.contextmanager
-    def _timed(self, tag: str):
+    def _timed(self, tag: str, stream=None):
         pr = self.probe
         if pr is None or tag not in pr:
             yield
             return
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        a.record()
+        a.record(st)
         yield
-        b.record()
+        b.record(st)
         pr[tag].append((a, b))
 
     # ------------------------------------------------------------ forward
@@ -192,23 +199,41 @@ class TPLayer:
         ext = external or {}
         d0, rep, ws, wsb = self.d0, self.rep, self.ws, self.ws_bytes
         T = self._timed
+        main = torch.cuda.current_stream(self.device)
+        side = self.side
+        wss = self.ws_side if side is not None else ws
+
+        def fork():
+            """Point the side stream past everything issued on main so far."""
+            if side is not None:
+                side.wait_stream(main)
+
+        def on_side():
+            return torch.cuda.stream(side) if side is not None else contextlib.nullcontext()
+
         # Each linear map's backward is issued as two calls: the data gradient
-        # (with the bias gradient) and the weight gradient.
+        # on the main stream and the weight + bias gradients on the side one.
+        fork()
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
             db2 = self.rgrads["db2"] if r == self.owns_bias else None
             with T("fc2_dgrad"):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], None,
-                                       db2, 0, ws, wsb)
-            with T("fc2_wgrad"):
-                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, g["dw2"],
                                        None, 0, ws, wsb)
+            with on_side(), T("fc2_wgrad", side):
+                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, g["dw2"],
+                                       None, 0, wss, wsb)
+            if db2 is not None:
+                with on_side():
+                    mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
+                                           db2, 0, wss, wsb)
             with T("fc1_dgrad"):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
-                                       g["db1"], 0, ws, wsb)
-            with T("fc1_wgrad"):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
                                        None, 0, ws, wsb)
+            fork()
+            with on_side(), T("fc1_wgrad", side):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
+                                       g["db1"], 0, wss, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
         with T("sum_fc1_dx"):
             mtp.mtp_partial_sum(d0, parts, None, None, self.dln2_sum)
@@ -216,24 +241,26 @@ class TPLayer:
             mtp.mtp_layernorm_bwd(d0, self.dln2_sum, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
                                   self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws,
                                   wsb)
+        fork()
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
             dbo = self.rgrads["dbo"] if r == self.owns_bias else None
             with T("proj_dgrad"):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
-                                       a["dctx"], None, dbo, 0, ws, wsb)
-            with T("proj_wgrad"):
+                                       a["dctx"], None, None, 0, ws, wsb)
+            with on_side(), T("proj_wgrad", side):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None, None,
-                                       g["dwo"], None, 0, ws, wsb)
+                                       g["dwo"], dbo, 0, wss, wsb)
             with T("attn_bwd"):
                 mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
                                  self.n_seqs, ws, wsb)
             with T("qkv_dgrad"):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
-                                       None, g["dbqkv"], 0, ws, wsb)
-            with T("qkv_wgrad"):
+                                       None, None, 0, ws, wsb)
+            fork()
+            with on_side(), T("qkv_wgrad", side):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
-                                       g["dwqkv"], None, 0, ws, wsb)
+                                       g["dwqkv"], g["dbqkv"], 0, wss, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
         with T("sum_qkv_dx"):
             mtp.mtp_partial_sum(d0, parts, None, None, self.dln1_sum)
@@ -241,6 +268,8 @@ class TPLayer:
             mtp.mtp_layernorm_bwd(d0, self.dln1_sum, self.x, rep["ln1_g"], self.mu1, self.rs1,
                                   self.dy1, self.dx, self.rgrads["dln1_g"], self.rgrads["dln1_b"],
                                   0, ws, wsb)
+        if side is not None:
+            main.wait_stream(side)
         return self.dx
 
     def partials(self) -> Dict[str, List[torch.Tensor]]:
