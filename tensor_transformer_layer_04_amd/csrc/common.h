@@ -100,20 +100,21 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 in[8], uint4 out[8
   }
 }
 
-// GeLU, tanh form, and its derivative (fp32).  tanh(z) = 1 - 2/(exp(2z)+1).
-__device__ __forceinline__ float tanh_fast(float z) {
-  const float e = __expf(2.0f * z);
-  return 1.0f - 2.0f / (e + 1.0f);
-}
+// GeLU, tanh form, and its derivative (fp32).  With z = c (u + a u^3),
+// 0.5 (1 + tanh(z)) = sigmoid(2 z), so GeLU(u) = u * s with
+// s = 1 / (1 + exp(-2 z)) (one v_exp_f32 and one v_rcp_f32), and
+// GeLU'(u) = s + u s (1 - s) 2 c (1 + 3 a u^2).
 constexpr float kGeluC = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float kGeluA = 0.044715f;
-__device__ __forceinline__ float gelu_tanh(float u) {
-  const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
-  return 0.5f * u * (1.0f + t);
+constexpr float kGeluK = -2.0f * kGeluC * 1.4426950408889634f;  // -2 c log2(e)
+__device__ __forceinline__ float gelu_sigmoid(float u) {
+  const float t = kGeluK * u * fmaf(kGeluA * u, u, 1.0f);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
+__device__ __forceinline__ float gelu_tanh(float u) { return u * gelu_sigmoid(u); }
 __device__ __forceinline__ float gelu_tanh_grad(float u) {
-  const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
-  return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluC * (1.0f + 3.0f * kGeluA * u * u);
+  const float s = gelu_sigmoid(u);
+  return s * fmaf(u * (1.0f - s) * (2.0f * kGeluC), fmaf(3.0f * kGeluA * u, u, 1.0f), 1.0f);
 }
 
 __device__ __forceinline__ float warp_sum(float v) {

@@ -292,21 +292,46 @@ gemm_bf16_kernel(GemmParams p) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
 
-  // Epilogue: lane holds m = lrow, n = 8*g + 4*lk + c for acc element 4*g + c.
+  // Epilogue, staged through LDS one 32x32 block at a time: the wave writes
+  // its accumulators (lane: row lrow, columns 8g + 4lk .. +3 of acc element
+  // 4g..4g+3) row-major into a private LDS region, then reads them back as
+  // row segments, so every global store (and every load of C or of the
+  // GeLU pre-activation) covers 8 rows x 32 contiguous columns.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with the stage buffers
+  constexpr int kPitch = 36;  // floats per staged row: 32 + 4 (bank spread)
+  constexpr int kRegion = 32 * kPitch * 4;
+  constexpr int kPerBuf = NW / 4;
+  static_assert(kPerBuf * kRegion <= (BM < BN ? BM : BN) * 128, "epilogue staging does not fit");
+  char* const base = (wave / kPerBuf) == 0 ? lds_a0
+                   : (wave / kPerBuf) == 1 ? lds_a1
+                   : (wave / kPerBuf) == 2 ? lds_b0 : lds_b1;
+  float* stage = reinterpret_cast<float*>(base + (wave % kPerBuf) * kRegion);
+  const int sr = lane >> 3, sc = (lane & 7) * 4;  // read-back row offset / column
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + lrow;
-    if (m >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * lk;
-        if (n < p.N) {
-          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                        acc[i][j][4 * g + 3]};
-          epi_apply<EPI, bf16_t>(p, m, n, v);
-        }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(stage + lrow * kPitch + 8 * g + 4 * lk) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                  acc[i][j][4 * g + 3]};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      float v[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(stage + (8 * r + sr) * kPitch + sc);
+        v[r][0] = t[0]; v[r][1] = t[1]; v[r][2] = t[2]; v[r][3] = t[3];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      const int n = n0 + wn * WTN + j * 32 + sc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * WTM + i * 32 + 8 * r + sr;
+        if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
       }
     }
   }
