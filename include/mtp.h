@@ -198,7 +198,9 @@ int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* 
 
 /* Attention backward: given qkv, ctx and lse from mtp_attn_fwd and dctx
  * [T,h_l], writes dqkv [T,3h_l] dtype = [dq | dk | dv] in the qkv layout.
- * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ATTN_BWD, 0).           */
+ * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ATTN_BWD, 0) (= two fp32
+ * values per local head and token: D = rowsum(dctx * ctx) and the
+ * log-sum-exp in base 2).                                                    */
 int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                  const float* lse, const void* dctx, void* dqkv,
                  const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,

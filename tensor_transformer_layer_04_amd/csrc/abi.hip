@@ -107,7 +107,7 @@ size_t mtp_workspace_size(const mtp_shard_desc* desc, int op, int kind) {
     }
     case MTP_OP_ROW_LINEAR_BWD:
       return row_in(s, kind) > 0 ? mtp::column_sum_ws_bytes(s.T, s.h) : 0;
-    case MTP_OP_ATTN_BWD: return static_cast<size_t>(s.al) * s.T * sizeof(float);
+    case MTP_OP_ATTN_BWD: return static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
     default: return 0;
   }
 }
@@ -282,7 +282,7 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, c
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
     return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
-  const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float);
+  const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);

@@ -53,7 +53,9 @@ __device__ __forceinline__ int seq_end(const AttnParams& p, int i) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // -------------------------------------------------- backward preprocess
-// delta[n][i] = sum_d dctx[i, n*D + d] * ctx[i, n*D + d]  (= rowsum(P * dP)).
+// delta[n][i] = sum_d dctx[i, n*D + d] * ctx[i, n*D + d]  (= rowsum(P * dP)),
+// and (bf16 path) lse2[n][i] = lse[n][i] * log2(e) right after delta in the
+// workspace, so the MFMA passes get exp(S - lse) as exp2(S*scale*log2e - lse2).
 template <typename T>
 __global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D) {
   const int per_row = D / 8;                 // threads per (token, head)
@@ -73,7 +75,11 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D) {
     for (int e = 0; e < 8; ++e) acc += a[e] * b[e];
   }
   for (int o = per_row / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-  if (c == 0 && pair < static_cast<int64_t>(p.T) * p.heads) p.delta[static_cast<int64_t>(n) * p.T + i] = acc;
+  if (c == 0 && pair < static_cast<int64_t>(p.T) * p.heads) {
+    const int64_t at = static_cast<int64_t>(n) * p.T + i;
+    p.delta[at] = acc;
+    if (sizeof(T) == 2) p.delta[static_cast<int64_t>(p.heads) * p.T + at] = p.lse[at] * kLog2e;
+  }
 }
 
 // row max and sum, pass 2 accumulates P v in chunks of 64 keys via LDS.

@@ -40,7 +40,7 @@ struct BwdParams {
   int ld;  // 3 * hl
   const bf16_t* dctx;
   int hl;
-  const float* lse;    // [heads, T] natural log
+  const float* lse;    // [heads, T] log-sum-exp times log2(e)
   const float* delta;  // [heads, T]
   bf16_t* dqkv;
   const int32_t* cu;
@@ -136,8 +136,15 @@ __device__ __forceinline__ int balanced_item(int b, int nb) {
 }
 
 // ----------------------------------------------------------------- dK / dV
+// Key-major pass.  Every key block is handled by two workgroups: one
+// accumulates dV^T += dO^T P (needs S only), the other dK^T += Q^T dS (needs
+// S and dP).  Each then holds one 32 x D accumulator per wave instead of
+// two, which leaves room for two waves per SIMD; the two roles run side by
+// side on the chip.  Per 64-query tile and wave (32 keys, 32 query rows of
+// the tile): S = Q K^T [, dP = dO V^T] with one key per lane, P / dS on the
+// vector units, then the transposed-operand MFMAs.
 template <int D>
-__global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
+__global__ void __launch_bounds__(256, 2) attn_dkv_mfma(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int kTile = kBT * D * 2;
   __shared__ __attribute__((aligned(1024))) char sq0[kTile];
@@ -148,8 +155,9 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char st1[2048];
 
   const int T = p.T;
-  // Item order: key blocks from the first (longest causal query range) down.
-  const int item = balanced_item(blockIdx.x, gridDim.x);
+  const bool want_dk = blockIdx.x & 1;  // role: dK (1) or dV (0)
+  // Key blocks from the first (longest causal query range) down.
+  const int item = balanced_item(blockIdx.x >> 1, gridDim.x >> 1);
   const int head = item % p.heads;
   const int kblk = item / p.heads;
   const int k0 = kblk * kBT;
@@ -162,9 +170,13 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
   const int kj = ka + lk;       // this lane's key
   const bool kvalid = kj < T;
   const int ka_last = min(ka + 31, T - 1);
+  // queries that see this lane's key: [kj, kend); wend <= every lane's kend
+  const int kend = kvalid ? seq_end(p, kj) : kj;
+  const int wend = (ka + 31 < T) ? seq_end(p, ka) : 0;
   const int q_lo = k0;
   const int q_hi = seq_end(p, min(k0 + kBT - 1, T - 1));
   const int nt = (((q_hi - q_lo + kBT - 1) / kBT) + 1) & ~1;
+  const int rb = qh * 32;
 
   const uint32_t ld_bytes = static_cast<uint32_t>(p.ld) * 2;
   const uint32_t ldo_bytes = static_cast<uint32_t>(p.hl) * 2;
@@ -173,59 +185,64 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse, p.stat_bytes);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta, p.stat_bytes);
 
-  // K^T and V^T fragments (B operands of S = Q K^T and dP = dO V^T): lane
-  // holds d = 16 s + 8 g .. +7 of key kj.
+  // K^T (and for dK, V^T) fragments, B operands of S = Q K^T / dP = dO V^T:
+  // lane holds d = 16 s + 8 g .. +7 of key kj.
   bf16x8 kf[KS], vf[KS];
   {
     const bf16_t* kr = p.qkv + static_cast<int64_t>(kvalid ? kj : 0) * p.ld + p.hl + head * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const uint4 a = kvalid ? *reinterpret_cast<const uint4*>(kr + 16 * s + 8 * g) : make_uint4(0, 0, 0, 0);
-      const uint4 b = kvalid ? *reinterpret_cast<const uint4*>(kr + p.hl + 16 * s + 8 * g)
+      const uint4 a = kvalid ? *reinterpret_cast<const uint4*>(kr + 16 * s + 8 * g)
                              : make_uint4(0, 0, 0, 0);
+      const uint4 b = (kvalid && want_dk)
+                          ? *reinterpret_cast<const uint4*>(kr + p.hl + 16 * s + 8 * g)
+                          : make_uint4(0, 0, 0, 0);
       kf[s] = __builtin_bit_cast(bf16x8, a);
       vf[s] = __builtin_bit_cast(bf16x8, b);
     }
   }
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { dk[d][e] = 0.0f; dv[d][e] = 0.0f; }
+    for (int e = 0; e < 16; ++e) acc[d][e] = 0.0f;
 
   auto issue = [&](char* tq, char* to, char* ts, int r0) {
     issue_rows<D>(rq, tq, wave, lane, r0, T, head * D, ld_bytes);
     issue_rows<D>(ro, to, wave, lane, r0, T, head * D, ldo_bytes);
-    if (wave == 0) issue_stat(rl, ts, lane, head, r0, T);
-    if (wave == 1) issue_stat(rd, ts + 1024, lane, head, r0, T);
+    // waves 0/2 copy lse, 1/3 copy D (the pairs write identical bytes)
+    issue_stat((wave & 1) ? rd : rl, ts + (wave & 1) * 1024, lane, head, r0, T);
   };
 
   auto compute = [&](const char* tq, const char* to, const char* ts, int r0) {
-    const int qa = r0 + qh * 32;  // first query of this wave's half
-    const int qa_last = min(qa + 31, T - 1);
-    if (qa >= T || ka >= T || qa_last < ka || ka_last < seq_start(p, qa)) return;
-    const int rb = qh * 32;
+    const int qa = r0 + rb;  // first query row of this wave's half
+    // wave-uniform skip: no query of the half sees a key of this wave
+    if (qa >= T || ka >= T || min(qa + 31, T - 1) < ka || ka_last < seq_start(p, min(qa, T - 1)))
+      return;
     f32x16 s_acc, p_acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s_acc[e] = 0.0f; p_acc[e] = 0.0f; }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 qf = row_frag<D>(tq, rb + lk, 2 * s + g);
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], s_acc, 0, 0, 0);
-    }
+    for (int s = 0; s < KS; ++s)
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, rb + lk, 2 * s + g), kf[s],
+                                                      s_acc, 0, 0, 0);
+    if (want_dk) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 of = row_frag<D>(to, rb + lk, 2 * s + g);
-      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vf[s], p_acc, 0, 0, 0);
+      for (int s = 0; s < KS; ++s)
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(to, rb + lk, 2 * s + g),
+                                                        vf[s], p_acc, 0, 0, 0);
     }
-    // Rows of the accumulators: query qa + 8 (e/4) + 4 g + e%4; column: key kj.
+    // accumulator rows: query qa + 8 (e/4) + 4 g + e%4; column: key kj.
+    // Query qi sees key kj iff kj <= qi < end of kj's sequence; a tile whose
+    // first query is at or past the wave's last key and whose last query is
+    // before the end of the first key's sequence needs no mask.
     const float* lse = reinterpret_cast<const float*>(ts);
     const float* dl = lse + 256;
-    const bool full = (qa >= ka_last) && (qa + 31 < T) && (kvalid && ka + 31 < T) &&
-                      (seq_start(p, qa + 31) <= ka);
+    const bool full = (qa >= ka + 31) && (qa + 31 < wend);
+    float v[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int qr = rb + 8 * a + 4 * g;  // tile row of element 4a
+      const int qr = rb + 8 * a + 4 * g;
       const float4 l4 = *reinterpret_cast<const float4*>(lse + qr);
       const float4 d4 = *reinterpret_cast<const float4*>(dl + qr);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
@@ -233,27 +250,28 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = 4 * a + c;
-        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -lv[c] * kLog2e));
-        if (!full) {
-          const int qi = qa + 8 * a + 4 * g + c;
-          if (!(kvalid && qi < T && qi >= kj && kj >= seq_start(p, qi))) pe = 0.0f;
-        }
-        s_acc[e] = pe;
-        p_acc[e] = pe * (p_acc[e] - dv4[c]);
+        v[e] = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -lv[c]));
+        if (want_dk) v[e] *= p_acc[e] - dv4[c];
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries.
+    if (!full) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 pb = pack8(s_acc, 8 * t);
-      const bf16x8 sb = pack8(p_acc, 8 * t);
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_frag<D>(to, rb, t, 32 * d, lane), pb,
-                                                        dv[d], 0, 0, 0);
-        dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_frag<D>(tq, rb, t, 32 * d, lane), sb,
-                                                        dk[d], 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        const int qi = qa + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (!(qi >= kj && qi < kend)) v[e] = 0.0f;
       }
+    }
+    const char* tt = want_dk ? tq : to;  // dK^T += Q^T dS, dV^T += dO^T P
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int o = 8 * t2;
+      const bf16x8 vb = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf2(v[o], v[o + 1]), pack_bf2(v[o + 2], v[o + 3]),
+                             pack_bf2(v[o + 4], v[o + 5]), pack_bf2(v[o + 6], v[o + 7])));
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col_frag<D>(tt, rb, t2, 32 * d, lane), vb,
+                                                         acc[d], 0, 0, 0);
     }
   };
 
@@ -263,8 +281,11 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
   };
   issue(sq0, so0, st0, q_lo);
   issue(sq1, so1, st1, q_lo + kBT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  {
+    constexpr int kTileInstr = 2 * (kBT * (D / 8) / 64 / 4) + 1;
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
+    __syncthreads();
+  }
   for (int t = 0; t < nt; t += 2) {
     const int r0 = q_lo + t * kBT;
     compute(sq0, so0, st0, r0);
@@ -277,34 +298,29 @@ __global__ void __launch_bounds__(256, 1) attn_dkv_mfma(BwdParams p) {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Sum the two query halves: the half-1 wave parks dK, dV in LDS.
-  float* park = reinterpret_cast<float*>(kg == 0 ? sq0 : sq1);   // dK (16 KB for D=128)
-  float* park2 = reinterpret_cast<float*>(kg == 0 ? so0 : so1);  // dV
+  // Sum the two query halves: the half-1 wave parks its accumulator in LDS.
+  float* park = reinterpret_cast<float*>(kg == 0 ? sq0 : sq1);
   if (qh == 1) {
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        park[(d * 16 + e) * 64 + lane] = dk[d][e];
-        park2[(d * 16 + e) * 64 + lane] = dv[d][e];
-      }
+      for (int e = 0; e < 16; ++e) park[(d * 16 + e) * 64 + lane] = acc[d][e];
   }
   __syncthreads();
   if (qh == 0 && kvalid) {
-    bf16_t* out = p.dqkv + static_cast<int64_t>(kj) * p.ld + p.hl + head * D;
+    bf16_t* out = p.dqkv + static_cast<int64_t>(kj) * p.ld + (want_dk ? p.hl : 2 * p.hl) + head * D;
+    const float sc = want_dk ? p.scale : 1.0f;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        float vk[4], vv[4];
+        float w[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int e = 4 * a + c;
-          vk[c] = (dk[d][e] + park[(d * 16 + e) * 64 + lane]) * p.scale;
-          vv[c] = dv[d][e] + park2[(d * 16 + e) * 64 + lane];
+          w[c] = (acc[d][e] + park[(d * 16 + e) * 64 + lane]) * sc;
         }
-        store4(out + 32 * d + 8 * a + 4 * g, vk);
-        store4(out + p.hl + 32 * d + 8 * a + 4 * g, vv);
+        store4(out + 32 * d + 8 * a + 4 * g, w);
       }
   }
 }
@@ -357,7 +373,7 @@ __global__ void __launch_bounds__(256, 2) attn_dq_mfma(BwdParams p) {
       of[s] = __builtin_bit_cast(bf16x8, b);
     }
   }
-  const float lse2 = qvalid ? p.lse[static_cast<int64_t>(head) * T + qi] * kLog2e : 0.0f;
+  const float lse2 = qvalid ? p.lse[static_cast<int64_t>(head) * T + qi] : 0.0f;
   const float dlt = qvalid ? p.delta[static_cast<int64_t>(head) * T + qi] : 0.0f;
 
   f32x16 dq[DB];
@@ -459,7 +475,7 @@ hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.ld = 3 * a.heads * a.head_dim;
   p.dctx = static_cast<const bf16_t*>(a.dctx);
   p.hl = a.heads * a.head_dim;
-  p.lse = a.lse;
+  p.lse = a.delta + a.heads * a.T;  // lse * log2(e), written by the preprocess
   p.delta = a.delta;
   p.dqkv = static_cast<bf16_t*>(a.dqkv);
   p.cu = a.cu_seqlens;
@@ -478,11 +494,12 @@ hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.dctx_bytes = static_cast<uint32_t>(ob);
   p.stat_bytes = static_cast<uint32_t>(sb);
   const dim3 grid(static_cast<unsigned>(p.nblk * a.heads));
+  const dim3 grid2(static_cast<unsigned>(2 * p.nblk * a.heads));  // dV and dK roles
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(attn_dkv_mfma<128>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkv_mfma<128>, grid2, dim3(256), 0, s, p);
     hipLaunchKernelGGL(attn_dq_mfma<128>, grid, dim3(256), 0, s, p);
   } else if (a.head_dim == 64) {
-    hipLaunchKernelGGL(attn_dkv_mfma<64>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkv_mfma<64>, grid2, dim3(256), 0, s, p);
     hipLaunchKernelGGL(attn_dq_mfma<64>, grid, dim3(256), 0, s, p);
   } else {
     return hipErrorInvalidValue;

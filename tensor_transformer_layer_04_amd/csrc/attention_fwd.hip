@@ -21,7 +21,9 @@
 //  * K and V tiles go HBM -> LDS with buffer_load ... lds, double-buffered;
 //    keys outside [0, T) read as zeros (buffer offset past num_records).
 //  * Scores stay in log2 units: p = exp2(s * scale * log2(e) - m) is one FMA
-//    and one v_exp_f32.  O is rescaled only when some lane's max grew.
+//    and one v_exp_f32.  The reference max m of a row moves (and O is
+//    rescaled) only when a tile's max exceeds it by more than 8, so p < 2^8;
+//    the result is exact for any reference at or below the running max.
 //  * Block ids are ordered so that block b and block b + ceil(nb/2) (placed
 //    on the same CU by the in-order dispatcher when the grid is two blocks
 //    per CU) take the longest and the shortest remaining causal row blocks.
@@ -181,8 +183,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * p.scale_log2;
-    const float m_new = fmaxf(m, mt);
-    if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+    // The reference max m only moves when some lane's tile max exceeds it
+    // by more than 8 (log2 units): p = exp2(s - m) then stays below 2^8 and
+    // the rescale of O and l is skipped for most tiles.
+    if (__builtin_amdgcn_ballot_w64(mt > m + 8.0f)) {
+      const float m_new = fmaxf(m, mt);
       const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
