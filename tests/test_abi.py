@@ -123,7 +123,7 @@ def test_page_divisibility_examples():
     bad = mtp.make_desc(12288, 96, 49152, g["rejected"]["tp"], 0, 2048)
     assert ln(bad) == mtp.MTP_ERR_INVALID_ARG
     # the valid split sizes the attention workspace by its 96/8 local heads
-    assert mtp.mtp_workspace_size(ok, mtp.MTP_OP_ATTN_BWD) == (96 // 8) * 2048 * 4
+    assert mtp.mtp_workspace_size(ok, mtp.MTP_OP_ATTN_BWD) == 2 * (96 // 8) * 2048 * 4
     assert 12288 // g["ok"]["tp"] == g["ok"]["per_rank"]
 
 
