@@ -55,12 +55,13 @@ struct GemmParams {
 
 // Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids
 // are dispatched round-robin over the 8 XCDs; the first step gives every XCD
-// a contiguous range of tile ids so tiles that share operands share an L2.
+// a contiguous range of tile ids so tiles that share operands share an L2
+// (with nb = 8q + r blocks, the first r XCDs take q + 1 ids, the rest q).
 // The second step walks tiles in groups of kGroupM tile-rows.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  int pid = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) pid = (pid & 7) * (nb >> 3) + (pid >> 3);
+  const int xcd = blockIdx.x & 7, q = nb >> 3, r = nb & 7;
+  const int pid = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + (blockIdx.x >> 3);
   const int per_group = kGroupM * tiles_n;
   const int group = pid / per_group;
   const int first_m = group * kGroupM;
