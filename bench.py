@@ -43,6 +43,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # concurrently with the data-gradient chain, so their durations include
 # sharing the CUs and are reported separately.
 FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
+PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
 FWD_KERNEL = "gemm_bf16_kernel, forward layout (k-major A and B, bf16 C, fused bias/GeLU)"
 WGRAD_KERNEL = "gemm_bf16_kernel, weight-gradient layout (m-major A, n-major B, fp32 C)"
@@ -90,7 +91,7 @@ def traffic_for(kernel: str):
 
 def roofline(kernel, tags, probes, flops, ms, steps) -> dict:
     """Roofline entry of one GEMM family: model flops of its probed launches
-    over their summed HIP-event durations."""
+    over their summed HIP-event durations (``steps``: the probed steps)."""
     dur_ms = sum(a.elapsed_time(b) for t in tags for a, b in probes[t])
     launches = sum(len(probes[t]) for t in tags)
     fl = sum(flops[t] * len(probes[t]) for t in tags)
@@ -106,6 +107,7 @@ def roofline(kernel, tags, probes, flops, ms, steps) -> dict:
         "launches_per_step": launches // max(steps, 1),
         "avg_launch_us": round(1e3 * dur_ms / max(launches, 1), 2),
         "share_of_step": round(dur_ms / (ms * steps), 4),
+        "probed_steps": steps,
     }
 
 
@@ -203,19 +205,22 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    L.probe = {t: [] for t in FWD_TAGS + WGRAD_TAGS}
+    # Every PROBE_EVERY-th timed step records HIP events around the probed
+    # launches (each event adds a few us of gap, so not every step does).
+    probes = {t: [] for t in FWD_TAGS + WGRAD_TAGS}
+    probed = [i for i in range(args.steps) if (i + 1) % PROBE_EVERY == 0] or [args.steps - 1]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        L.probe = probes if i in probed else None
         step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
-    probes = L.probe
     L.probe = None
 
     fl = shard_flops(cfg, cu)
@@ -243,9 +248,9 @@ def main(argv=None) -> int:
         "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),
         "model_gflop_per_step": round(fl["total"] / 1e9, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
-        "roofline": roofline(FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms, args.steps),
+        "roofline": roofline(FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms, len(probed)),
         "roofline_wgrad_overlapped": roofline(WGRAD_KERNEL, WGRAD_TAGS, probes, fl["call"], ms,
-                                              args.steps),
+                                              len(probed)),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, data)

@@ -121,6 +121,22 @@ int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x,
                       const void* dres, void* dx, float* dgamma, float* dbeta,
                       int accumulate, void* ws, size_t ws_bytes, void* stream);
 
+/* LayerNorm backward of a gradient that arrives as tensor-parallel partials
+ * (the column-parallel input gradient of page "Megatron-LM 3D parallelism
+ * guide", §2.1: the input reached every rank, so its gradient is the sum of
+ * the ranks' partials), in one pass where the width allows:
+ *   dy = sum_{i<n} dy_partials[i], accumulated in fp32 in the order
+ *   i = 0..n-1 and rounded to dtype exactly as mtp_partial_sum would store
+ *   it (a single partial is used as is); then everything as
+ *   mtp_layernorm_bwd(dy, ...).  The sum itself is not stored.
+ * dy_partials: HOST array of n_partials (1..16) device pointers, [T,h] dtype.
+ * Other arguments, workspace and errors as mtp_layernorm_bwd.                */
+int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_partials,
+                          int32_t n_partials, const void* x, const void* gamma,
+                          const float* mean, const float* rstd, const void* dres, void* dx,
+                          float* dgamma, float* dbeta, int accumulate, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* ----------------------------------------------- column-parallel linear
  * ColumnParallelLinear with the output left sharded (page "Megatron-LM:
  * NVIDIA large-model training framework", section "Tensor parallelism":
@@ -219,6 +235,19 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
 int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials,
                     int32_t n_partials, const void* bias, const void* residual, void* out,
                     void* stream);
+
+/* The partial sum followed by the LayerNorm of its result (the sum that
+ * completes the row-parallel projection, §2.1 of page "Megatron-LM 3D
+ * parallelism guide", feeding the next pre-LN LayerNorm; the same page, §4.2,
+ * fuses LayerNorm with its neighbours), in one pass where the width allows:
+ *   out = exactly what mtp_partial_sum(partials, n_partials, bias, residual)
+ *   stores; then ln_out, mean, rstd = exactly what mtp_layernorm(out, gamma,
+ *   beta) writes.  Arguments as those two calls; out may alias residual or a
+ *   partial.                                                                 */
+int mtp_partial_sum_layernorm(const mtp_shard_desc* desc, const void* const* partials,
+                              int32_t n_partials, const void* bias, const void* residual,
+                              void* out, const void* gamma, const void* beta, void* ln_out,
+                              float* mean, float* rstd, void* stream);
 
 /* ------------------------------------------------- vocab-parallel CE head
  * Cross-entropy over a vocabulary split across ranks (VocabParallelEmbedding,

@@ -100,7 +100,7 @@ size_t mtp_workspace_size(const mtp_shard_desc* desc, int op, int kind) {
   Shard s;
   if (check_desc(desc, &s) != MTP_OK) return 0;
   switch (op) {
-    case MTP_OP_LAYERNORM_BWD: return mtp::layernorm_bwd_ws_bytes(s.T, s.h);
+    case MTP_OP_LAYERNORM_BWD: return mtp::layernorm_bwd_ws_bytes(s.T, s.h, s.bf16);
     case MTP_OP_COL_LINEAR_BWD: {
       const int64_t n = col_out(s, kind);
       return n > 0 ? mtp::column_sum_ws_bytes(s.T, n) : 0;
@@ -133,11 +133,32 @@ int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x,
   if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(mean) || !ok_ptr(rstd) ||
       !ok_opt(dres) || !ok_ptr(dx) || !ok_ptr(dgamma) || !ok_ptr(dbeta))
     return MTP_ERR_INVALID_ARG;
-  const size_t need = mtp::layernorm_bwd_ws_bytes(s.T, s.h);
+  const size_t need = mtp::layernorm_bwd_ws_bytes(s.T, s.h, s.bf16);
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
   return hip_status(mtp::layernorm_bwd(s.bf16, dy, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
                                        accumulate != 0, s.T, s.h, ws,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_partials,
+                          int32_t n_partials, const void* x, const void* gamma,
+                          const float* mean, const float* rstd, const void* dres, void* dx,
+                          float* dgamma, float* dbeta, int accumulate, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!dy_partials || n_partials < 1 || n_partials > mtp::kMaxPartials) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_partials; ++i)
+    if (!ok_ptr(dy_partials[i])) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(mean) || !ok_ptr(rstd) || !ok_opt(dres) ||
+      !ok_ptr(dx) || !ok_ptr(dgamma) || !ok_ptr(dbeta))
+    return MTP_ERR_INVALID_ARG;
+  const size_t need = mtp::layernorm_bwd_ws_bytes(s.T, s.h, s.bf16);
+  if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  return hip_status(mtp::layernorm_bwd_sum(s.bf16, dy_partials, n_partials, x, gamma, mean, rstd,
+                                           dres, dx, dgamma, dbeta, accumulate != 0, s.T, s.h,
+                                           ws, static_cast<hipStream_t>(stream)));
 }
 
 int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, const void* w,
@@ -303,6 +324,24 @@ int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials, int
   if (!ok_opt(bias) || !ok_opt(residual) || !ok_ptr(out)) return MTP_ERR_INVALID_ARG;
   return hip_status(mtp::partial_sum(s.bf16, partials, n_partials, bias, residual, out, s.T, s.h,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int mtp_partial_sum_layernorm(const mtp_shard_desc* desc, const void* const* partials,
+                              int32_t n_partials, const void* bias, const void* residual,
+                              void* out, const void* gamma, const void* beta, void* ln_out,
+                              float* mean, float* rstd, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!partials || n_partials < 1 || n_partials > mtp::kMaxPartials) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_partials; ++i)
+    if (!ok_ptr(partials[i])) return MTP_ERR_INVALID_ARG;
+  if (!ok_opt(bias) || !ok_opt(residual) || !ok_ptr(out) || !ok_ptr(gamma) || !ok_ptr(beta) ||
+      !ok_ptr(ln_out) || !ok_ptr(mean) || !ok_ptr(rstd))
+    return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::sum_layernorm_fwd(s.bf16, partials, n_partials, bias, residual, out,
+                                           gamma, beta, ln_out, mean, rstd, s.T, s.h, s.eps,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int mtp_vocab_ce_stats(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,

@@ -44,7 +44,7 @@ hipError_t column_sum(bool bf16, const void* x, int64_t rows, int64_t cols, floa
 hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void* beta, void* y,
                          float* mean, float* rstd, int64_t T, int h, float eps,
                          hipStream_t stream);
-size_t layernorm_bwd_ws_bytes(int64_t T, int h);
+size_t layernorm_bwd_ws_bytes(int64_t T, int h, bool bf16);
 hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* gamma,
                          const float* mean, const float* rstd, const void* dres, void* dx,
                          float* dgamma, float* dbeta, bool accumulate, int64_t T, int h,
@@ -52,6 +52,16 @@ hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* g
 constexpr int kMaxPartials = 16;
 hipError_t partial_sum(bool bf16, const void* const* partials, int n, const void* bias,
                        const void* residual, void* out, int64_t T, int h, hipStream_t stream);
+// partial_sum into out, then LayerNorm of out (one pass when h = 512*{1,2,4,8}).
+hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, const void* bias,
+                             const void* residual, void* out, const void* gamma,
+                             const void* beta, void* y, float* mean, float* rstd, int64_t T,
+                             int h, float eps, hipStream_t stream);
+// LayerNorm backward of dy = sum of n partials (rounded to the storage type).
+hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const void* x,
+                             const void* gamma, const float* mean, const float* rstd,
+                             const void* dres, void* dx, float* dgamma, float* dbeta,
+                             bool accumulate, int64_t T, int h, void* ws, hipStream_t stream);
 hipError_t zero_f32(float* p, int64_t n, hipStream_t stream);
 
 // ------------------------------------------------------------- attention

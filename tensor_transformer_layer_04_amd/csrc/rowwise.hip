@@ -17,6 +17,14 @@ template <typename T> __host__ __device__ __forceinline__ const T* cptr(const vo
   return static_cast<const T*>(p);
 }
 
+// Load one row's NC chunks of 8 elements owned by a lane (chunks lane,
+// lane+64, ...), every load issued before any use.
+template <typename T, int NC>
+__device__ __forceinline__ void load_row(const T* r, int lane, float v[NC][8]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) load8(r + (lane + 64 * c) * 8, v[c]);
+}
+
 // Block-wide sum over kRowThreads threads (result broadcast to all).
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = warp_sum(v);
@@ -321,8 +329,18 @@ reduce_parts_kernel(const float* __restrict__ part0, float* __restrict__ out0,
   const int tx = threadIdx.x % kRedCols, ty = threadIdx.x / kRedCols;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCols + tx;
   float s = 0.0f;
-  if (c < cols)
-    for (int b = ty; b < nparts; b += kRedLanes) s += part[static_cast<int64_t>(b) * cols + c];
+  if (c < cols) {
+    // eight loads in flight per thread; the additions stay in ascending b
+    int b = ty;
+    for (; b + 7 * kRedLanes < nparts; b += 8 * kRedLanes) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = part[static_cast<int64_t>(b + u * kRedLanes) * cols + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += t[u];
+    }
+    for (; b < nparts; b += kRedLanes) s += part[static_cast<int64_t>(b) * cols + c];
+  }
   red[ty][tx] = s;
   __syncthreads();
   if (ty == 0 && c < cols) {
@@ -398,6 +416,228 @@ partial_sum_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
     }
     store8(out + off, acc);
   }
+}
+
+// Round 8 fp32 values to the storage type T in place (identity for fp32,
+// round-to-nearest-even bf16 otherwise): the value a store + load would give.
+template <typename T> __device__ __forceinline__ void round8(float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t w = pack_bf2(v[e], v[e + 1]);
+      v[e] = lo_bf(w);
+      v[e + 1] = hi_bf(w);
+    }
+  }
+}
+
+// ------------------------------------------- partial sum + LayerNorm fwd
+// out = sum_i parts[i] (+ bias) (+ residual), rounded to T and stored, then
+// the LayerNorm of that stored row: the arithmetic of partial_sum_kernel
+// followed by that of the LayerNorm forward kernels, in one pass with the
+// row in registers.  One wave per row, four rows per workgroup, h = 512*NC
+// (lane l owns the 16-byte chunks l, l+64, ...).  A lane reads every
+// element it writes before writing it, so out may alias an input.
+template <typename T, int NC>
+__global__ void __launch_bounds__(256)
+sum_layernorm_fwd_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
+                         const T* residual, T* out, const T* __restrict__ gamma,
+                         const T* __restrict__ beta, T* __restrict__ y, float* __restrict__ mean,
+                         float* __restrict__ rstd, int64_t T_rows, int h, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
+  const int64_t base = row * h;
+  float v[NC][8];
+  load_row<T, NC>(static_cast<const T*>(parts.p[0]) + base, lane, v);
+  for (int i = 1; i < n; ++i) {
+    float t[NC][8];
+    load_row<T, NC>(static_cast<const T*>(parts.p[i]) + base, lane, t);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+  }
+  if (bias) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float t[8];
+      load8(bias + (lane + 64 * c) * 8, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] += t[e];
+    }
+  }
+  if (residual) {
+    float t[NC][8];
+    load_row<T, NC>(residual + base, lane, t);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    round8<T>(v[c]);
+    store8(out + base + (lane + 64 * c) * 8, v[c]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[c][e];
+  const float mu = warp_sum(s) / h;
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { const float d = v[c][e] - mu; q += d * d; }
+  const float rs = rsqrtf(warp_sum(q) / h + eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float g[8], b[8], o[8];
+    load8(gamma + (lane + 64 * c) * 8, g);
+    load8(beta + (lane + 64 * c) * 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * g[e] + b[e];
+    store8(y + base + (lane + 64 * c) * 8, o);
+  }
+  if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+}
+
+// ------------------------------------- LayerNorm bwd with column partials
+// dy = sum_i dys[i], rounded to T when there is more than one part (the
+// value partial_sum_kernel would store), then dx = dres + rstd*(gh -
+// mean(gh) - xhat*mean(gh*xhat)), gh = dy*gamma, as in the row kernels
+// above.  The same pass accumulates the column sums of dy*xhat and dy
+// (dgamma, dbeta).  A workgroup has 8 waves; a row of h = 512*NC elements is
+// held by SPLIT waves (NC/SPLIT 16-byte chunks per lane, SPLIT = 2 for the
+// widest rows so that two workgroups fit a CU), so 8/SPLIT rows are in
+// flight per iteration and the SPLIT waves of a row add their two row sums
+// through LDS (in wave order).  Row slot q of workgroup b takes rows
+// q + (8/SPLIT)*b + k*(8/SPLIT)*gridDim.x.  Each lane sums dy*xhat and dy
+// over its rows; the slots' sums are then added in slot order through LDS
+// and workgroup b writes row b of the partial matrices, which
+// reduce_parts_kernel adds in workgroup order.
+template <typename T, int NC, int SPLIT>
+__global__ void __launch_bounds__(512)
+layernorm_bwd_fused_kernel(PartialPtrs dys, int n, const T* __restrict__ x,
+                           const T* __restrict__ gamma, const float* __restrict__ mean,
+                           const float* __restrict__ rstd, const T* dres, T* dx, int64_t T_rows,
+                           int h, float* __restrict__ part_g, float* __restrict__ part_b) {
+  constexpr int NCW = NC / SPLIT;     // chunks per lane
+  constexpr int kSlots = 8 / SPLIT;   // rows per iteration
+  __shared__ float red[2][512 * NC];
+  __shared__ float xch[2][8][2];      // [iteration parity][wave][s1, s2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = wave / SPLIT, half = wave % SPLIT;
+  // chunk c of this lane starts at element col(c)
+  auto col = [&](int c) { return ((half * NCW + c) * 64 + lane) * 8; };
+  float gm[NCW][8], ag[NCW][8], ab[NCW][8];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    load8(gamma + col(c), gm[c]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ag[c][e] = 0.0f; ab[c][e] = 0.0f; }
+  }
+  const int64_t per_iter = static_cast<int64_t>(gridDim.x) * kSlots;
+  const int64_t iters = (T_rows + per_iter - 1) / per_iter;  // the same for every wave
+  for (int64_t k = 0; k < iters; ++k) {
+    const int64_t row = k * per_iter + static_cast<int64_t>(blockIdx.x) * kSlots + slot;
+    const bool valid = row < T_rows;
+    const int64_t base = row * h;
+    float xv[NCW][8], dv[NCW][8];
+    float s1 = 0.0f, s2 = 0.0f, rs = 0.0f;
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) load8(x + base + col(c), xv[c]);
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) load8(static_cast<const T*>(dys.p[0]) + base + col(c), dv[c]);
+      for (int i = 1; i < n; ++i) {
+        const T* src = static_cast<const T*>(dys.p[i]) + base;
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) {
+          float t[8];
+          load8(src + col(c), t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dv[c][e] += t[e];
+        }
+      }
+      if (n > 1) {
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) round8<T>(dv[c]);
+      }
+      const float mu = mean[row];
+      rs = rstd[row];
+#pragma unroll
+      for (int c = 0; c < NCW; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = (xv[c][e] - mu) * rs, g = dv[c][e] * gm[c][e];
+          s1 += g;
+          s2 += g * a;
+          xv[c][e] = a;
+          ag[c][e] += dv[c][e] * a;
+          ab[c][e] += dv[c][e];
+        }
+    }
+    s1 = warp_sum(s1);
+    s2 = warp_sum(s2);
+    if constexpr (SPLIT > 1) {
+      const int par = static_cast<int>(k & 1);
+      if (lane == 0) { xch[par][wave][0] = s1; xch[par][wave][1] = s2; }
+      __syncthreads();
+      s1 = 0.0f;
+      s2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < SPLIT; ++w) {
+        s1 += xch[par][slot * SPLIT + w][0];
+        s2 += xch[par][slot * SPLIT + w][1];
+      }
+    }
+    if (valid) {
+      const float m1 = s1 / h, m2 = s2 / h;
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        float o[8];
+        if (dres) {
+          load8(dres + base + col(c), o);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += rs * (dv[c][e] * gm[c][e] - m1 - xv[c][e] * m2);
+        store8(dx + base + col(c), o);
+      }
+    }
+  }
+  for (int q = 0; q < kSlots; ++q) {
+    if (slot == q) {
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        float4* rg = reinterpret_cast<float4*>(&red[0][col(c)]);
+        float4* rb = reinterpret_cast<float4*>(&red[1][col(c)]);
+        float4 g0 = make_float4(ag[c][0], ag[c][1], ag[c][2], ag[c][3]);
+        float4 g1 = make_float4(ag[c][4], ag[c][5], ag[c][6], ag[c][7]);
+        float4 b0 = make_float4(ab[c][0], ab[c][1], ab[c][2], ab[c][3]);
+        float4 b1 = make_float4(ab[c][4], ab[c][5], ab[c][6], ab[c][7]);
+        if (q > 0) {
+          const float4 pg0 = rg[0], pg1 = rg[1], pb0 = rb[0], pb1 = rb[1];
+          g0 = make_float4(pg0.x + g0.x, pg0.y + g0.y, pg0.z + g0.z, pg0.w + g0.w);
+          g1 = make_float4(pg1.x + g1.x, pg1.y + g1.y, pg1.z + g1.z, pg1.w + g1.w);
+          b0 = make_float4(pb0.x + b0.x, pb0.y + b0.y, pb0.z + b0.z, pb0.w + b0.w);
+          b1 = make_float4(pb1.x + b1.x, pb1.y + b1.y, pb1.z + b1.z, pb1.w + b1.w);
+        }
+        rg[0] = g0; rg[1] = g1; rb[0] = b0; rb[1] = b1;
+      }
+    }
+    __syncthreads();
+  }
+  float4* og = reinterpret_cast<float4*>(part_g + static_cast<int64_t>(blockIdx.x) * h);
+  float4* ob = reinterpret_cast<float4*>(part_b + static_cast<int64_t>(blockIdx.x) * h);
+  const float4* rg = reinterpret_cast<const float4*>(red[0]);
+  const float4* rb = reinterpret_cast<const float4*>(red[1]);
+  for (int i = threadIdx.x; i < h / 4; i += 512) { og[i] = rg[i]; ob[i] = rb[i]; }
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
@@ -596,35 +836,133 @@ hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void
   return hipGetLastError();
 }
 
-size_t layernorm_bwd_ws_bytes(int64_t T, int h) {
-  return static_cast<size_t>(colsum_parts(T)) * h * 2 * sizeof(float);
+// Workgroups of the fused LayerNorm backward: one per 8 rows, at most 256
+// (each writes one row of column partials).
+static int64_t ln_bwd_blocks(int64_t T) {
+  const int64_t b = (T + 7) / 8;
+  return b > 256 ? 256 : b;
+}
+
+// Chunks per lane of the fused row kernels (h = 512*NC), 0 if h does not fit.
+static int fused_row_nc(int h) {
+  if (h % 512 != 0) return 0;
+  const int nc = h / 512;
+  return (nc == 1 || nc == 2 || nc == 4 || nc == 8) ? nc : 0;
+}
+
+static size_t round_up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t layernorm_bwd_ws_bytes(int64_t T, int h, bool bf16) {
+  const size_t parts = round_up256(static_cast<size_t>(ln_bwd_blocks(T)) * h * 2 * sizeof(float));
+  // rows too wide for the fused kernel stage the summed gradient here
+  const size_t stage = fused_row_nc(h) ? 0 : static_cast<size_t>(T) * h * (bf16 ? 2 : 4);
+  return parts + stage;
+}
+
+hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, const void* bias,
+                             const void* residual, void* out, const void* gamma,
+                             const void* beta, void* y, float* mean, float* rstd, int64_t T,
+                             int h, float eps, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (h / 8 > kMaxRowChunks || n < 1 || n > kMaxPartials) return hipErrorInvalidValue;
+  const int nc = fused_row_nc(h);
+  if (nc == 0) {
+    const hipError_t e = partial_sum(bf16, partials, n, bias, residual, out, T, h, s);
+    if (e != hipSuccess) return e;
+    return layernorm_fwd(bf16, out, gamma, beta, y, mean, rstd, T, h, eps, s);
+  }
+  PartialPtrs pp{};
+  for (int i = 0; i < n; ++i) pp.p[i] = partials[i];
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+#define MTP_SUM_LN(TT, NC)                                                                     \
+  hipLaunchKernelGGL((sum_layernorm_fwd_kernel<TT, NC>), grid, dim3(256), 0, s, pp, n,           \
+                     cptr<TT>(bias), cptr<TT>(residual), static_cast<TT*>(out), cptr<TT>(gamma), \
+                     cptr<TT>(beta), static_cast<TT*>(y), mean, rstd, T, h, eps)
+#define MTP_SUM_LN_T(TT)                  \
+  switch (nc) {                           \
+    case 1: MTP_SUM_LN(TT, 1); break;     \
+    case 2: MTP_SUM_LN(TT, 2); break;     \
+    case 4: MTP_SUM_LN(TT, 4); break;     \
+    default: MTP_SUM_LN(TT, 8); break;    \
+  }
+  if (bf16) { MTP_SUM_LN_T(bf16_t) } else { MTP_SUM_LN_T(float) }
+#undef MTP_SUM_LN_T
+#undef MTP_SUM_LN
+  return hipGetLastError();
+}
+
+hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const void* x,
+                             const void* gamma, const float* mean, const float* rstd,
+                             const void* dres, void* dx, float* dgamma, float* dbeta,
+                             bool accumulate, int64_t T, int h, void* ws, hipStream_t s) {
+  if (h / 8 > kMaxRowChunks || n < 1 || n > kMaxPartials) return hipErrorInvalidValue;
+  const int nc = fused_row_nc(h);
+  float* pg = static_cast<float*>(ws);
+  const dim3 rg((h + kRedCols - 1) / kRedCols, 2);
+  if (nc == 0) {
+    // Wide or unaligned rows: the sum (if any) goes to the staging area,
+    // then the row pass and the column pass run separately.
+    const int64_t parts = colsum_parts(T);
+    float* pb = pg + parts * h;
+    const void* dy = dys[0];
+    if (n > 1 && T > 0) {
+      void* stage = static_cast<char*>(ws) +
+                    round_up256(static_cast<size_t>(ln_bwd_blocks(T)) * h * 2 * sizeof(float));
+      const hipError_t e = partial_sum(bf16, dys, n, nullptr, nullptr, stage, T, h, s);
+      if (e != hipSuccess) return e;
+      dy = stage;
+    }
+    if (T > 0) {
+      if (bf16) ln_bwd_rows<bf16_t>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
+      else ln_bwd_rows<float>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
+      const int rpb = static_cast<int>((T + parts - 1) / parts);
+      const dim3 g((h + 511) / 512, static_cast<unsigned>(parts));
+      if (bf16)
+        hipLaunchKernelGGL(layernorm_bwd_cols_kernel<bf16_t>, g, dim3(256), 0, s,
+                           cptr<bf16_t>(dy), cptr<bf16_t>(x), mean, rstd, T, h, rpb, pg, pb);
+      else
+        hipLaunchKernelGGL(layernorm_bwd_cols_kernel<float>, g, dim3(256), 0, s,
+                           cptr<float>(dy), cptr<float>(x), mean, rstd, T, h, rpb, pg, pb);
+    }
+    hipLaunchKernelGGL(reduce_parts_kernel, rg, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
+                       dbeta, static_cast<int>(T > 0 ? parts : 0), static_cast<int64_t>(h),
+                       accumulate ? 1 : 0);
+    return hipGetLastError();
+  }
+  const int64_t blocks = ln_bwd_blocks(T);
+  float* pb = pg + blocks * h;
+  if (T > 0) {
+    PartialPtrs pp{};
+    for (int i = 0; i < n; ++i) pp.p[i] = dys[i];
+    const dim3 grid(static_cast<unsigned>(blocks));
+#define MTP_LN_BWD_F(TT, NC)                                                                    \
+  hipLaunchKernelGGL((layernorm_bwd_fused_kernel<TT, NC, (NC >= 8 ? 2 : 1)>), grid, dim3(512), 0, \
+                     s, pp, n, cptr<TT>(x), cptr<TT>(gamma), mean, rstd, cptr<TT>(dres),         \
+                     static_cast<TT*>(dx), T, h, pg, pb)
+#define MTP_LN_BWD_F_T(TT)                  \
+  switch (nc) {                             \
+    case 1: MTP_LN_BWD_F(TT, 1); break;     \
+    case 2: MTP_LN_BWD_F(TT, 2); break;     \
+    case 4: MTP_LN_BWD_F(TT, 4); break;     \
+    default: MTP_LN_BWD_F(TT, 8); break;    \
+  }
+    if (bf16) { MTP_LN_BWD_F_T(bf16_t) } else { MTP_LN_BWD_F_T(float) }
+#undef MTP_LN_BWD_F_T
+#undef MTP_LN_BWD_F
+  }
+  hipLaunchKernelGGL(reduce_parts_kernel, rg, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
+                     dbeta, static_cast<int>(T > 0 ? blocks : 0), static_cast<int64_t>(h),
+                     accumulate ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* gamma,
                          const float* mean, const float* rstd, const void* dres, void* dx,
                          float* dgamma, float* dbeta, bool accumulate, int64_t T, int h,
                          void* ws, hipStream_t s) {
-  if (h / 8 > kMaxRowChunks) return hipErrorInvalidValue;
-  const int64_t parts = colsum_parts(T);
-  float* pg = static_cast<float*>(ws);
-  float* pb = pg + parts * h;
-  if (T > 0) {
-    if (bf16) ln_bwd_rows<bf16_t>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
-    else ln_bwd_rows<float>(dy, x, gamma, mean, rstd, dres, dx, T, h, s);
-    const int rpb = static_cast<int>((T + parts - 1) / parts);
-    const dim3 g((h + 511) / 512, static_cast<unsigned>(parts));
-    if (bf16)
-      hipLaunchKernelGGL(layernorm_bwd_cols_kernel<bf16_t>, g, dim3(256), 0, s, cptr<bf16_t>(dy),
-                         cptr<bf16_t>(x), mean, rstd, T, h, rpb, pg, pb);
-    else
-      hipLaunchKernelGGL(layernorm_bwd_cols_kernel<float>, g, dim3(256), 0, s, cptr<float>(dy),
-                         cptr<float>(x), mean, rstd, T, h, rpb, pg, pb);
-  }
-  const dim3 g((h + kRedCols - 1) / kRedCols, 2);
-  hipLaunchKernelGGL(reduce_parts_kernel, g, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
-                     dbeta, static_cast<int>(T > 0 ? parts : 0), static_cast<int64_t>(h),
-                     accumulate ? 1 : 0);
-  return hipGetLastError();
+  const void* dys[1] = {dy};
+  return layernorm_bwd_sum(bf16, dys, 1, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
+                           accumulate, T, h, ws, s);
 }
 
 size_t column_sum_ws_bytes(int64_t rows, int64_t cols) {

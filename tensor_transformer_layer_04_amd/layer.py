@@ -119,7 +119,7 @@ class TPLayer:
                 "du": E(T, fl), "dln2": E(T, h), "dctx": E(T, hl), "dqkv": E(T, 3 * hl),
                 "dln1": E(T, h),
             }
-        self.dy1, self.dx, self.dln2_sum, self.dln1_sum = E(T, h), E(T, h), E(T, h), E(T, h)
+        self.dy1, self.dx = E(T, h), E(T, h)
         f32 = torch.float32
         self.grads: Dict[int, Dict[str, torch.Tensor]] = {}
         for r in self.ranks:
@@ -179,10 +179,9 @@ class TPLayer:
             with T("proj_fwd"):
                 mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
-        with T("sum_proj"):
-            mtp.mtp_partial_sum(d0, parts, rep["bo"], x, self.y1)
-        with T("ln2"):
-            mtp.mtp_layernorm(d0, self.y1, rep["ln2_g"], rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+        with T("sum_proj_ln2"):
+            mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
+                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2)
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
             with T("fc1_fwd"):
@@ -235,12 +234,10 @@ class TPLayer:
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
                                        g["db1"], 0, wss, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
-        with T("sum_fc1_dx"):
-            mtp.mtp_partial_sum(d0, parts, None, None, self.dln2_sum)
         with T("ln2_bwd"):
-            mtp.mtp_layernorm_bwd(d0, self.dln2_sum, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
-                                  self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws,
-                                  wsb)
+            mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
+                                      self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws,
+                                      wsb)
         fork()
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
@@ -262,12 +259,10 @@ class TPLayer:
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
                                        g["dwqkv"], g["dbqkv"], 0, wss, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
-        with T("sum_qkv_dx"):
-            mtp.mtp_partial_sum(d0, parts, None, None, self.dln1_sum)
         with T("ln1_bwd"):
-            mtp.mtp_layernorm_bwd(d0, self.dln1_sum, self.x, rep["ln1_g"], self.mu1, self.rs1,
-                                  self.dy1, self.dx, self.rgrads["dln1_g"], self.rgrads["dln1_b"],
-                                  0, ws, wsb)
+            mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                                      self.dy1, self.dx, self.rgrads["dln1_g"],
+                                      self.rgrads["dln1_b"], 0, ws, wsb)
         if side is not None:
             main.wait_stream(side)
         return self.dx

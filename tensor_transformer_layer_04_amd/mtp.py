@@ -56,6 +56,9 @@ _SIGS = {
     "mtp_attn_fwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int32, _VP]),
     "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "mtp_partial_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
+    "mtp_partial_sum_layernorm": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8 + [_VP]),
+    "mtp_layernorm_bwd_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8
+                              + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
     "mtp_vocab_ce_stats": (ctypes.c_int, [_VP] + [_VP] * 5 + [_VP]),
     "mtp_vocab_ce_combine": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32] + [_VP] * 4 + [_VP]),
     "mtp_vocab_ce_bwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_float, _VP, _VP]),
@@ -181,6 +184,22 @@ def mtp_partial_sum(desc, partials, bias, residual, out, stream=None):
     arr = _ptr_array(partials)
     return _call("mtp_partial_sum", ctypes.byref(desc), arr, len(partials), _addr(bias),
                  _addr(residual), _addr(out), _stream(stream))
+
+
+def mtp_partial_sum_layernorm(desc, partials, bias, residual, out, gamma, beta, ln_out, mean,
+                              rstd, stream=None):
+    arr = _ptr_array(partials)
+    return _call("mtp_partial_sum_layernorm", ctypes.byref(desc), arr, len(partials), _addr(bias),
+                 _addr(residual), _addr(out), _addr(gamma), _addr(beta), _addr(ln_out),
+                 _addr(mean), _addr(rstd), _stream(stream))
+
+
+def mtp_layernorm_bwd_sum(desc, dy_partials, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
+                          accumulate, ws, ws_bytes, stream=None):
+    arr = _ptr_array(dy_partials)
+    return _call("mtp_layernorm_bwd_sum", ctypes.byref(desc), arr, len(dy_partials), _addr(x),
+                 _addr(gamma), _addr(mean), _addr(rstd), _addr(dres), _addr(dx), _addr(dgamma),
+                 _addr(dbeta), int(accumulate), _addr(ws), ws_bytes, _stream(stream))
 
 
 def mtp_vocab_ce_stats(desc, logits, targets, m, s, z_tgt, stream=None):

@@ -129,7 +129,8 @@ def test_vocab_linear_fp32_logits():
 
 # ------------------------------------------------------------- LayerNorm
 @pytest.mark.parametrize("dtype,h,T", [("bf16", 192, 53), ("f32", 256, 7), ("bf16", 12288, 9),
-                                       ("bf16", 4096, 1)])
+                                       ("bf16", 4096, 1), ("f32", 512, 300), ("bf16", 2048, 2049),
+                                       ("bf16", 4096, 2048)])
 def test_layernorm_fwd_bwd(dtype, h, T):
     require_gpu()
     mtp = _m()
@@ -236,6 +237,71 @@ def test_partial_sum(n):
     check("sum_inplace", host(p0), sum(oracle.to64(p) for p in parts), TOL["bf16"], rep)
 
 
+# --------------------------------------- partial sum fused with LayerNorm
+# dtype, h, T, number of partials.  h = 512 * {1, 2, 4, 8} takes the one-pass
+# kernels; 192 and 12288 take the separate passes (12288 with a staged sum).
+FUSED_CASES = [("bf16", 512, 77, 2), ("bf16", 4096, 2048, 2), ("f32", 1024, 300, 3),
+               ("bf16", 2048, 1, 16), ("bf16", 192, 53, 2), ("f32", 256, 100, 1),
+               ("bf16", 12288, 9, 4)]
+
+
+@pytest.mark.parametrize("dtype,h,T,n", FUSED_CASES)
+def test_fused_sum_layernorm(dtype, h, T, n):
+    """mtp_partial_sum_layernorm and mtp_layernorm_bwd_sum store exactly what
+    the separate calls store (sum, LayerNorm output and statistics, dx); the
+    dgamma/dbeta column sums are added in another order and are checked
+    against the oracle."""
+    require_gpu()
+    mtp = _m()
+    d = desc(mtp, h, h // 64, 0, 1, 0, T, dtype)
+    parts = [dev(rnd((T, h), dtype, 90 + i)) for i in range(n)]
+    bias, res = dev(rnd((h,), dtype, 110, 0.1)), dev(rnd((T, h), dtype, 111))
+    gm = dev((1 + 0.1 * torch.randn(h, generator=torch.Generator().manual_seed(112))).to(DT[dtype]))
+    bt = dev(rnd((h,), dtype, 113, 0.1))
+    E = lambda: torch.empty(T, h, dtype=DT[dtype], device="cuda")
+    F = lambda k=T: torch.empty(k, dtype=torch.float32, device="cuda")
+    out_u, y_u, mu_u, rs_u = E(), E(), F(), F()
+    mtp.mtp_partial_sum(d, parts, bias, res, out_u)
+    mtp.mtp_layernorm(d, out_u, gm, bt, y_u, mu_u, rs_u)
+    out_f, y_f, mu_f, rs_f = E(), E(), F(), F()
+    mtp.mtp_partial_sum_layernorm(d, parts, bias, res, out_f, gm, bt, y_f, mu_f, rs_f)
+    torch.cuda.synchronize()
+    for name, a, b in (("out", out_f, out_u), ("ln", y_f, y_u), ("mean", mu_f, mu_u),
+                       ("rstd", rs_f, rs_u)):
+        assert torch.equal(a, b), f"fused {name} differs from the separate calls"
+    # out aliasing the residual
+    res2 = res.clone()
+    mtp.mtp_partial_sum_layernorm(d, parts, bias, res2, res2, gm, bt, y_f, mu_f, rs_f)
+    torch.cuda.synchronize()
+    assert torch.equal(res2, out_u) and torch.equal(y_f, y_u)
+
+    dys = [dev(rnd((T, h), dtype, 120 + i)) for i in range(n)]
+    dres = dev(rnd((T, h), dtype, 130))
+    ws, wsb = ws_for(mtp, d, mtp.MTP_OP_LAYERNORM_BWD)
+    dsum = E()
+    mtp.mtp_partial_sum(d, dys, None, None, dsum)
+    dx_u, dg_u, db_u = E(), F(h), F(h)
+    mtp.mtp_layernorm_bwd(d, dsum, out_u, gm, mu_u, rs_u, dres, dx_u, dg_u, db_u, 0, ws, wsb)
+    dx_f, dg_f, db_f = E(), F(h), F(h)
+    mtp.mtp_layernorm_bwd_sum(d, dys, out_u, gm, mu_u, rs_u, dres, dx_f, dg_f, db_f, 0, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_f, dx_u), "fused dx differs from the separate calls"
+    X, GM = oracle.to64(out_u.cpu()), oracle.to64(gm.cpu())
+    _, rmu, rrs = oracle.layernorm(X, GM, oracle.to64(bt.cpu()), 1e-5)
+    rdx, rdg, rdb = oracle.layernorm_backward(oracle.to64(dsum.cpu()), X, GM, rmu, rrs)
+    rep = {}
+    tol = TOL[dtype]
+    check("fused_dx", host(dx_f), rdx + oracle.to64(dres.cpu()), tol, rep)
+    check("fused_dgamma", host(dg_f), rdg, tol, rep)
+    check("fused_dbeta", host(db_f), rdb, tol, rep)
+    # accumulate adds onto the previous values
+    mtp.mtp_layernorm_bwd_sum(d, dys, out_u, gm, mu_u, rs_u, None, dx_f, dg_f, db_f, 1, ws, wsb)
+    check("fused_dgamma_acc", host(dg_f), 2 * rdg, tol, rep)
+    check("fused_dx_nores", host(dx_f), rdx, tol, rep)
+    log(f"fused sum+layernorm {dtype} h={h} T={T} n={n}: "
+        + ", ".join(f"{k}={v:.1e}" for k, v in rep.items()))
+
+
 # --------------------------------------------------------------- vocab CE
 def test_vocab_ce_pieces():
     require_gpu()
@@ -293,9 +359,16 @@ def test_zero_tokens_writes_zero_gradients():
     dbt = torch.full((h,), 7.0, device="cuda")
     stat = torch.empty(64, dtype=torch.float32, device="cuda")
     mtp.mtp_layernorm_bwd(d, dummy, dummy, dummy, stat, stat, None, dummy, dg, dbt, 0, ws, 256)
+    dg2 = torch.full((h,), 7.0, device="cuda")
+    dbt2 = torch.full((h,), 7.0, device="cuda")
+    mtp.mtp_layernorm_bwd_sum(d, [dummy, dummy], dummy, dummy, stat, stat, None, dummy, dg2, dbt2,
+                              0, ws, 256)
+    mtp.mtp_partial_sum_layernorm(d, [dummy, dummy], None, None, dummy, dummy, dummy, dummy,
+                                  stat, stat)
     lse = torch.empty(64, dtype=torch.float32, device="cuda")
     mtp.mtp_attn_fwd(d, dummy, dummy, lse)
     torch.cuda.synchronize()
     assert float(dw.abs().max()) == 0.0 and float(db.abs().max()) == 0.0
     assert float(dg.abs().max()) == 0.0 and float(dbt.abs().max()) == 0.0
+    assert float(dg2.abs().max()) == 0.0 and float(dbt2.abs().max()) == 0.0
     del e, e_f
