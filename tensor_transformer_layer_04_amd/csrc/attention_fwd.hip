@@ -6,12 +6,13 @@
 // exchange between ranks and the softmax runs in fp32 (page "Megatron-LM 3D
 // parallelism guide", §2.1 and the attention_softmax_in_fp32 flag of §3.2).
 //
-// Work decomposition (one workgroup = 4 waves, 64 queries of one head):
-//  * waves (g, h) for query group g in {0,1} (32 queries) and key half h in
-//    {0,1}: every 64-key tile is split between the two key halves, so two
-//    waves share each query group and the chip holds 2 waves per SIMD even
-//    when T x heads / 32 is only 4 waves per CU.  The halves keep separate
-//    online-softmax states and are merged exactly at the end.
+// Work decomposition (one workgroup = 2*KH waves, 64 queries of one head):
+//  * waves (g, h) for query group g in {0,1} (32 queries) and key part h in
+//    [0, KH): every tile of 32*KH keys is split into KH parts of 32 keys, so
+//    KH waves share each query group.  With KH = 4 a workgroup is 8 waves and
+//    one workgroup fills a CU with 2 waves per SIMD that all work on the same
+//    (possibly long) causal row block; the parts keep separate online-softmax
+//    states and are merged exactly at the end.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 puts one query per lane (16
 //    keys each, the other 16 in lane ^ 32), so row max and row sum are
 //    in-lane plus one exchange.  P^T then feeds O^T += V^T P^T straight from
@@ -24,9 +25,8 @@
 //    and one v_exp_f32.  The reference max m of a row moves (and O is
 //    rescaled) only when a tile's max exceeds it by more than 8, so p < 2^8;
 //    the result is exact for any reference at or below the running max.
-//  * Block ids are ordered so that block b and block b + ceil(nb/2) (placed
-//    on the same CU by the in-order dispatcher when the grid is two blocks
-//    per CU) take the longest and the shortest remaining causal row blocks.
+//  * Blocks are dispatched longest causal row block first, so the shorter
+//    ones fill the CUs that finish early.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -35,7 +35,12 @@ namespace mtp {
 namespace {
 
 constexpr int kFQ = 64;  // queries per workgroup
-constexpr int kFK = 64;  // keys per tile
+#ifndef MTP_FWD_KH
+#define MTP_FWD_KH 2
+#endif
+constexpr int kKH = MTP_FWD_KH;  // key parts per tile (waves per query group)
+constexpr int kFK = 32 * kKH;    // keys per tile
+constexpr int kFW = 2 * kKH;     // waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -73,13 +78,13 @@ __device__ __forceinline__ int swz_val(int r) {
   return r & (D / 32 - 1);
 }
 
-// Copy keys [k0, k0+64) of one head's K (V) columns into an LDS tile.
+// Copy keys [k0, k0+kFK) of one head's K (V) columns into an LDS tile.
 template <int D, bool VAL>
 __device__ __forceinline__ void issue_kv(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int lane,
                                          int k0, int T, int col0, uint32_t ld_bytes) {
   constexpr int kCpr = D / 8;                 // chunks per key row
   constexpr int kInstr = kFK * kCpr / 64;     // 1 KB copies per tile
-  constexpr int kPer = kInstr / 4;
+  constexpr int kPer = kInstr / kFW;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = wave * kPer + i;
@@ -95,7 +100,7 @@ __device__ __forceinline__ void issue_kv(__amdgpu_buffer_rsrc_t rs, char* tile, 
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
+__global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) {
   constexpr int KS = D / 16;  // k-steps of S over d
   constexpr int DB = D / 32;  // 32-wide d blocks of O
   constexpr int kTileBytes = kFK * D * 2;
@@ -105,9 +110,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char sv1[kTileBytes];
 
   const int T = p.T;
-  const int nb = gridDim.x, half = (nb + 1) / 2;
-  const int b = blockIdx.x;
-  const int item = b < half ? b : nb - 1 - (b - half);
+  const int item = blockIdx.x;
   const int head = item % p.heads;
   const int qblk = p.nqb - 1 - item / p.heads;
   const int q0 = qblk * kFQ;
@@ -157,20 +160,44 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
   };
 
   auto compute = [&](const char* tk, const char* tv, int j0) {
-    const int ja = j0 + kh * 32;  // first key of this wave's half
+    const int ja = j0 + kh * 32;  // first key of this wave's part
     // Wave-uniform: skip when no (query, key) pair of the half is visible.
     if (qa >= T || ja > wq_last || ja + 31 < w_start_lo) return;
-    f32x16 sacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+    // Every LDS operand of the tile is read up front: the K rows of S^T and
+    // the V^T columns of the P V step (whose latency then hides under S and
+    // the softmax arithmetic).
     const int krow = kh * 32 + lq;
+    bf16x8 kfr[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int c = 2 * s + g;
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-          tk + krow * (D * 2) + ((c ^ swz_key<D>(krow)) << 4));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+      kfr[s] = *reinterpret_cast<const bf16x8*>(tk + krow * (D * 2) +
+                                                ((c ^ swz_key<D>(krow)) << 4));
     }
+    const int G = lane >> 4, s16 = lane & 15;
+    bf16x8 vfr[2][DB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r1 = kh * 32 + 16 * t + 4 * (G >> 1) + (s16 >> 2);
+      const int r2 = r1 + 8;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const int col = 32 * d + 16 * (G & 1) + 4 * (s16 & 3);
+        const int seg = col >> 5, within = (col & 31) * 2;
+        const v4i16 lo = tr_read(tv + r1 * (D * 2) + ((seg ^ swz_val<D>(r1)) << 6) + within);
+        const v4i16 hi = tr_read(tv + r2 * (D * 2) + ((seg ^ swz_val<D>(r2)) << 6) + within);
+        vfr[t][d] = cat_bf16x8(lo, hi);
+      }
+    }
+    f32x16 sacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], sacc, 0, 0, 0);
+    // all LDS reads of the tile first, then the S MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, KS + 4 * DB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
     const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
     if (!full) {
 #pragma unroll
@@ -205,22 +232,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
       l += p0 + p1;
       pk[e >> 1] = pack_bf2(p0, p1);
     }
-    // O^T += V^T P^T over the half's 32 keys, 16 per k-step.
-    const int G = lane >> 4, s16 = lane & 15;
+    // O^T += V^T P^T over the part's 32 keys, 16 per k-step.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bf16x8 pb = __builtin_bit_cast(
           bf16x8, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
-      const int r1 = kh * 32 + 16 * t + 4 * (G >> 1) + (s16 >> 2);
-      const int r2 = r1 + 8;
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const int col = 32 * d + 16 * (G & 1) + 4 * (s16 & 3);
-        const int seg = col >> 5, within = (col & 31) * 2;
-        const v4i16 lo = tr_read(tv + r1 * (D * 2) + ((seg ^ swz_val<D>(r1)) << 6) + within);
-        const v4i16 hi = tr_read(tv + r2 * (D * 2) + ((seg ^ swz_val<D>(r2)) << 6) + within);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16x8(lo, hi), pb, o[d], 0, 0, 0);
-      }
+      for (int d = 0; d < DB; ++d)
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t][d], pb, o[d], 0, 0, 0);
     }
   };
 
@@ -232,7 +251,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
   issue(sk0, sv0, kv_lo);
   issue(sk1, sv1, kv_lo + kFK);
   {
-    constexpr int kTileInstr = 2 * (kFK * (D / 8) / 64) / 4;
+    constexpr int kTileInstr = 2 * (kFK * (D / 8) / 64) / kFW;
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
     __syncthreads();
   }
@@ -248,26 +267,47 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Merge the two key halves of each query group.  The half-1 wave parks
-  // m, l and O in LDS (tile buffers are free now); the half-0 wave combines.
+  // Merge the KH key parts of each query group.  Waves of parts 1..KH-1
+  // park m, l and O in LDS (the tile buffers are free now; O of one wave
+  // takes half a tile buffer); the part-0 wave combines them in part order.
   l += __shfl_xor(l, 32, kWave);
-  float* park_o = reinterpret_cast<float*>(qg == 0 ? sk0 : sk1);
-  float* park_ml = reinterpret_cast<float*>(sv0) + qg * 128;
-  if (kh == 1) {
+  constexpr int kOBytes = DB * 16 * 64 * 4;
+  constexpr int kSlotsPerBuf = kTileBytes / kOBytes;
+  static_assert(3 * kSlotsPerBuf >= 2 * (kKH - 1), "merge slots");
+  auto slot_o = [&](int part) {
+    const int sl = qg * (kKH - 1) + (part - 1);
+    const int bi = sl / kSlotsPerBuf;
+    char* const buf = bi == 0 ? sk0 : bi == 1 ? sk1 : sv0;
+    return reinterpret_cast<float*>(buf + (sl % kSlotsPerBuf) * kOBytes);
+  };
+  float* park_ml = reinterpret_cast<float*>(sv1) + (qg * kKH) * 128;
+  if (kh > 0) {
+    float* po = slot_o(kh);
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) park_o[(d * 16 + e) * 64 + lane] = o[d][e];
-    park_ml[lane] = m;
-    park_ml[64 + lane] = l;
+      for (int e = 0; e < 16; ++e) po[(d * 16 + e) * 64 + lane] = o[d][e];
+    park_ml[kh * 128 + lane] = m;
+    park_ml[kh * 128 + 64 + lane] = l;
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = park_ml[lane], l1 = park_ml[64 + lane];
-    const float mf = fmaxf(m, m1);
-    const float a0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mf);
-    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mf);
-    const float lt = l * a0 + l1 * a1;
+    float mk[kKH], lk[kKH];
+    mk[0] = m;
+    lk[0] = l;
+    float mf = m;
+#pragma unroll
+    for (int k = 1; k < kKH; ++k) {
+      mk[k] = park_ml[k * 128 + lane];
+      lk[k] = park_ml[k * 128 + 64 + lane];
+      mf = fmaxf(mf, mk[k]);
+    }
+    float ak[kKH], lt = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kKH; ++k) {
+      ak[k] = mk[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk[k] - mf);
+      lt += lk[k] * ak[k];
+    }
     if (qvalid) {
       const float inv = 1.0f / lt;
       bf16_t* out = p.ctx + static_cast<int64_t>(qi) * p.hl + head * D;
@@ -279,7 +319,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_mfma(FwdParams p) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int e = 4 * a + c;
-            v[c] = (o[d][e] * a0 + park_o[(d * 16 + e) * 64 + lane] * a1) * inv;
+            const int idx = (d * 16 + e) * 64 + lane;
+            float acc = o[d][e] * ak[0];
+#pragma unroll
+            for (int k = 1; k < kKH; ++k) acc += slot_o(k)[idx] * ak[k];
+            v[c] = acc * inv;
           }
           store4(out + 32 * d + 8 * a + 4 * g, v);
         }
@@ -309,8 +353,8 @@ hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   if (bytes >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;
   p.qkv_bytes = static_cast<uint32_t>(bytes);
   const dim3 grid(static_cast<unsigned>(p.nqb * a.heads));
-  if (a.head_dim == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(256), 0, s, p);
-  else if (a.head_dim == 64) hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(256), 0, s, p);
+  if (a.head_dim == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(64 * kFW), 0, s, p);
+  else if (a.head_dim == 64) hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(64 * kFW), 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
