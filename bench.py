@@ -43,6 +43,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # concurrently with the data-gradient chain, so their durations include
 # sharing the CUs and are reported separately.
 FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
+# Every call of one step, in issue order (the per-call times of the probed steps).
+CALL_TAGS = ("ln1", "qkv_fwd", "attn_fwd", "proj_fwd", "sum_proj_ln2", "fc1_fwd", "fc2_fwd",
+             "sum_fc2", "fc2_dgrad", "fc2_wgrad", "fc2_bias", "fc1_dgrad", "fc1_wgrad", "ln2_bwd",
+             "proj_dgrad", "proj_wgrad", "attn_bwd", "qkv_dgrad", "qkv_wgrad", "ln1_bwd")
 PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
 FWD_KERNEL = "gemm_bf16_kernel, forward layout (k-major A and B, bf16 C, fused bias/GeLU)"
@@ -115,12 +119,25 @@ def cpu_baseline(cfg, data) -> dict:
     """The fp64 oracle (as it stands) on the host: one unsharded fwd+bwd."""
     import numpy as np
     import oracle
+    blas = "numpy BLAS"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 0) for i in info), default=0)
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                                 for i in info if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = 0
     threads = threads or len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens", "targets")}
     starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
     t0 = time.perf_counter()
@@ -131,11 +148,11 @@ def cpu_baseline(cfg, data) -> dict:
     fl = shard_flops(full, data["cu_seqlens"].tolist())["total"]
     del np
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model, "blas": blas,
             "tokens_per_s": round(cfg.tokens / dt, 1),
             "sample": f"one unsharded fp64 forward+backward of the {cfg.name} layer "
                       f"({cfg.tokens} tokens, all {cfg.tp} shards' work; "
-                      f"{fl / 1e9:.0f} model GFLOP), numpy/OpenBLAS"}
+                      f"{fl / 1e9:.0f} model GFLOP), numpy fp64"}
 
 
 def main(argv=None) -> int:
@@ -223,6 +240,57 @@ def main(argv=None) -> int:
     ms = e0.elapsed_time(e1) / args.steps
     L.probe = None
 
+    # Spread: the same steps once more, each between its own pair of events
+    # (which adds the events' own gaps to every step).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in ev)
+
+    def pct(q):
+        return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 4)
+
+    # Per-call times: a few more steps with events around every call.
+    calls = {t: [] for t in CALL_TAGS}
+    n_call_steps = 5
+    L.probe = calls
+    for _ in range(n_call_steps):
+        step()
+    torch.cuda.synchronize()
+    L.probe = None
+    call_us = {t: round(1e3 * sum(a.elapsed_time(b) for a, b in calls[t]) / n_call_steps, 1)
+               for t in CALL_TAGS if calls[t]}
+
+    # The same step replayed from a HIP graph (captured once, inputs unchanged).
+    graph_ms = None
+    try:
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = round(a.elapsed_time(b) / args.steps, 4)
+        del g
+    except RuntimeError as exc:  # capture unsupported: report it, keep the eager figure
+        graph_ms = f"capture failed: {exc}"[:200]
+
     fl = shard_flops(cfg, cu)
     tflops = fl["total"] / (ms * 1e-3) / 1e12
     out = {
@@ -248,6 +316,9 @@ def main(argv=None) -> int:
         "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),
         "model_gflop_per_step": round(fl["total"] / 1e9, 2),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "graph_replay_ms_per_step": graph_ms,
+        "call_us_per_step": call_us,
         "roofline": roofline(FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms, len(probed)),
         "roofline_wgrad_overlapped": roofline(WGRAD_KERNEL, WGRAD_TAGS, probes, fl["call"], ms,
                                               len(probed)),

@@ -223,7 +223,7 @@ class TPLayer:
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, g["dw2"],
                                        None, 0, wss, wsb)
             if db2 is not None:
-                with on_side():
+                with on_side(), T("fc2_bias", side):
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
                                            db2, 0, wss, wsb)
             with T("fc1_dgrad"):
