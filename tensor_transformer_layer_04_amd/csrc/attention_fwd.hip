@@ -6,21 +6,24 @@
 // exchange between ranks and the softmax runs in fp32 (page "Megatron-LM 3D
 // parallelism guide", §2.1 and the attention_softmax_in_fp32 flag of §3.2).
 //
-// Work decomposition (one workgroup = 2*KH waves, 64 queries of one head):
-//  * waves (g, h) for query group g in {0,1} (32 queries) and key part h in
-//    [0, KH): every tile of 32*KH keys is split into KH parts of 32 keys, so
-//    KH waves share each query group.  With KH = 4 a workgroup is 8 waves and
-//    one workgroup fills a CU with 2 waves per SIMD that all work on the same
-//    (possibly long) causal row block; the parts keep separate online-softmax
-//    states and are merged exactly at the end.
+// Work decomposition (one workgroup = QG*KH waves, 32*QG queries of one head):
+//  * waves (g, h) for query group g in [0, QG) (32 queries) and key part h
+//    in [0, KH): every tile of 32*KH keys is split into KH parts of 32 keys,
+//    so KH waves share each query group and keep separate online-softmax
+//    states, merged exactly at the end.  QG = KH = 2 (four waves, two
+//    workgroups per CU) measured best at the 7B shard shape: four query
+//    groups halve the K/V copies per (query, key) pair but leave one
+//    workgroup per CU with nothing to balance the long causal row blocks.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 puts one query per lane (16
 //    keys each, the other 16 in lane ^ 32), so row max and row sum are
 //    in-lane plus one exchange.  P^T then feeds O^T += V^T P^T straight from
 //    registers; its contraction order is the key order the lane holds
 //    ({4g..4g+3, 8+4g..8+4g+3} per 16 keys), and V^T is gathered from the
 //    natural [key][d] tile in that order with ds_read_b64_tr_b16.
-//  * K and V tiles go HBM -> LDS with buffer_load ... lds, double-buffered;
-//    keys outside [0, T) read as zeros (buffer offset past num_records).
+//  * K and V tiles go HBM -> LDS with buffer_load ... lds; keys outside
+//    [0, T) read as zeros (buffer offset past num_records).  The loop is
+//    software-pipelined: K runs two tiles ahead and V one, and the S MFMAs
+//    of the next tile are issued before the softmax of the current one.
 //  * Scores stay in log2 units: p = exp2(s * scale * log2(e) - m) is one FMA
 //    and one v_exp_f32.  The reference max m of a row moves (and O is
 //    rescaled) only when a tile's max exceeds it by more than 8, so p < 2^8;
@@ -34,13 +37,17 @@
 namespace mtp {
 namespace {
 
-constexpr int kFQ = 64;  // queries per workgroup
+#ifndef MTP_FWD_QG
+#define MTP_FWD_QG 2
+#endif
 #ifndef MTP_FWD_KH
 #define MTP_FWD_KH 2
 #endif
-constexpr int kKH = MTP_FWD_KH;  // key parts per tile (waves per query group)
+constexpr int kQG = MTP_FWD_QG;  // query groups of 32 per workgroup
+constexpr int kKH = MTP_FWD_KH;  // key parts of 32 per tile (waves per query group)
+constexpr int kFQ = 32 * kQG;    // queries per workgroup
 constexpr int kFK = 32 * kKH;    // keys per tile
-constexpr int kFW = 2 * kKH;     // waves per workgroup
+constexpr int kFW = kQG * kKH;   // waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -85,6 +92,7 @@ __device__ __forceinline__ void issue_kv(__amdgpu_buffer_rsrc_t rs, char* tile, 
   constexpr int kCpr = D / 8;                 // chunks per key row
   constexpr int kInstr = kFK * kCpr / 64;     // 1 KB copies per tile
   constexpr int kPer = kInstr / kFW;
+  static_assert(kInstr % kFW == 0, "copies split evenly over the waves");
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = wave * kPer + i;
@@ -100,7 +108,7 @@ __device__ __forceinline__ void issue_kv(__amdgpu_buffer_rsrc_t rs, char* tile, 
 }
 
 template <int D>
-__global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) {
+__global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(FwdParams p) {
   constexpr int KS = D / 16;  // k-steps of S over d
   constexpr int DB = D / 32;  // 32-wide d blocks of O
   constexpr int kTileBytes = kFK * D * 2;
@@ -117,7 +125,7 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qg = wave & 1, kh = wave >> 1;
+  const int qg = wave % kQG, kh = wave / kQG;
   const int lq = lane & 31, g = lane >> 5;
   const int qa = q0 + qg * 32;            // first query of this wave
   const int qi = qa + lq;                 // this lane's query
@@ -154,18 +162,17 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
     for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
   float m = -INFINITY, l = 0.0f;
 
-  auto issue = [&](char* tk, char* tv, int k0) {
-    issue_kv<D, false>(rs, tk, wave, lane, k0, T, kcol, ld_bytes);
-    issue_kv<D, true>(rs, tv, wave, lane, k0, T, vcol, ld_bytes);
+  auto issue_k = [&](char* tk, int k0) { issue_kv<D, false>(rs, tk, wave, lane, k0, T, kcol, ld_bytes); };
+  auto issue_v = [&](char* tv, int k0) { issue_kv<D, true>(rs, tv, wave, lane, k0, T, vcol, ld_bytes); };
+  // Wave-uniform: does any (query, key) pair of this wave's part of the tile
+  // at key j0 exist?
+  auto visible = [&](int j0) {
+    const int ja = j0 + kh * 32;
+    return !(qa >= T || ja > wq_last || ja + 31 < w_start_lo);
   };
 
-  auto compute = [&](const char* tk, const char* tv, int j0) {
-    const int ja = j0 + kh * 32;  // first key of this wave's part
-    // Wave-uniform: skip when no (query, key) pair of the half is visible.
-    if (qa >= T || ja > wq_last || ja + 31 < w_start_lo) return;
-    // Every LDS operand of the tile is read up front: the K rows of S^T and
-    // the V^T columns of the P V step (whose latency then hides under S and
-    // the softmax arithmetic).
+  // S^T of this wave's part of the tile at key j0 (K rows from LDS).
+  auto s_tile = [&](const char* tk) {
     const int krow = kh * 32 + lq;
     bf16x8 kfr[KS];
 #pragma unroll
@@ -174,6 +181,21 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
       kfr[s] = *reinterpret_cast<const bf16x8*>(tk + krow * (D * 2) +
                                                 ((c ^ swz_key<D>(krow)) << 4));
     }
+    f32x16 sacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+    return sacc;
+  };
+
+  // Online softmax of the scores of the tile at key j0 and O^T += V^T P^T.
+  auto softmax_pv = [&](f32x16 sacc, const char* tv, int j0) {
+    const int ja = j0 + kh * 32;
+    // V^T operands first: their latency hides under the softmax arithmetic.
     const int G = lane >> 4, s16 = lane & 15;
     bf16x8 vfr[2][DB];
 #pragma unroll
@@ -189,15 +211,6 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
         vfr[t][d] = cat_bf16x8(lo, hi);
       }
     }
-    f32x16 sacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], sacc, 0, 0, 0);
-    // all LDS reads of the tile first, then the S MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, KS + 4 * DB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
     const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
     if (!full) {
 #pragma unroll
@@ -209,7 +222,7 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
     float mt = sacc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * p.scale_log2;
+    mt = xor32_max(mt) * p.scale_log2;
     // The reference max m only moves when some lane's tile max exceeds it
     // by more than 8 (log2 units): p = exp2(s - m) then stays below 2^8 and
     // the rescale of O and l is skipped for most tiles.
@@ -243,26 +256,38 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
     }
   };
 
-  auto stage_ready = [&]() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  issue(sk0, sv0, kv_lo);
-  issue(sk1, sv1, kv_lo + kFK);
+  // Software pipeline over key tiles t = 0 .. nt-1 (nt even; tiles past the
+  // visible range are skipped, tiles past T load zeros).  K runs two tiles
+  // ahead and V one: tile t's K is in kbuf[t % 2], its V in vbuf[t % 2].
+  // Iteration t, after its barrier (which both publishes the copies issued
+  // one iteration earlier and retires every read of the buffers refilled
+  // next): copy K(t+2) into kbuf[t % 2] and V(t+1) into vbuf[(t+1) % 2],
+  // issue the S MFMAs of tile t+1, then the softmax and P V of tile t, so the
+  // matrix cores work on S(t+1) while the vector units run tile t's softmax.
+  issue_k(sk0, kv_lo);
+  issue_k(sk1, kv_lo + kFK);
+  issue_v(sv0, kv_lo);
   {
-    constexpr int kTileInstr = 2 * (kFK * (D / 8) / 64) / kFW;
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
+    constexpr int kPerTile = (kFK * (D / 8) / 64) / kFW;  // copies per wave per tile
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kPerTile) : "memory");
     __syncthreads();
   }
-  for (int t = 0; t < nt; t += 2) {
+  f32x16 s_cur = visible(kv_lo) ? s_tile(sk0) : f32x16{};
+  auto iteration = [&](char* k_free, const char* k_next, const char* v_cur, char* v_free, int t) {
     const int j0 = kv_lo + t * kFK;
-    compute(sk0, sv0, j0);
-    stage_ready();
-    issue(sk0, sv0, j0 + 2 * kFK);
-    compute(sk1, sv1, j0 + kFK);
-    stage_ready();
-    issue(sk1, sv1, j0 + 3 * kFK);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue_k(k_free, j0 + 2 * kFK);
+    issue_v(v_free, j0 + kFK);
+    const bool vis_next = visible(j0 + kFK);
+    f32x16 s_next{};
+    if (vis_next) s_next = s_tile(k_next);
+    if (visible(j0)) softmax_pv(s_cur, v_cur, j0);
+    s_cur = s_next;
+  };
+  for (int t = 0; t < nt; t += 2) {
+    iteration(sk0, sk1, sv0, sv1, t);
+    iteration(sk1, sk0, sv1, sv0, t + 1);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
@@ -270,17 +295,18 @@ __global__ void __launch_bounds__(64 * kFW, 8 / kFW) attn_fwd_mfma(FwdParams p) 
   // Merge the KH key parts of each query group.  Waves of parts 1..KH-1
   // park m, l and O in LDS (the tile buffers are free now; O of one wave
   // takes half a tile buffer); the part-0 wave combines them in part order.
-  l += __shfl_xor(l, 32, kWave);
+  l = xor32_sum(l);
   constexpr int kOBytes = DB * 16 * 64 * 4;
   constexpr int kSlotsPerBuf = kTileBytes / kOBytes;
-  static_assert(3 * kSlotsPerBuf >= 2 * (kKH - 1), "merge slots");
+  static_assert(4 * kSlotsPerBuf >= kQG * (kKH - 1), "merge slots");
   auto slot_o = [&](int part) {
     const int sl = qg * (kKH - 1) + (part - 1);
     const int bi = sl / kSlotsPerBuf;
-    char* const buf = bi == 0 ? sk0 : bi == 1 ? sk1 : sv0;
+    char* const buf = bi == 0 ? sk0 : bi == 1 ? sk1 : bi == 2 ? sv0 : sv1;
     return reinterpret_cast<float*>(buf + (sl % kSlotsPerBuf) * kOBytes);
   };
-  float* park_ml = reinterpret_cast<float*>(sv1) + (qg * kKH) * 128;
+  __shared__ float park_mls[kQG * kKH * 128];
+  float* park_ml = park_mls + (qg * kKH) * 128;
   if (kh > 0) {
     float* po = slot_o(kh);
 #pragma unroll

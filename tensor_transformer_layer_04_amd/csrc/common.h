@@ -117,14 +117,30 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
   return s * fmaf(u * (1.0f - s) * (2.0f * kGeluC), fmaf(3.0f * kGeluA * u, u, 1.0f), 1.0f);
 }
 
+// v combined with the value of lane ^ 32: v_permlane32_swap exchanges the
+// two 32-lane halves without an LDS round trip; the pair it returns holds,
+// in every lane, the lower-half value first and the upper-half value second.
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
+  v = xor32_sum(v);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 __device__ __forceinline__ float warp_max(float v) {
+  v = xor32_max(v);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
