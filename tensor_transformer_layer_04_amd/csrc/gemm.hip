@@ -40,6 +40,7 @@ namespace mtp {
 namespace {
 
 constexpr int kBK = 64;
+
 constexpr int kGroupM = 8;
 
 struct GemmParams {
@@ -258,32 +259,54 @@ gemm_bf16_kernel(GemmParams p) {
     __syncthreads();
   };
 
-  // Pipeline over k-tiles (stage s holds tile kt):
-  //   steps 0..2 of tile kt, each prefetching the next step's fragments;
-  //   wait for the next tile's copy and for every wave to finish reading
-  //   stage s (all of tile kt's fragments are in registers by now);
-  //   refill stage s with tile kt+2; step 3 of tile kt, prefetching step 0
-  //   of tile kt+1 from the other stage.
+  // Pipeline over k-tiles (stage kt % 2 holds tile kt):
+  //   steps 1..3 of tile kt, each prefetching the next step's fragments;
+  //   wait for tile kt+1's copies and for every wave to finish reading
+  //   stage kt % 2 (all of tile kt's fragments are in registers by now);
+  //   then step 3 of tile kt, which prefetches step 0 of tile kt+1 from the
+  //   other stage and, one copy per MFMA, refills stage kt % 2 with tile
+  //   kt+2 (issued as a burst after the barrier, the copies of all waves
+  //   queued behind each other and the last waves reached the next barrier
+  //   late).
   // The barrier thus sits before the last k-step, whose MFMAs cover the
-  // first fragment reads of the next tile.  The tile count is rounded up to
-  // even so that the two stages alternate in a branch-free loop: tiles past
-  // K (and copies issued for them) are all-zero loads that add nothing.
+  // first fragment reads of the next tile and the refill.  The tile count is
+  // rounded up to even so that the stages alternate in a branch-free loop:
+  // tiles past K (and copies issued for them) are all-zero loads that add
+  // nothing.
+  constexpr int kCopies = (BM / 8 + BN / 8) / NW;  // copies per wave per tile
   const int nk = ((p.K + kBK - 1) / kBK + 1) & ~1;
   Frags f0, f1;
+  auto step_dma = [&](const Frags& f, const char* ta, const char* tb, char* ca, char* cb, int k0,
+                      Frags& nf) {
+    issue(ca, cb, k0);
+    load_frags(ta, tb, 0, nf);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < FM * FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t < kCopies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kPerMfma, 0);
+    }
+    if (kCopies > FM * FN) __builtin_amdgcn_sched_group_barrier(0x020, kCopies - FM * FN, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto tile = [&](char* ca, char* cb, char* na, char* nb, int kt) {
     step(f0, true, ca, cb, 1, f1);
     step(f1, true, ca, cb, 2, f0);
     step(f0, true, ca, cb, 3, f1);
-    stage_ready();
-    issue(ca, cb, (kt + 2) * kBK);
-    step(f1, true, na, nb, 0, f0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    step_dma(f1, na, nb, ca, cb, (kt + 2) * kBK, f0);
   };
   if (nk > 0) {
     issue(lds_a0, lds_b0, 0);
     issue(lds_a1, lds_b1, kBK);
     // Only tile 0 is needed now: tile 1's copies may stay in flight.
-    constexpr int kTileInstr = (BM / 8 + BN / 8) / NW;
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileInstr) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopies) : "memory");
     __syncthreads();
     load_frags(lds_a0, lds_b0, 0, f0);
     for (int kt = 0; kt < nk; kt += 2) {
