@@ -40,6 +40,7 @@ namespace mtp {
 namespace {
 
 constexpr int kBK = 64;
+template <int N> struct IntTag { static constexpr int v = N; };
 
 constexpr int kGroupM = 8;
 
@@ -264,22 +265,25 @@ gemm_bf16_kernel(GemmParams p) {
   //   wait for tile kt+1's copies and for every wave to finish reading
   //   stage kt % 2 (all of tile kt's fragments are in registers by now);
   //   then step 3 of tile kt, which prefetches step 0 of tile kt+1 from the
-  //   other stage and, one copy per MFMA, refills stage kt % 2 with tile
-  //   kt+2 (issued as a burst after the barrier, the copies of all waves
-  //   queued behind each other and the last waves reached the next barrier
-  //   late).
+  //   other stage.  The copies that refill the stages are issued one per
+  //   MFMA in two k-steps (A after the barrier, B in the next tile's first
+  //   step) rather than as a burst after the barrier, where the copies of
+  //   all waves queued behind each other and the last waves reached the
+  //   next barrier late.
   // The barrier thus sits before the last k-step, whose MFMAs cover the
-  // first fragment reads of the next tile and the refill.  The tile count is
-  // rounded up to even so that the stages alternate in a branch-free loop:
-  // tiles past K (and copies issued for them) are all-zero loads that add
-  // nothing.
-  constexpr int kCopies = (BM / 8 + BN / 8) / NW;  // copies per wave per tile
+  // first fragment reads of the next tile.  The tile count is rounded up to
+  // even so that the stages alternate in a branch-free loop: tiles past K
+  // (and copies issued for them) are all-zero loads that add nothing.
   const int nk = ((p.K + kBK - 1) / kBK + 1) & ~1;
   Frags f0, f1;
-  auto step_dma = [&](const Frags& f, const char* ta, const char* tb, char* ca, char* cb, int k0,
-                      Frags& nf) {
-    issue(ca, cb, k0);
-    load_frags(ta, tb, 0, nf);
+  // One k-step (MFMAs on f, fragment reads of step kk into nf) with nc
+  // operand copies issued between its MFMAs, one per MFMA.
+  constexpr int kCopiesA = BM / 8 / NW, kCopiesB = BN / 8 / NW;
+  auto step_c = [&](const Frags& f, const char* ta, const char* tb, int kk, Frags& nf,
+                    auto&& copies, auto nc_tag) {
+    constexpr int nc = decltype(nc_tag)::v;
+    copies();
+    load_frags(ta, tb, kk, nf);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -288,25 +292,36 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int t = 0; t < FM * FN; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t < kCopies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (t < nc) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, kPerMfma, 0);
     }
-    if (kCopies > FM * FN) __builtin_amdgcn_sched_group_barrier(0x020, kCopies - FM * FN, 0);
+    if constexpr (nc > FM * FN) __builtin_amdgcn_sched_group_barrier(0x020, nc - FM * FN, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto copy_a = [&](char* sa, int k0) {
+    issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
+  };
+  auto copy_b = [&](char* sb, int k0) {
+    issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
+  };
+  // Tile kt: its first k-step also copies B of tile kt+1 into the other
+  // stage (free since the previous barrier); after the barrier, the last
+  // k-step copies A of tile kt+2 into this tile's stage.  Both land before
+  // the barrier of tile kt+1, which waits for them.
   auto tile = [&](char* ca, char* cb, char* na, char* nb, int kt) {
-    step(f0, true, ca, cb, 1, f1);
+    step_c(f0, ca, cb, 1, f1, [&] { copy_b(nb, (kt + 1) * kBK); }, IntTag<kCopiesB>{});
     step(f1, true, ca, cb, 2, f0);
     step(f0, true, ca, cb, 3, f1);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    step_dma(f1, na, nb, ca, cb, (kt + 2) * kBK, f0);
+    step_c(f1, na, nb, 0, f0, [&] { copy_a(ca, (kt + 2) * kBK); }, IntTag<kCopiesA>{});
   };
   if (nk > 0) {
-    issue(lds_a0, lds_b0, 0);
-    issue(lds_a1, lds_b1, kBK);
-    // Only tile 0 is needed now: tile 1's copies may stay in flight.
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopies) : "memory");
+    copy_a(lds_a0, 0);
+    copy_b(lds_b0, 0);
+    copy_a(lds_a1, kBK);
+    // Only tile 0 is needed now: tile 1's A copies may stay in flight.
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopiesA) : "memory");
     __syncthreads();
     load_frags(lds_a0, lds_b0, 0, f0);
     for (int kt = 0; kt < nk; kt += 2) {
