@@ -130,6 +130,22 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int off) {
                                                pack_bf2(a[off + 6], a[off + 7])));
 }
 
+// Schedule N LDS reads and the N MFMAs that consume them in order with a
+// window of kWin reads in flight: kWin reads, then (MFMA, read) pairs, then
+// the last kWin MFMAs.
+constexpr int kWin = 4;
+template <int N>
+__device__ __forceinline__ void window_schedule() {
+  constexpr int W = N > kWin ? kWin : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, W, 0);
+#pragma unroll
+  for (int t = 0; t < N - W; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, W, 0);
+}
+
 __device__ __forceinline__ int balanced_item(int b, int nb) {
   const int half = (nb + 1) / 2;
   return b < half ? b : nb - 1 - (b - half);
@@ -222,15 +238,29 @@ __global__ void __launch_bounds__(256, 2) attn_dkv_mfma(BwdParams p) {
     f32x16 s_acc, p_acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s_acc[e] = 0.0f; p_acc[e] = 0.0f; }
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, rb + lk, 2 * s + g), kf[s],
-                                                      s_acc, 0, 0, 0);
+    // The Q (and dO) row fragments are read a window of kWin reads ahead of
+    // the MFMAs that use them, so LDS latency overlaps the matrix pipe.
     if (want_dk) {
+      bf16x8 fr[2 * KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        fr[2 * s] = row_frag<D>(tq, rb + lk, 2 * s + g);
+        fr[2 * s + 1] = row_frag<D>(to, rb + lk, 2 * s + g);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * s], kf[s], s_acc, 0, 0, 0);
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * s + 1], vf[s], p_acc, 0, 0, 0);
+      }
+      window_schedule<2 * KS>();
+    } else {
+      bf16x8 fr[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) fr[s] = row_frag<D>(tq, rb + lk, 2 * s + g);
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(to, rb + lk, 2 * s + g),
-                                                        vf[s], p_acc, 0, 0, 0);
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[s], kf[s], s_acc, 0, 0, 0);
+      window_schedule<KS>();
     }
     // accumulator rows: query qa + 8 (e/4) + 4 g + e%4; column: key kj.
     // Query qi sees key kj iff kj <= qi < end of kj's sequence; a tile whose
@@ -394,12 +424,19 @@ __global__ void __launch_bounds__(256, 2) attn_dq_mfma(BwdParams p) {
     f32x16 s_acc, p_acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s_acc[e] = 0.0f; p_acc[e] = 0.0f; }
+    {
+      bf16x8 fr[2 * KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tk, rb + lq, 2 * s + g), qf[s],
-                                                      s_acc, 0, 0, 0);
-      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tv, rb + lq, 2 * s + g), of[s],
-                                                      p_acc, 0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        fr[2 * s] = row_frag<D>(tk, rb + lq, 2 * s + g);
+        fr[2 * s + 1] = row_frag<D>(tv, rb + lq, 2 * s + g);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * s], qf[s], s_acc, 0, 0, 0);
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * s + 1], of[s], p_acc, 0, 0, 0);
+      }
+      window_schedule<2 * KS>();
     }
     // Rows: key ja + 8 (e/4) + 4 g + e%4; column: query qi.
     const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
