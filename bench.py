@@ -47,6 +47,7 @@ FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
 CALL_TAGS = ("ln1", "qkv_fwd", "attn_fwd", "proj_fwd", "sum_proj_ln2", "fc1_fwd", "fc2_fwd",
              "sum_fc2", "fc2_dgrad", "fc2_wgrad", "fc2_bias", "fc1_dgrad", "fc1_wgrad", "ln2_bwd",
              "proj_dgrad", "proj_wgrad", "attn_bwd", "qkv_dgrad", "qkv_wgrad", "ln1_bwd")
+HEAD_TAGS = ("vocab_fwd", "ce_stats", "ce_combine", "ce_bwd", "vocab_bwd", "sum_vocab_dy")
 PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
 FWD_KERNEL = "gemm_bf16_kernel, forward layout (k-major A and B, bf16 C, fused bias/GeLU)"
@@ -138,21 +139,44 @@ def cpu_baseline(cfg, data) -> dict:
                     break
     except OSError:  # pragma: no cover
         pass
-    p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens", "targets")}
-    starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    # The whole layer when it is small enough for tens of seconds of host
+    # work, else the first P tokens (a causal layer's output on a token
+    # prefix depends on that prefix only), P sized to about 2.5 TFLOP.
+    cu = data["cu_seqlens"].tolist()
+    layer_only = cfg.replace(tp=1, vocab=0)
+
+    def prefix_flops(n):
+        return shard_flops(layer_only.replace(seq_len=n, micro_batch=1, varlen_tokens=0),
+                           prefix_cu(cu, n))["total"]
+    P = cfg.tokens
+    while P > 64 and prefix_flops(P) > 2.5e12:
+        P //= 2
+    pcu = prefix_cu(cu, P)
+    p64 = {k: oracle.to64(v) for k, v in data.items()
+           if k not in ("cu_seqlens", "targets", "emb", "x", "dy")}
+    x64 = oracle.to64(data["x"][:P])
+    dy64 = oracle.to64(data["dy"][:P]) if "dy" in data else np.ones_like(x64)
+    starts = oracle.doc_starts(pcu, P)
     t0 = time.perf_counter()
-    c = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
-    oracle.layer_backward(p64, c, p64["dy"], cfg.heads, starts)
+    c = oracle.layer_forward(p64, x64, cfg.heads, cfg.eps, starts)
+    oracle.layer_backward(p64, c, dy64, cfg.heads, starts)
     dt = time.perf_counter() - t0
-    full = cfg.replace(tp=1)
-    fl = shard_flops(full, data["cu_seqlens"].tolist())["total"]
+    fl = prefix_flops(P)
+    what = (f"one unsharded fp64 forward+backward of the {cfg.name} layer ({P} tokens, all "
+            f"{cfg.tp} shards' work; {fl / 1e9:.0f} model GFLOP), numpy fp64")
+    if P < cfg.tokens or cfg.vocab:
+        what += (f"; the first {P} of {cfg.tokens} tokens"
+                 + (", layer without the vocab head" if cfg.vocab else ""))
     del np
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model, "blas": blas,
-            "tokens_per_s": round(cfg.tokens / dt, 1),
-            "sample": f"one unsharded fp64 forward+backward of the {cfg.name} layer "
-                      f"({cfg.tokens} tokens, all {cfg.tp} shards' work; "
-                      f"{fl / 1e9:.0f} model GFLOP), numpy fp64"}
+            "tokens_per_s": round(P / dt, 1), "sample": what}
+
+
+def prefix_cu(cu, P):
+    """Sequence offsets of the first P tokens of a packed batch."""
+    out = [c for c in cu if c < P] + [P]
+    return out if out[0] == 0 else [0] + out
 
 
 def main(argv=None) -> int:
@@ -178,7 +202,7 @@ def main(argv=None) -> int:
 
     import torch
     import synth
-    from tensor_transformer_layer_04_amd.layer import TPLayer
+    from tensor_transformer_layer_04_amd.layer import TPLayer, VocabHead
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU (no GPU visible)", file=sys.stderr)
@@ -192,31 +216,44 @@ def main(argv=None) -> int:
         print("copy probe: 5 x 256 MiB read + 256 MiB written", flush=True)
         return 0
     cfg = synth.get_config(args.config)
-    if cfg.vocab:
-        print("bench.py times layer configs without the vocab head", file=sys.stderr)
-        return 2
     data = synth.generate(cfg)
     cu = data["cu_seqlens"].tolist()
     dev = "cuda"
     x = data["x"].to(dev)
-    dy = data["dy"].to(dev)
+    # With a vocab head the layer's upstream gradient comes from the head.
+    dy = data["dy"].to(dev) if not cfg.vocab else None
 
-    ext = None
+    ext, head_ext = None, ((), ())
     if cfg.tp > 1:
-        # The other ranks' partials of this very step, computed once and kept
-        # resident: the timed shard's t-way sums read them as inputs.
+        # The other ranks' partials of this very step (and, with a vocab head,
+        # their CE stats and dy partials), computed once and kept resident:
+        # the timed shard's t-way sums read them as inputs.
         full = TPLayer(cfg, data, device=dev, cu_seqlens=data["cu_seqlens"])
         full.forward(x)
-        full.backward(dy)
+        if cfg.vocab:
+            head = VocabHead(cfg, data, device=dev)
+            head.forward(full.y)
+            full.backward(head.backward())
+            stats, dys = head.partials()
+            others = [i for i, r in enumerate(head.ranks) if r != args.rank]
+            head_ext = ([stats[i] for i in others], [dys[i] for i in others])
+            del head
+        else:
+            full.backward(dy)
         parts = full.partials()
         ext = {k: [v[i] for i, r in enumerate(full.ranks) if r != args.rank] for k, v in parts.items()}
         del full
         torch.cuda.synchronize()
     L = TPLayer(cfg, data, ranks=[args.rank], device=dev, cu_seqlens=data["cu_seqlens"])
+    H = VocabHead(cfg, data, ranks=[args.rank], device=dev) if cfg.vocab else None
 
     def step():
         L.forward(x, ext)
-        L.backward(dy, ext)
+        if H is None:
+            L.backward(dy, ext)
+        else:
+            H.forward(L.y, head_ext[0])
+            L.backward(H.backward(head_ext[1]), ext)
 
     for _ in range(args.warmup):
         step()
@@ -255,15 +292,19 @@ def main(argv=None) -> int:
         return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 4)
 
     # Per-call times: a few more steps with events around every call.
-    calls = {t: [] for t in CALL_TAGS}
+    calls = {t: [] for t in CALL_TAGS + HEAD_TAGS}
     n_call_steps = 5
     L.probe = calls
+    if H is not None:
+        H.probe = calls
     for _ in range(n_call_steps):
         step()
     torch.cuda.synchronize()
     L.probe = None
+    if H is not None:
+        H.probe = None
     call_us = {t: round(1e3 * sum(a.elapsed_time(b) for a, b in calls[t]) / n_call_steps, 1)
-               for t in CALL_TAGS if calls[t]}
+               for t in CALL_TAGS + HEAD_TAGS if calls[t]}
 
     # The same step replayed from a HIP graph (captured once, inputs unchanged).
     graph_ms = None
@@ -307,7 +348,8 @@ def main(argv=None) -> int:
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic: seeded x, dy ~ N(0,1), weights ~ N(0,0.02), biases 0, LN gamma 1",
         "config": {
-            "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard fwd+bwd",
+            "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard"
+                        + (" + vocab-parallel CE head" if cfg.vocab else "") + " fwd+bwd",
             "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn, "tp": cfg.tp,
             "rank": args.rank, "seq_len": cfg.seq_len, "micro_batch": cfg.micro_batch,
             "tokens": cfg.tokens, "global_batch": cfg.micro_batch, "parallelism": f"tp{cfg.tp}-shard",

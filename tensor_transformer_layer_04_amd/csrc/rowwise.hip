@@ -510,10 +510,10 @@ sum_layernorm_fwd_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
 // mean(gh) - xhat*mean(gh*xhat)), gh = dy*gamma, as in the row kernels
 // above.  The same pass accumulates the column sums of dy*xhat and dy
 // (dgamma, dbeta).  A workgroup has 8 waves; a row of h = 512*NC elements is
-// held by SPLIT waves (NC/SPLIT 16-byte chunks per lane, SPLIT = 2 for the
-// widest rows so that two workgroups fit a CU), so 8/SPLIT rows are in
-// flight per iteration and the SPLIT waves of a row add their two row sums
-// through LDS (in wave order).  Row slot q of workgroup b takes rows
+// held by SPLIT waves (NC/SPLIT 16-byte chunks per lane: SPLIT grows with
+// the row width so that the registers allow two waves per SIMD), so
+// 8/SPLIT rows are in flight per iteration and the SPLIT waves of a row add
+// their two row sums through LDS (in wave order).  Row slot q of workgroup b takes rows
 // q + (8/SPLIT)*b + k*(8/SPLIT)*gridDim.x.  Each lane sums dy*xhat and dy
 // over its rows; the slots' sums are then added in slot order through LDS
 // and workgroup b writes row b of the partial matrices, which
@@ -843,11 +843,20 @@ static int64_t ln_bwd_blocks(int64_t T) {
   return b > 256 ? 256 : b;
 }
 
-// Chunks per lane of the fused row kernels (h = 512*NC), 0 if h does not fit.
+// Chunks per lane of a one-wave-per-row fused kernel (h = 512*NC), 0 if h
+// does not fit (the partial sum + LayerNorm forward).
 static int fused_row_nc(int h) {
   if (h % 512 != 0) return 0;
   const int nc = h / 512;
   return (nc == 1 || nc == 2 || nc == 4 || nc == 8) ? nc : 0;
+}
+
+// Chunks per row of the fused LayerNorm backward (a row split over up to 8
+// waves), 0 if h does not fit.
+static int fused_bwd_nc(int h) {
+  if (h % 512 != 0) return 0;
+  const int nc = h / 512;
+  return (nc == 1 || nc == 2 || nc == 4 || nc == 8 || nc == 16 || nc == 24 || nc == 32) ? nc : 0;
 }
 
 static size_t round_up256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -855,7 +864,7 @@ static size_t round_up256(size_t b) { return (b + 255) & ~static_cast<size_t>(25
 size_t layernorm_bwd_ws_bytes(int64_t T, int h, bool bf16) {
   const size_t parts = round_up256(static_cast<size_t>(ln_bwd_blocks(T)) * h * 2 * sizeof(float));
   // rows too wide for the fused kernel stage the summed gradient here
-  const size_t stage = fused_row_nc(h) ? 0 : static_cast<size_t>(T) * h * (bf16 ? 2 : 4);
+  const size_t stage = fused_bwd_nc(h) ? 0 : static_cast<size_t>(T) * h * (bf16 ? 2 : 4);
   return parts + stage;
 }
 
@@ -896,7 +905,7 @@ hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const voi
                              const void* dres, void* dx, float* dgamma, float* dbeta,
                              bool accumulate, int64_t T, int h, void* ws, hipStream_t s) {
   if (h / 8 > kMaxRowChunks || n < 1 || n > kMaxPartials) return hipErrorInvalidValue;
-  const int nc = fused_row_nc(h);
+  const int nc = fused_bwd_nc(h);
   float* pg = static_cast<float*>(ws);
   const dim3 rg((h + kRedCols - 1) / kRedCols, 2);
   if (nc == 0) {
@@ -935,16 +944,19 @@ hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const voi
     PartialPtrs pp{};
     for (int i = 0; i < n; ++i) pp.p[i] = dys[i];
     const dim3 grid(static_cast<unsigned>(blocks));
-#define MTP_LN_BWD_F(TT, NC)                                                                    \
-  hipLaunchKernelGGL((layernorm_bwd_fused_kernel<TT, NC, (NC >= 8 ? 2 : 1)>), grid, dim3(512), 0, \
-                     s, pp, n, cptr<TT>(x), cptr<TT>(gamma), mean, rstd, cptr<TT>(dres),         \
+#define MTP_LN_BWD_F(TT, NC, SPLIT)                                                             \
+  hipLaunchKernelGGL((layernorm_bwd_fused_kernel<TT, NC, SPLIT>), grid, dim3(512), 0, s, pp, n,   \
+                     cptr<TT>(x), cptr<TT>(gamma), mean, rstd, cptr<TT>(dres),                   \
                      static_cast<TT*>(dx), T, h, pg, pb)
-#define MTP_LN_BWD_F_T(TT)                  \
-  switch (nc) {                             \
-    case 1: MTP_LN_BWD_F(TT, 1); break;     \
-    case 2: MTP_LN_BWD_F(TT, 2); break;     \
-    case 4: MTP_LN_BWD_F(TT, 4); break;     \
-    default: MTP_LN_BWD_F(TT, 8); break;    \
+#define MTP_LN_BWD_F_T(TT)                      \
+  switch (nc) {                                 \
+    case 1: MTP_LN_BWD_F(TT, 1, 1); break;      \
+    case 2: MTP_LN_BWD_F(TT, 2, 1); break;      \
+    case 4: MTP_LN_BWD_F(TT, 4, 1); break;      \
+    case 8: MTP_LN_BWD_F(TT, 8, 2); break;      \
+    case 16: MTP_LN_BWD_F(TT, 16, 4); break;    \
+    case 24: MTP_LN_BWD_F(TT, 24, 8); break;    \
+    default: MTP_LN_BWD_F(TT, 32, 8); break;    \
   }
     if (bf16) { MTP_LN_BWD_F_T(bf16_t) } else { MTP_LN_BWD_F_T(float) }
 #undef MTP_LN_BWD_F_T

@@ -77,7 +77,30 @@ def replicated_params(full: Dict[str, torch.Tensor], device="cuda") -> Dict[str,
     return {k: full[k].to(device).contiguous() for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "bo", "b2")}
 
 
-class TPLayer:
+class _Probed:
+    """Optional timing probe: ``probe`` = {tag: [(start_event, end_event), ...]}
+    for the tags present as keys; events are recorded on the given stream
+    (default: the current one)."""
+
+    probe: Optional[Dict[str, list]] = None
+    device: torch.device
+
+    @contextlib.contextmanager
+    def _timed(self, tag: str, stream=None):
+        pr = self.probe
+        if pr is None or tag not in pr:
+            yield
+            return
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        yield
+        b.record(st)
+        pr[tag].append((a, b))
+
+
+class TPLayer(_Probed):
     """One pre-LN layer, ``ranks`` of its ``cfg.tp`` shards computed here."""
 
     def __init__(self, cfg, full: Dict[str, torch.Tensor], ranks: Optional[Sequence[int]] = None,
@@ -141,23 +164,7 @@ class TPLayer:
         # the side stream gets a workspace of its own
         self.ws_side = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
-        # Optional timing probe: {tag: [(start_event, end_event), ...]} for the
-        # tags present as keys; events are recorded on the current stream.
-        self.probe: Optional[Dict[str, list]] = None
-
-    @contextlib.contextmanager
-    def _timed(self, tag: str, stream=None):
-        pr = self.probe
-        if pr is None or tag not in pr:
-            yield
-            return
-        st = stream if stream is not None else torch.cuda.current_stream(self.device)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(st)
-        yield
-        b.record(st)
-        pr[tag].append((a, b))
+        self.probe = None
 
     # ------------------------------------------------------------ forward
     def forward(self, x: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
@@ -278,7 +285,7 @@ class TPLayer:
         }
 
 
-class VocabHead:
+class VocabHead(_Probed):
     """Vocab-parallel output head with cross-entropy from per-shard stats.
 
     Rank r holds rows [r*V/t, (r+1)*V/t) of the output embedding
@@ -309,28 +316,46 @@ class VocabHead:
         self.M, self.S, self.loss = E(T, d=f32), E(T, d=f32), E(T, d=f32)
         self.loss_mean = E(1, d=f32)
         self.dy = E(T, h)
+        self.probe = None
         del vl_rows
 
     def forward(self, y: torch.Tensor, external_stats: Sequence = ()):
         self.y = y
+        T = self._timed
         for r in self.ranks:
             d = self.descs[r]
-            mtp.mtp_col_linear_fwd(d, mtp.MTP_VOCAB, y, self.emb[r], None, self.logits[r], None)
+            with T("vocab_fwd"):
+                mtp.mtp_col_linear_fwd(d, mtp.MTP_VOCAB, y, self.emb[r], None, self.logits[r],
+                                       None)
             m, s, z = self.stats[r]
-            mtp.mtp_vocab_ce_stats(d, self.logits[r], self.targets, m, s, z)
+            with T("ce_stats"):
+                mtp.mtp_vocab_ce_stats(d, self.logits[r], self.targets, m, s, z)
         stats = [self.stats[r] for r in self.ranks] + list(external_stats)
-        mtp.mtp_vocab_ce_combine(self.d0, [s[0] for s in stats], [s[1] for s in stats],
-                                 [s[2] for s in stats], self.M, self.S, self.loss, self.loss_mean)
+        with T("ce_combine"):
+            mtp.mtp_vocab_ce_combine(self.d0, [s[0] for s in stats], [s[1] for s in stats],
+                                     [s[2] for s in stats], self.M, self.S, self.loss,
+                                     self.loss_mean)
         return self.loss_mean
 
     def backward(self, external_dy: Sequence[torch.Tensor] = ()):
-        T = self.cfg.tokens
+        T = self._timed
+        n_tok = self.cfg.tokens
         for r in self.ranks:
             d = self.descs[r]
-            mtp.mtp_vocab_ce_bwd(d, self.logits[r], self.targets, self.M, self.S,
-                                 1.0 / max(T, 1), self.dlogits[r])
-            mtp.mtp_col_linear_bwd(d, mtp.MTP_VOCAB, self.dlogits[r], self.y, self.emb[r],
-                                   self.dy_part[r], self.demb[r], None, 0, None, 0)
+            with T("ce_bwd"):
+                mtp.mtp_vocab_ce_bwd(d, self.logits[r], self.targets, self.M, self.S,
+                                     1.0 / max(n_tok, 1), self.dlogits[r])
+            with T("vocab_bwd"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_VOCAB, self.dlogits[r], self.y, self.emb[r],
+                                       self.dy_part[r], self.demb[r], None, 0, None, 0)
         parts = [self.dy_part[r] for r in self.ranks] + list(external_dy)
-        mtp.mtp_partial_sum(self.d0, parts, None, None, self.dy)
+        with T("sum_vocab_dy"):
+            mtp.mtp_partial_sum(self.d0, parts, None, None, self.dy)
         return self.dy
+
+    def partials(self):
+        """This object's per-rank stats and dy partials, to be passed as
+        ``external_stats`` / ``external_dy`` to a head that computes the
+        remaining ranks."""
+        return ([tuple(t.clone() for t in self.stats[r]) for r in self.ranks],
+                [self.dy_part[r].clone() for r in self.ranks])

@@ -239,10 +239,13 @@ def test_partial_sum(n):
 
 # --------------------------------------- partial sum fused with LayerNorm
 # dtype, h, T, number of partials.  h = 512 * {1, 2, 4, 8} takes the one-pass
-# kernels; 192 and 12288 take the separate passes (12288 with a staged sum).
+# kernels both ways; h = 512 * {16, 24, 32} the one-pass backward (a row split
+# over 4 or 8 waves) and the separate forward passes; 192 and 256 the
+# separate passes both ways (with a staged sum).
 FUSED_CASES = [("bf16", 512, 77, 2), ("bf16", 4096, 2048, 2), ("f32", 1024, 300, 3),
                ("bf16", 2048, 1, 16), ("bf16", 192, 53, 2), ("f32", 256, 100, 1),
-               ("bf16", 12288, 9, 4)]
+               ("bf16", 12288, 9, 4), ("bf16", 8192, 300, 4), ("f32", 8192, 33, 2),
+               ("bf16", 16384, 17, 2)]
 
 
 @pytest.mark.parametrize("dtype,h,T,n", FUSED_CASES)
