@@ -8,7 +8,7 @@
 // page "Megatron-LM 3D parallelism guide", §2.1 per-head attention, §3.3
 // FlashAttention-2 recomputing P from the saved log-sum-exp).
 //
-// Two passes, no atomics (deterministic):
+// Two block kinds in one launch, no atomics (deterministic):
 //  * dK/dV: a workgroup owns 64 keys of one head (2 key groups of 32, one key
 //    per lane) and walks the query tiles that can see them; the query rows of
 //    every 64-query tile are split between two waves per key group, whose
@@ -146,9 +146,24 @@ __device__ __forceinline__ void window_schedule() {
   __builtin_amdgcn_sched_group_barrier(0x008, W, 0);
 }
 
-__device__ __forceinline__ int balanced_item(int b, int nb) {
-  const int half = (nb + 1) / 2;
-  return b < half ? b : nb - 1 - (b - half);
+// Rank r of the causal block lengths -> the key block and the query block of
+// that rank, longest first.  A key block's queries run to the end of its
+// sequence and a query block's keys start at the start of its sequence, so
+// for sequences of one length (a multiple of 64) rank r is local position r /
+// n_seq from the start (keys) or from the end (queries) of sequence r % n_seq.
+// Otherwise (packed documents, ragged lengths) the ranks follow the block
+// index, which only approximates longest-first.
+__device__ __forceinline__ void ranked_blocks(const BwdParams& p, int r, int& kblk, int& qblk) {
+  const int nbs = p.seq_len / kBT;
+  if (!p.cu && p.seq_len % kBT == 0 && nbs > 0 && p.nblk % nbs == 0) {
+    const int n_seq = p.nblk / nbs;
+    const int li = r / n_seq, sq = r % n_seq;
+    kblk = sq * nbs + li;
+    qblk = sq * nbs + nbs - 1 - li;
+  } else {
+    kblk = r;
+    qblk = p.nblk - 1 - r;
+  }
 }
 
 // ----------------------------------------------------------------- dK / dV
@@ -160,22 +175,11 @@ __device__ __forceinline__ int balanced_item(int b, int nb) {
 // the tile): S = Q K^T [, dP = dO V^T] with one key per lane, P / dS on the
 // vector units, then the transposed-operand MFMAs.
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_dkv_mfma(BwdParams p) {
+__device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int kblk, int head,
+                                          char* sq0, char* sq1, char* so0, char* so1, char* st0,
+                                          char* st1) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int kTile = kBT * D * 2;
-  __shared__ __attribute__((aligned(1024))) char sq0[kTile];
-  __shared__ __attribute__((aligned(1024))) char sq1[kTile];
-  __shared__ __attribute__((aligned(1024))) char so0[kTile];
-  __shared__ __attribute__((aligned(1024))) char so1[kTile];
-  __shared__ __attribute__((aligned(1024))) char st0[2048];  // lse | delta
-  __shared__ __attribute__((aligned(1024))) char st1[2048];
-
   const int T = p.T;
-  const bool want_dk = blockIdx.x & 1;  // role: dK (1) or dV (0)
-  // Key blocks from the first (longest causal query range) down.
-  const int item = balanced_item(blockIdx.x >> 1, gridDim.x >> 1);
-  const int head = item % p.heads;
-  const int kblk = item / p.heads;
   const int k0 = kblk * kBT;
 
   const int lane = threadIdx.x & 63;
@@ -357,18 +361,10 @@ __global__ void __launch_bounds__(256, 2) attn_dkv_mfma(BwdParams p) {
 
 // ---------------------------------------------------------------------- dQ
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_dq_mfma(BwdParams p) {
+__device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head, char* sk0,
+                                         char* sk1, char* sv0, char* sv1) {
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int kTile = kBT * D * 2;
-  __shared__ __attribute__((aligned(1024))) char sk0[kTile];
-  __shared__ __attribute__((aligned(1024))) char sk1[kTile];
-  __shared__ __attribute__((aligned(1024))) char sv0[kTile];
-  __shared__ __attribute__((aligned(1024))) char sv1[kTile];
-
   const int T = p.T;
-  const int item = balanced_item(blockIdx.x, gridDim.x);
-  const int head = item % p.heads;
-  const int qblk = p.nblk - 1 - item / p.heads;
   const int q0 = qblk * kBT;
 
   const int lane = threadIdx.x & 63;
@@ -504,6 +500,34 @@ __global__ void __launch_bounds__(256, 2) attn_dq_mfma(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------- one launch
+// Every (rank, head) has three workgroups: dK and dV of the key block of that
+// rank and dQ of the query block of that rank.  The dQ pass alone cannot
+// fill the chip once its short blocks are done; in one launch its blocks fill
+// the slots the key-major blocks leave.  Blocks are issued rank-major
+// (longest first), and the three roles of one head are 'heads' blocks apart,
+// so with a head count that is a multiple of 8 they land on one XCD and share
+// its L2 for the Q, dO, K and V tiles they all read.
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_bwd_mfma(BwdParams p) {
+  constexpr int kTile = kBT * D * 2;
+  __shared__ __attribute__((aligned(1024))) char t0[kTile];
+  __shared__ __attribute__((aligned(1024))) char t1[kTile];
+  __shared__ __attribute__((aligned(1024))) char t2[kTile];
+  __shared__ __attribute__((aligned(1024))) char t3[kTile];
+  __shared__ __attribute__((aligned(1024))) char st0[2048];  // lse | delta
+  __shared__ __attribute__((aligned(1024))) char st1[2048];
+  const int per_rank = 3 * p.heads;
+  const int r = blockIdx.x / per_rank, j = blockIdx.x % per_rank;
+  const int role = j / p.heads, head = j % p.heads;
+  int kblk, qblk;
+  ranked_blocks(p, r, kblk, qblk);
+  if (role == 1)
+    dq_block<D>(p, qblk, head, t0, t1, t2, t3);
+  else
+    dkv_block<D>(p, role == 0, kblk, head, t0, t1, t2, t3, st0, st1);
+}
+
 }  // namespace
 
 hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
@@ -530,14 +554,11 @@ hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.qkv_bytes = static_cast<uint32_t>(qb);
   p.dctx_bytes = static_cast<uint32_t>(ob);
   p.stat_bytes = static_cast<uint32_t>(sb);
-  const dim3 grid(static_cast<unsigned>(p.nblk * a.heads));
-  const dim3 grid2(static_cast<unsigned>(2 * p.nblk * a.heads));  // dV and dK roles
+  const dim3 grid(static_cast<unsigned>(3 * p.nblk * a.heads));  // dK, dQ and dV roles
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(attn_dkv_mfma<128>, grid2, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(attn_dq_mfma<128>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_mfma<128>, grid, dim3(256), 0, s, p);
   } else if (a.head_dim == 64) {
-    hipLaunchKernelGGL(attn_dkv_mfma<64>, grid2, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(attn_dq_mfma<64>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_mfma<64>, grid, dim3(256), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

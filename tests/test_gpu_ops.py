@@ -165,28 +165,35 @@ def test_layernorm_fwd_bwd(dtype, h, T):
 
 # ------------------------------------------------------------- attention
 ATTN_CASES = [
-    # dtype, heads(local), d, T, cu_seqlens (None = one causal sequence)
-    ("bf16", 2, 128, 77, None),
-    ("bf16", 3, 64, 200, None),
-    ("bf16", 2, 128, 300, [0, 1, 2, 130, 130, 131, 300]),
-    ("bf16", 1, 128, 520, [0, 129, 257, 520]),
-    ("bf16", 2, 64, 1, None),
-    ("f32", 2, 64, 128, None),
-    ("f32", 1, 128, 90, [0, 40, 41, 90]),
+    # dtype, heads(local), d, T, cu_seqlens (None = micro-batch sequences of
+    # T / mb tokens each), mb
+    ("bf16", 2, 128, 77, None, 1),
+    ("bf16", 3, 64, 200, None, 1),
+    ("bf16", 2, 128, 300, [0, 1, 2, 130, 130, 131, 300], 1),
+    ("bf16", 1, 128, 520, [0, 129, 257, 520], 1),
+    ("bf16", 2, 64, 1, None, 1),
+    # sequences of a multiple of 64 tokens (blocks ranked per sequence), and
+    # of a ragged length
+    ("bf16", 2, 128, 384, None, 3),
+    ("bf16", 8, 128, 512, None, 2),
+    ("bf16", 2, 64, 200, None, 2),
+    ("f32", 2, 64, 128, None, 1),
+    ("f32", 1, 128, 90, [0, 40, 41, 90], 1),
 ]
 
 
-@pytest.mark.parametrize("dtype,al,D,T,cu", ATTN_CASES)
-def test_attention_fwd_bwd(dtype, al, D, T, cu):
+@pytest.mark.parametrize("dtype,al,D,T,cu,mb", ATTN_CASES)
+def test_attention_fwd_bwd(dtype, al, D, T, cu, mb):
     require_gpu()
     mtp = _m()
     h = al * D
-    d = desc(mtp, h, al, 0, 1, 0, T, dtype)
+    d = mtp.make_desc(h, al, 0, 1, 0, T // mb, mb,
+                      mtp.MTP_BF16 if dtype == "bf16" else mtp.MTP_F32)
     qkv = rnd((T, 3 * h), dtype, 30)
     dctx = rnd((T, h), dtype, 31)
     cu_t = None
     n = 0
-    cu_list = cu if cu is not None else [0, T]
+    cu_list = cu if cu is not None else list(range(0, T + 1, T // mb))
     if cu is not None:
         cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
         n = len(cu) - 1
@@ -213,7 +220,7 @@ def test_attention_fwd_bwd(dtype, al, D, T, cu):
     check("dq", got[:, :h], dq, tol, rep, floor)
     check("dk", got[:, h:2 * h], dk, tol, rep, floor)
     check("dv", got[:, 2 * h:], dv, tol, rep)
-    log(f"attention {dtype} al={al} D={D} T={T} cu={cu}: " +
+    log(f"attention {dtype} al={al} D={D} T={T} cu={cu} mb={mb}: " +
         ", ".join(f"{k}={v:.1e}" for k, v in rep.items()))
 
 
