@@ -124,6 +124,17 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, char* stag
   }
 }
 
+// Workgroup barrier without the fence of __syncthreads(), whose release
+// semantics make the compiler wait for every outstanding LDS copy
+// (vmcnt(0)) first.  The caller's s_waitcnt has already waited for the
+// copies the next reads need; the empty asm statements keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // MFMA operand (8 consecutive k of one row) from a k-major LDS tile.
 __device__ __forceinline__ bf16x8 frag_k(const char* t, int row, int c) {
   return *reinterpret_cast<const bf16x8*>(t + row * 128 + ((c ^ swz_k(row)) << 4));
@@ -322,7 +333,7 @@ gemm_bf16_kernel(GemmParams p) {
     copy_a(lds_a1, kBK);
     // Only tile 0 is needed now: tile 1's A copies may stay in flight.
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopiesA) : "memory");
-    __syncthreads();
+    lds_barrier();
     load_frags(lds_a0, lds_b0, 0, f0);
     for (int kt = 0; kt < nk; kt += 2) {
       tile(lds_a0, lds_b0, lds_a1, lds_b1, kt);

@@ -233,13 +233,15 @@ class TPLayer(_Probed):
                 with on_side(), T("fc2_bias", side):
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
                                            db2, 0, wss, wsb)
-            with T("fc1_dgrad"):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
-                                       None, 0, ws, wsb)
+            # FC1's weight gradient needs only du: it is queued as soon as
+            # du exists, beside FC1's data gradient.
             fork()
             with on_side(), T("fc1_wgrad", side):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
                                        g["db1"], 0, wss, wsb)
+            with T("fc1_dgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
+                                       None, 0, ws, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
         with T("ln2_bwd"):
             mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
@@ -258,13 +260,14 @@ class TPLayer(_Probed):
             with T("attn_bwd"):
                 mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
                                  self.n_seqs, ws, wsb)
-            with T("qkv_dgrad"):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
-                                       None, None, 0, ws, wsb)
+            # likewise QKV's weight gradient needs only dqkv
             fork()
             with on_side(), T("qkv_wgrad", side):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
                                        g["dwqkv"], g["dbqkv"], 0, wss, wsb)
+            with T("qkv_dgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
+                                       None, None, 0, ws, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
         with T("ln1_bwd"):
             mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
