@@ -41,6 +41,14 @@ namespace {
 
 constexpr int kBK = 64;
 template <int N> struct IntTag { static constexpr int v = N; };
+// f(IntTag<I>{}), ..., f(IntTag<N-1>{}) in order.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntTag<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 constexpr int kGroupM = 8;
 
@@ -196,12 +204,22 @@ gemm_bf16_kernel(GemmParams p) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1, "wave tile too small");
-  // Two stages per operand, as separate objects so the compiler can tell
-  // the stage being filled from the stage being read.
-  __shared__ __attribute__((aligned(1024))) char lds_a0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) char lds_a1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) char lds_b0[BN * 128];
-  __shared__ __attribute__((aligned(1024))) char lds_b1[BN * 128];
+  // NA stages of A and NB of B, each a separate object so the compiler can
+  // tell the stage being filled from the stages being read.  With one
+  // workgroup per CU anyway: three of both where they fit in LDS (128x256,
+  // 256x128), else three of A and two of B where those fit (256x192,
+  // 192x256: A's panels are shared by fewer of the tiles an XCD runs at
+  // once than B's, so more of A's copies miss L2); else two of both.
+  constexpr int kA = BM * 128, kB = BN * 128, kLds = 160 * 1024;
+  constexpr bool kOnePerCu = 2 * (kA + kB) > kLds / 2;
+  constexpr int NB = (kOnePerCu && 3 * (kA + kB) <= kLds) ? 3 : 2;
+  constexpr int NA = (NB == 3 || (kOnePerCu && 3 * kA + 2 * kB < kLds)) ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char lds_a0[kA];
+  __shared__ __attribute__((aligned(1024))) char lds_a1[kA];
+  __shared__ __attribute__((aligned(1024))) char lds_a2[NA > 2 ? kA : 1024];
+  __shared__ __attribute__((aligned(1024))) char lds_b0[kB];
+  __shared__ __attribute__((aligned(1024))) char lds_b1[kB];
+  __shared__ __attribute__((aligned(1024))) char lds_b2[NB > 2 ? kB : 1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -266,30 +284,37 @@ gemm_bf16_kernel(GemmParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto stage_ready = [&]() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
 
-  // Pipeline over k-tiles (stage kt % 2 holds tile kt):
+  // Pipeline over k-tiles (A stage kt % NA and B stage kt % NB hold tile
+  // kt):
   //   steps 1..3 of tile kt, each prefetching the next step's fragments;
-  //   wait for tile kt+1's copies and for every wave to finish reading
-  //   stage kt % 2 (all of tile kt's fragments are in registers by now);
+  //   wait for tile kt+1's copies (copies of later tiles stay in flight)
+  //   and for every wave to finish reading tile kt's stages (all of tile
+  //   kt's fragments are in registers by now);
   //   then step 3 of tile kt, which prefetches step 0 of tile kt+1 from the
-  //   other stage.  The copies that refill the stages are issued one per
-  //   MFMA in two k-steps (A after the barrier, B in the next tile's first
-  //   step) rather than as a burst after the barrier, where the copies of
-  //   all waves queued behind each other and the last waves reached the
-  //   next barrier late.
+  //   next stages.
+  // The copies that refill the stages are issued one per MFMA in two
+  // k-steps, the first step of a tile (slot 1) and the step after its
+  // barrier (slot 0), rather than as a burst after the barrier, where the
+  // copies of all waves queued behind each other and the last waves reached
+  // the next barrier late.  With NA = NB = N: B of tile kt+N-1 in slot 1
+  // (into the stage tile kt-1 freed), A of tile kt+N in slot 0 (into tile
+  // kt's).  With NA = 3, NB = 2: A of tile kt+2 in slot 1 and B of tile kt+2
+  // in slot 0, so that at each barrier only the latest A copies are still
+  // in flight and the load counter can be waited down to them.
   // The barrier thus sits before the last k-step, whose MFMAs cover the
-  // first fragment reads of the next tile.  The tile count is rounded up to
-  // even so that the stages alternate in a branch-free loop: tiles past K
-  // (and copies issued for them) are all-zero loads that add nothing.
-  const int nk = ((p.K + kBK - 1) / kBK + 1) & ~1;
+  // first fragment reads of the next tile.  It is a bare s_barrier: the
+  // fence of __syncthreads() would make the compiler wait for every
+  // outstanding copy, the deeper stages' included.  Tiles past K (and
+  // copies issued for them) are all-zero loads that add nothing.
+  const int nk = (p.K + kBK - 1) / kBK;
   Frags f0, f1;
   // One k-step (MFMAs on f, fragment reads of step kk into nf) with nc
   // operand copies issued between its MFMAs, one per MFMA.
   constexpr int kCopiesA = BM / 8 / NW, kCopiesB = BN / 8 / NW;
+  constexpr bool kSym = NA == NB;
+  // copies that may still be in flight at a barrier
+  constexpr int kInFlight = kSym ? (NA - 2) * (kCopiesA + kCopiesB) : kCopiesA;
   auto step_c = [&](const Frags& f, const char* ta, const char* tb, int kk, Frags& nf,
                     auto&& copies, auto nc_tag) {
     constexpr int nc = decltype(nc_tag)::v;
@@ -315,30 +340,59 @@ gemm_bf16_kernel(GemmParams p) {
   auto copy_b = [&](char* sb, int k0) {
     issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
   };
-  // Tile kt: its first k-step also copies B of tile kt+1 into the other
-  // stage (free since the previous barrier); after the barrier, the last
-  // k-step copies A of tile kt+2 into this tile's stage.  Both land before
-  // the barrier of tile kt+1, which waits for them.
-  auto tile = [&](char* ca, char* cb, char* na, char* nb, int kt) {
-    step_c(f0, ca, cb, 1, f1, [&] { copy_b(nb, (kt + 1) * kBK); }, IntTag<kCopiesB>{});
+  // Stage objects by compile-time index.
+  auto sa = [&](auto i) -> char* {
+    constexpr int v = decltype(i)::v % NA;
+    return v == 0 ? lds_a0 : v == 1 ? lds_a1 : lds_a2;
+  };
+  auto sb = [&](auto i) -> char* {
+    constexpr int v = decltype(i)::v % NB;
+    return v == 0 ? lds_b0 : v == 1 ? lds_b1 : lds_b2;
+  };
+  // Tile kt, with J = kt mod the stage period known at compile time.
+  auto tile = [&](auto j, int kt) {
+    constexpr int J = decltype(j)::v;
+    char* const ca = sa(IntTag<J>{});
+    char* const cb = sb(IntTag<J>{});
+    char* const na = sa(IntTag<J + 1>{});
+    char* const nb = sb(IntTag<J + 1>{});
+    if constexpr (kSym) {
+      step_c(f0, ca, cb, 1, f1, [&] { copy_b(sb(IntTag<J + NB - 1>{}), (kt + NB - 1) * kBK); },
+             IntTag<kCopiesB>{});
+    } else {
+      step_c(f0, ca, cb, 1, f1, [&] { copy_a(sa(IntTag<J + 2>{}), (kt + 2) * kBK); },
+             IntTag<kCopiesA>{});
+    }
     step(f1, true, ca, cb, 2, f0);
     step(f0, true, ca, cb, 3, f1);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    step_c(f1, na, nb, 0, f0, [&] { copy_a(ca, (kt + 2) * kBK); }, IntTag<kCopiesA>{});
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(kInFlight) : "memory");
+    lds_barrier();
+    if constexpr (kSym) {
+      step_c(f1, na, nb, 0, f0, [&] { copy_a(ca, (kt + NA) * kBK); }, IntTag<kCopiesA>{});
+    } else {
+      step_c(f1, na, nb, 0, f0, [&] { copy_b(cb, (kt + NB) * kBK); }, IntTag<kCopiesB>{});
+    }
   };
   if (nk > 0) {
+    // Tiles 0 .. N-2 whole and, with NA = NB = N, A of tile N-1 (its B
+    // follows in tile 0); with NA = 3, NB = 2, tiles 0 and 1.
     copy_a(lds_a0, 0);
     copy_b(lds_b0, 0);
     copy_a(lds_a1, kBK);
-    // Only tile 0 is needed now: tile 1's A copies may stay in flight.
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopiesA) : "memory");
+    if constexpr (!kSym || NA > 2) copy_b(lds_b1, kBK);
+    if constexpr (kSym && NA > 2) copy_a(lds_a2, 2 * kBK);
+    // Only tile 0 is needed now: the later tiles' copies may stay in flight.
+    constexpr int kFirstWait = kSym ? kInFlight + kCopiesA : kCopiesA + kCopiesB;
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kFirstWait) : "memory");
     lds_barrier();
     load_frags(lds_a0, lds_b0, 0, f0);
-    for (int kt = 0; kt < nk; kt += 2) {
-      tile(lds_a0, lds_b0, lds_a1, lds_b1, kt);
-      tile(lds_a1, lds_b1, lds_a0, lds_b0, kt + 1);
-    }
+    // The loop is unrolled over one period of the stage rotation, each tile
+    // behind a (uniform) test against the tile count.
+    constexpr int kPeriod = NA * NB / (NA == NB ? NA : 1);
+    for (int kt = 0; kt < nk; kt += kPeriod)
+      static_for<0, kPeriod>([&](auto j) {
+        if (kt + decltype(j)::v < nk) tile(j, kt + decltype(j)::v);
+      });
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
 
@@ -401,12 +455,12 @@ hipError_t launch_bf16(const GemmParams& p0, hipStream_t s) {
 // Tile shapes compiled in.
 enum TileShape : int {
   kTile256x256 = 0,  // 8 waves (2x4), 128 KB LDS
-  kTile256x128 = 1,  // 8 waves (4x2), 96 KB LDS
-  kTile128x256 = 2,  // 8 waves (2x4), 96 KB LDS
+  kTile256x128 = 1,  // 8 waves (4x2), three stages, 144 KB LDS
+  kTile128x256 = 2,  // 8 waves (2x4), three stages, 144 KB LDS
   kTile128x128 = 3,  // 4 waves (2x2), 64 KB LDS
   kTile256x256w4 = 4,  // 4 waves (2x2), one per SIMD, 128 KB LDS
-  kTile256x192 = 5,  // 8 waves (4x2), 112 KB LDS
-  kTile192x256 = 6,  // 8 waves (2x4), 112 KB LDS
+  kTile256x192 = 5,  // 8 waves (4x2), three A and two B stages, 144 KB LDS
+  kTile192x256 = 6,  // 8 waves (2x4), three A and two B stages, 136 KB LDS
   kNumTiles = 7
 };
 
@@ -416,13 +470,15 @@ int pick_tile(int M, int N) {
 #endif
   // Cost = rounds of tiles over the 256 CUs x tile area / relative
   // efficiency (measured on the 7B shard shapes).  128x128 tiles run two
-  // per CU, or one per CU (at lower efficiency) when they fit in one round.
+  // per CU, or one per CU when they fit in one round; one such round (two
+  // stages, four waves) measured slower than a round of three-stage
+  // 128x256 tiles of twice the area (2048 x 2048 x 4096: 46.7 vs 44.0 us).
   constexpr int kCUs = 256;
   const int bm[kNumTiles] = {256, 256, 128, 128, 256, 256, 192};
   const int bn[kNumTiles] = {256, 128, 256, 128, 256, 192, 256};
   const int per_cu[kNumTiles] = {1, 1, 1, 2, 1, 1, 1};
   const double eff[kNumTiles] = {1.0, 0.9, 0.92, 0.87, 0.0, 0.96, 0.96};
-  constexpr double kEffAlone128 = 0.78;
+  constexpr double kEffAlone128 = 0.45;
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
