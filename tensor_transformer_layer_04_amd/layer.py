@@ -260,14 +260,13 @@ class TPLayer(_Probed):
             with T("attn_bwd"):
                 mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
                                  self.n_seqs, ws, wsb)
-            # likewise QKV's weight gradient needs only dqkv
+            with T("qkv_dgrad"):
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
+                                       None, None, 0, ws, wsb)
             fork()
             with on_side(), T("qkv_wgrad", side):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
                                        g["dwqkv"], g["dbqkv"], 0, wss, wsb)
-            with T("qkv_dgrad"):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
-                                       None, None, 0, ws, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
         with T("ln1_bwd"):
             mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
