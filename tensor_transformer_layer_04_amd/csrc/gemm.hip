@@ -105,7 +105,7 @@ __device__ __forceinline__ int swz_m(int chunk, int k) {
 // instruction (64 lanes x 16 B, lane-contiguous); wave w issues
 // instructions w*kPer .. w*kPer+kPer-1.
 template <int R, int NW, bool KMAJ>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, char* stage, int wave,
+__device__ __forceinline__ void issue_tile(const u32x4& rs, char* stage, int wave,
                                            int lane, int row0, int rmax, int k0, int K,
                                            uint32_t ld_bytes) {
   constexpr int kInstr = R / 8;
@@ -128,7 +128,7 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, char* stag
       const int gk = k0 + kr, gm = row0 + lc * 8;
       off = (gk < K && gm < rmax) ? static_cast<uint32_t>(gk) * ld_bytes + gm * 2 : kOOB;
     }
-    copy16_to_lds(rs, stage + j * 1024, off);
+    copy16_raw(rs, lds_addr(stage) + j * 1024, off);
   }
 }
 
@@ -197,6 +197,40 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
   }
 }
 
+// Epilogue of one 32x32 accumulator block whose top-left element is C(mb, nb):
+// the wave writes the block (lane: row lane%32, columns 8g + 4(lane/32) ..
+// +3 of accumulator elements 4g..4g+3) row-major into its private LDS
+// region `stage` (36-float pitch), then reads it back as row segments, so
+// every global store (and every load of C or of the GeLU pre-activation)
+// covers 8 rows x 32 contiguous columns.
+template <int EPI>
+__device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, const f32x16& a,
+                                          int mb, int nb, int lane) {
+  constexpr int kPitch = 36;
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int sr = lane >> 3, sc = (lane & 7) * 4;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(stage + lrow * kPitch + 8 * g + 4 * lk) =
+        f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  float v[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(stage + (8 * r + sr) * kPitch + sc);
+    v[r][0] = t[0]; v[r][1] = t[1]; v[r][2] = t[2]; v[r][3] = t[3];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  const int n = nb + sc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = mb + 8 * r + sr;
+    if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
 __global__ void __launch_bounds__(WGM * WGN * 64, (WGM * WGN + 3) / 4)
 gemm_bf16_kernel(GemmParams p) {
@@ -228,8 +262,8 @@ gemm_bf16_kernel(GemmParams p) {
   tile_coords(p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
+  const u32x4 ra = rsrc_words(p.A, p.a_bytes);
+  const u32x4 rb = rsrc_words(p.B, p.b_bytes);
   const uint32_t lda_b = static_cast<uint32_t>(p.lda) * 2, ldb_b = static_cast<uint32_t>(p.ldb) * 2;
 
   f32x16 acc[FM][FN];
@@ -396,11 +430,7 @@ gemm_bf16_kernel(GemmParams p) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
 
-  // Epilogue, staged through LDS one 32x32 block at a time: the wave writes
-  // its accumulators (lane: row lrow, columns 8g + 4lk .. +3 of acc element
-  // 4g..4g+3) row-major into a private LDS region, then reads them back as
-  // row segments, so every global store (and every load of C or of the
-  // GeLU pre-activation) covers 8 rows x 32 contiguous columns.
+  // Epilogue, staged through LDS one 32x32 block at a time (epi_block).
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();  // every wave is done with the stage buffers
   constexpr int kPitch = 36;  // floats per staged row: 32 + 4 (bank spread)
@@ -411,34 +441,11 @@ gemm_bf16_kernel(GemmParams p) {
                    : (wave / kPerBuf) == 1 ? lds_a1
                    : (wave / kPerBuf) == 2 ? lds_b0 : lds_b1;
   float* stage = reinterpret_cast<float*>(base + (wave % kPerBuf) * kRegion);
-  const int sr = lane >> 3, sc = (lane & 7) * 4;  // read-back row offset / column
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(stage + lrow * kPitch + 8 * g + 4 * lk) =
-            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                  acc[i][j][4 * g + 3]};
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_wave_barrier();
-      float v[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(stage + (8 * r + sr) * kPitch + sc);
-        v[r][0] = t[0]; v[r][1] = t[1]; v[r][2] = t[2]; v[r][3] = t[3];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_wave_barrier();
-      const int n = n0 + wn * WTN + j * 32 + sc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WTM + i * 32 + 8 * r + sr;
-        if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
-      }
-    }
-  }
+    for (int j = 0; j < FN; ++j)
+      epi_block<EPI>(p, stage, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>

@@ -30,6 +30,39 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void* d
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(dst), 16, off, 0, 0, 0);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The resource of make_rsrc as four scalar words (base, base bits 32..47
+// with stride 0, num_records, word 3), for copies issued by copy16_raw.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = static_cast<uint32_t>(a);
+  r[1] = static_cast<uint32_t>(a >> 32) & 0xffffu;
+  r[2] = bytes;
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(to_lds(p)));
+}
+
+// The copy of copy16_to_lds (lane l writes 16 bytes at LDS address
+// dst + 16 l), issued from inline assembly so that the compiler's wait-count
+// insertion does not track it: the caller waits for it with an explicit
+// s_waitcnt vmcnt.  One wait state separates the M0 write from the load.
+// The statement is volatile but clobbers no memory: it keeps its order
+// relative to other volatile statements (the explicit waits and barriers,
+// which clobber memory), while LDS reads of other stages may be scheduled
+// around it.  The caller must not read a stage between issuing a copy into
+// it and the wait + barrier that make the copy visible.
+__device__ __forceinline__ void copy16_raw(const u32x4& rs, uint32_t dst, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(dst), "v"(off), "s"(rs) : "m0");
+}
+
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element j
 // (j = 0..3) from the 8-byte word addressed by lane 4j + i/4, at sub-element
 // i % 4.  With lane 4j + q pointing at row r0 + j, columns c0 + 4q .. +3 of
