@@ -46,7 +46,8 @@ FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
 # Every call of one step, in issue order (the per-call times of the probed steps).
 CALL_TAGS = ("ln1", "qkv_fwd", "attn_fwd", "proj_fwd", "sum_proj_ln2", "fc1_fwd", "fc2_fwd",
              "sum_fc2", "fc2_dgrad", "fc2_wgrad", "fc2_bias", "fc1_dgrad", "fc1_wgrad", "ln2_bwd",
-             "proj_dgrad", "proj_wgrad", "attn_bwd", "qkv_dgrad", "qkv_wgrad", "ln1_bwd")
+             "proj_dgrad", "proj_wgrad", "proj_bias", "attn_bwd", "qkv_dgrad", "qkv_wgrad",
+             "ln1_bwd")
 HEAD_TAGS = ("vocab_fwd", "ce_stats", "ce_combine", "ce_bwd", "vocab_bwd", "sum_vocab_dy")
 PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
@@ -248,9 +249,14 @@ def main(argv=None) -> int:
             full.backward(dy)
         parts = full.partials()
         ext = {k: [v[i] for i, r in enumerate(full.ranks) if r != args.rank] for k, v in parts.items()}
-        del full
         torch.cuda.synchronize()
     L = TPLayer(cfg, data, ranks=[args.rank], device=dev, cu_seqlens=data["cu_seqlens"])
+    if cfg.tp > 1:
+        if L.sp:
+            # The other ranks' row blocks of the token-sharded activations and
+            # gradients (what the all-gathers would deliver) stay resident.
+            L.adopt_rows(full)
+        del full
     H = VocabHead(cfg, data, ranks=[args.rank], device=dev) if cfg.vocab else None
 
     def step():
@@ -355,10 +361,12 @@ def main(argv=None) -> int:
         "data": "synthetic: seeded x, dy ~ N(0,1), weights ~ N(0,0.02), biases 0, LN gamma 1",
         "config": {
             "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard"
+                        + (" with sequence parallelism" if L.sp else "")
                         + (" + vocab-parallel CE head" if cfg.vocab else "") + " fwd+bwd",
             "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn, "tp": cfg.tp,
             "rank": args.rank, "seq_len": cfg.seq_len, "micro_batch": cfg.micro_batch,
-            "tokens": cfg.tokens, "global_batch": cfg.micro_batch, "parallelism": f"tp{cfg.tp}-shard",
+            "tokens": cfg.tokens, "global_batch": cfg.micro_batch,
+            "parallelism": f"tp{cfg.tp}" + ("-sp" if L.sp else "") + "-shard",
         },
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),

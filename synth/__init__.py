@@ -61,6 +61,7 @@ class LayerConfig:
     eps: float = 1e-5
     seed: int = 0
     affine_random: bool = False  # draw non-trivial biases / LayerNorm affine
+    sequence_parallel: bool = False  # per-token work on T/tp row blocks per rank
     description: str = ""
 
     @property
@@ -93,6 +94,10 @@ CONFIGS: Dict[str, LayerConfig] = {
     "bench_tp4_vocab": LayerConfig(
         "bench_tp4_vocab", hidden=8192, heads=64, ffn=32768, tp=4, seq_len=4096, dtype="bf16",
         vocab=131072, description="benchmark-shaped layer + vocab-parallel CE head, TP=4, bf16"),
+    "7b_tp2_sp": LayerConfig(
+        "7b_tp2_sp", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        sequence_parallel=True,
+        description="7B-style layer, one TP=2 rank shard with sequence parallelism, bf16"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -121,6 +126,12 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_f32_tp4": LayerConfig(
         "small_f32_tp4", hidden=256, heads=4, ffn=1024, tp=4, seq_len=77, dtype="f32",
         affine_random=True),
+    "small_bf16_tp2_sp": LayerConfig(
+        "small_bf16_tp2_sp", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        affine_random=True, sequence_parallel=True),
+    "small_f32_tp4_sp": LayerConfig(
+        "small_f32_tp4_sp", hidden=256, heads=4, ffn=1024, tp=4, seq_len=80, dtype="f32",
+        affine_random=True, sequence_parallel=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

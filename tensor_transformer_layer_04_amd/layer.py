@@ -22,6 +22,20 @@ sum of the ranks' partials (the input reached every rank).
 Ranks that are not computed in this process can contribute their partials
 through ``external`` buffers (e.g. precomputed by an earlier run), which is
 how one rank's shard is timed with the full t-way sums charged to it.
+
+Sequence parallelism (``cfg.sequence_parallel``; page "Megatron-LM: NVIDIA
+large-model training framework", section "Sequence parallelism"): the
+per-token work (LayerNorm, residual, bias, dropout) is split over the tokens
+instead of replicated, rank r owning rows [r T/t, (r+1) T/t).  The sum of
+the row-parallel partials becomes a reduce-scatter (rank r sums only its
+rows), followed by an all-gather of the LayerNorm output before the next
+column-parallel GEMM; in backward the column-dgrad partials are
+reduce-scattered into the LayerNorm backward of each rank's rows and the
+result all-gathered.  On one device the ranks' row blocks live in one
+[T, h] buffer, so the all-gather moves nothing: a rank writes its rows and
+the GEMMs read the whole buffer.  LayerNorm weight gradients and the
+row-parallel bias gradients are each rank's column sums over its rows,
+added over the computed ranks in rank order.
 """
 from __future__ import annotations
 
@@ -123,6 +137,20 @@ class TPLayer(_Probed):
         # ``overlap`` they run on a second stream (default priority) next to
         # the data gradients, joined back before backward() returns.
         self.side = torch.cuda.Stream(device=self.device) if overlap else None
+        self.sp = bool(getattr(cfg, "sequence_parallel", False)) and cfg.tp > 1
+        if self.sp:
+            # Each rank's row block must start on a 16-byte boundary of the
+            # fp32 per-token statistics (the C ABI takes 16-byte aligned
+            # pointers): T / tp a multiple of 4.
+            if self.T % (4 * cfg.tp):
+                raise ValueError(f"sequence parallelism needs T ({self.T}) divisible by "
+                                 f"4 * tp ({4 * cfg.tp})")
+            tr = self.T // cfg.tp
+            self.rows = {r: slice(r * tr, (r + 1) * tr) for r in range(cfg.tp)}
+            self.rdesc = {r: mtp.make_desc(cfg.hidden, cfg.heads, cfg.ffn, cfg.tp, r, tr, 1,
+                                           mtp.MTP_F32 if cfg.dtype == "f32" else mtp.MTP_BF16,
+                                           vocab=cfg.vocab, ln_eps=cfg.eps)
+                          for r in range(cfg.tp)}
         self._alloc()
 
     # ------------------------------------------------------------ buffers
@@ -166,6 +194,13 @@ class TPLayer(_Probed):
         self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
         self.probe = None
 
+    def adopt_rows(self, other: "TPLayer"):
+        """Sequence parallelism: share ``other``'s token-sharded buffers, whose
+        row blocks of the ranks not computed here stay resident (the
+        all-gathered activations and gradients of those ranks)."""
+        for k in ("ln1", "mu1", "rs1", "y1", "ln2", "mu2", "rs2", "y", "dy1", "dx"):
+            setattr(self, k, getattr(other, k))
+
     # ------------------------------------------------------------ forward
     def forward(self, x: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
         """Forward of the computed ranks; returns y (valid when every rank's
@@ -174,8 +209,15 @@ class TPLayer(_Probed):
         d0, rep = self.d0, self.rep
         self.x = x
         T = self._timed
-        with T("ln1"):
-            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln1"):
+                    mtp.mtp_layernorm(self.rdesc[r], x[s], rep["ln1_g"], rep["ln1_b"],
+                                      self.ln1[s], self.mu1[s], self.rs1[s])
+        else:
+            with T("ln1"):
+                mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
             with T("qkv_fwd"):
@@ -186,9 +228,17 @@ class TPLayer(_Probed):
             with T("proj_fwd"):
                 mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
-        with T("sum_proj_ln2"):
-            mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
-                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("sum_proj_ln2"):
+                    mtp.mtp_partial_sum_layernorm(self.rdesc[r], [q[s] for q in parts], rep["bo"],
+                                                  x[s], self.y1[s], rep["ln2_g"], rep["ln2_b"],
+                                                  self.ln2[s], self.mu2[s], self.rs2[s])
+        else:
+            with T("sum_proj_ln2"):
+                mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
+                                              rep["ln2_b"], self.ln2, self.mu2, self.rs2)
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
             with T("fc1_fwd"):
@@ -196,8 +246,15 @@ class TPLayer(_Probed):
             with T("fc2_fwd"):
                 mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, a["g"], w["w2"], a["q"])
         parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
-        with T("sum_fc2"):
-            mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("sum_fc2"):
+                    mtp.mtp_partial_sum(self.rdesc[r], [q[s] for q in parts], rep["b2"],
+                                        self.y1[s], self.y[s])
+        else:
+            with T("sum_fc2"):
+                mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
         return self.y
 
     # ----------------------------------------------------------- backward
@@ -222,7 +279,7 @@ class TPLayer(_Probed):
         fork()
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
-            db2 = self.rgrads["db2"] if r == self.owns_bias else None
+            db2 = self.rgrads["db2"] if (r == self.owns_bias and not self.sp) else None
             with T("fc2_dgrad"):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], None,
                                        None, 0, ws, wsb)
@@ -233,6 +290,13 @@ class TPLayer(_Probed):
                 with on_side(), T("fc2_bias", side):
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
                                            db2, 0, wss, wsb)
+            if self.sp:
+                # row-parallel bias: this rank's column sums of dy over its rows
+                s = self.rows[r]
+                with on_side(), T("fc2_bias", side):
+                    mtp.mtp_row_linear_bwd(self.rdesc[r], mtp.MTP_FC2, dy[s], a["g"][s], w["w2"],
+                                           None, None, None, self.rgrads["db2"],
+                                           int(r != self.ranks[0]), wss, wsb)
             # FC1's weight gradient needs only du: it is queued as soon as
             # du exists, beside FC1's data gradient.
             fork()
@@ -243,20 +307,36 @@ class TPLayer(_Probed):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
                                        None, 0, ws, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
-        with T("ln2_bwd"):
-            mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
-                                      self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0, ws,
-                                      wsb)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln2_bwd"):
+                    mtp.mtp_layernorm_bwd_sum(self.rdesc[r], [q[s] for q in parts], self.y1[s],
+                                              rep["ln2_g"], self.mu2[s], self.rs2[s], dy[s],
+                                              self.dy1[s], self.rgrads["dln2_g"],
+                                              self.rgrads["dln2_b"], int(r != self.ranks[0]), ws,
+                                              wsb)
+        else:
+            with T("ln2_bwd"):
+                mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
+                                          self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0,
+                                          ws, wsb)
         fork()
         for r in self.ranks:
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
-            dbo = self.rgrads["dbo"] if r == self.owns_bias else None
+            dbo = self.rgrads["dbo"] if (r == self.owns_bias and not self.sp) else None
             with T("proj_dgrad"):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
                                        a["dctx"], None, None, 0, ws, wsb)
             with on_side(), T("proj_wgrad", side):
                 mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None, None,
                                        g["dwo"], dbo, 0, wss, wsb)
+            if self.sp:
+                s = self.rows[r]
+                with on_side(), T("proj_bias", side):
+                    mtp.mtp_row_linear_bwd(self.rdesc[r], mtp.MTP_PROJ, self.dy1[s], a["ctx"][s],
+                                           w["wo"], None, None, None, self.rgrads["dbo"],
+                                           int(r != self.ranks[0]), wss, wsb)
             with T("attn_bwd"):
                 mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
                                  self.n_seqs, ws, wsb)
@@ -268,10 +348,20 @@ class TPLayer(_Probed):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
                                        g["dwqkv"], g["dbqkv"], 0, wss, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
-        with T("ln1_bwd"):
-            mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
-                                      self.dy1, self.dx, self.rgrads["dln1_g"],
-                                      self.rgrads["dln1_b"], 0, ws, wsb)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln1_bwd"):
+                    mtp.mtp_layernorm_bwd_sum(self.rdesc[r], [q[s] for q in parts], self.x[s],
+                                              rep["ln1_g"], self.mu1[s], self.rs1[s], self.dy1[s],
+                                              self.dx[s], self.rgrads["dln1_g"],
+                                              self.rgrads["dln1_b"], int(r != self.ranks[0]), ws,
+                                              wsb)
+        else:
+            with T("ln1_bwd"):
+                mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                                          self.dy1, self.dx, self.rgrads["dln1_g"],
+                                          self.rgrads["dln1_b"], 0, ws, wsb)
         if side is not None:
             main.wait_stream(side)
         return self.dx

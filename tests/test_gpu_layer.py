@@ -24,7 +24,7 @@ from gpu_common import (TOL, check, compare_layer, fmt_report, log, oracle_layer
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_tp2", "small_f32_tp4", "small_bf16_tp2", "small_bf16_d64_tp4", "small_bf16_mb2",
-         "small_varlen_tp1", "one_token_bf16"]
+         "small_varlen_tp1", "one_token_bf16", "small_bf16_tp2_sp", "small_f32_tp4_sp"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -174,3 +174,53 @@ def test_sum_of_partials_equals_unsharded():
     c, _ = oracle_layer(base, synth.generate(base))
     for y in outs:
         assert oracle.rel_frobenius(y, c["y"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["small_bf16_tp2_sp", "small_f32_tp4_sp"])
+def test_sequence_parallel_matches_replicated(name):
+    """Sequence parallelism only moves the per-token work onto row blocks:
+    every row-wise output is bit-identical to the replicated layer's, and
+    the LayerNorm and row-parallel bias gradients (column sums now added
+    rank by rank) agree to fp32 rounding."""
+    require_gpu()
+    cfg = synth.get_config(name)
+    data = synth.generate(cfg)
+    L_sp = run_gpu_layer(cfg, data)
+    L_rep = run_gpu_layer(cfg.replace(sequence_parallel=False), data)
+    assert L_sp.sp and not L_rep.sp
+    for k in ("ln1", "mu1", "rs1", "y1", "ln2", "mu2", "rs2", "y", "dy1", "dx"):
+        a, b = getattr(L_sp, k), getattr(L_rep, k)
+        assert torch.equal(a, b), f"{name}: {k} differs"
+    for r in L_sp.ranks:
+        for k in L_sp.a[r]:
+            assert torch.equal(L_sp.a[r][k], L_rep.a[r][k]), f"{name}: r{r}.{k} differs"
+    for k in L_sp.rgrads:
+        a, b = L_sp.rgrads[k].double().cpu(), L_rep.rgrads[k].double().cpu()
+        err = float((a - b).norm() / max(float(b.norm()), 1e-30))
+        log(f"  {k}: rel diff {err:.2e}")
+        assert err <= 1e-5, f"{name}: {k} rel diff {err}"
+
+
+def test_sequence_parallel_one_rank_with_resident_rows():
+    """The timed shard of the sequence-parallel workload: rank 0 alone, the
+    other rank's partials and row blocks resident from a full run, gives
+    rank 0's rows of every row-wise output bit-identically."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd.layer import TPLayer
+    cfg = synth.get_config("small_bf16_tp2_sp")
+    data = synth.generate(cfg)
+    full = run_gpu_layer(cfg, data)
+    ref = {k: getattr(full, k).clone() for k in ("y1", "y", "dy1", "dx", "ln1", "ln2")}
+    parts = full.partials()
+    ext = {k: [v[i] for i, r in enumerate(full.ranks) if r != 0] for k, v in parts.items()}
+    L = TPLayer(cfg, data, ranks=[0], device="cuda", cu_seqlens=data["cu_seqlens"])
+    L.adopt_rows(full)
+    # poison rank 0's rows of the shared buffers: the shard must rewrite them
+    rows = L.rows[0]
+    for k in ("ln1", "y1", "ln2", "y", "dy1", "dx"):
+        getattr(L, k)[rows] = float("nan")
+    L.forward(data["x"].cuda().contiguous(), ext)
+    L.backward(data["dy"].cuda().contiguous(), ext)
+    torch.cuda.synchronize()
+    for k, v in ref.items():
+        assert torch.equal(getattr(L, k)[rows], v[rows]), f"rank-0 rows of {k} differ"
