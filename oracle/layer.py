@@ -19,6 +19,12 @@ So the oracle is the plain definition of the unsharded pre-LN layer:
     ln2 = LN(y1)      u = ln2 W1^T + b1     g = GeLU_tanh(u)
     y   = y1 + g W2^T + b2
 
+or, in the SwiGLU variant without linear biases on the FFN input (present
+when the parameters hold an up projection ``w3``; page "Megatron-LM 3D
+parallelism guide", §3.3 launch flags ``--swiglu --disable-bias-linear``):
+
+    u = ln2 W1^T (gate)    u3 = ln2 W3^T (up)    g = SiLU(u) * u3
+
 and its backward by the chain rule.  The rank view (which slice of each
 tensor a given rank computes) is in ``rank_view``.
 
@@ -43,6 +49,7 @@ import numpy as np
 
 __all__ = [
     "to64", "linear", "layernorm", "layernorm_backward", "gelu_tanh", "gelu_tanh_grad",
+    "silu", "silu_grad",
     "doc_starts", "attention_probabilities", "attention_forward", "attention_backward",
     "layer_forward", "layer_backward", "vocab_ce_forward", "vocab_ce_backward",
     "rank_view", "rel_frobenius",
@@ -130,6 +137,18 @@ def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
     z = GELU_C * (u + GELU_A * u ** 3)
     th = np.tanh(z)
     return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th ** 2) * GELU_C * (1.0 + 3.0 * GELU_A * u ** 2)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU (swish): z * sigmoid(z), the sigmoid written as (1 + tanh(z/2)) / 2
+    so that it stays finite for every z."""
+    return z * 0.5 * (1.0 + np.tanh(0.5 * z))
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of ``silu``: s + z s (1 - s) with s = sigmoid(z)."""
+    s = 0.5 * (1.0 + np.tanh(0.5 * z))
+    return s * (1.0 + z * (1.0 - s))
 
 
 # ------------------------------------------------------------------ attention
@@ -254,8 +273,13 @@ def layer_forward(params: Dict, x, heads: int, eps: float, starts) -> Dict[str, 
     c["ctx"], c["lse"] = attention_forward(q, k, v, heads, starts)
     c["y1"] = x + linear(c["ctx"], p["wo"], p["bo"])
     c["ln2"], c["mu2"], c["rstd2"] = layernorm(c["y1"], p["ln2_g"], p["ln2_b"], eps)
-    c["u"] = linear(c["ln2"], p["w1"], p["b1"])
-    c["g"] = gelu_tanh(c["u"])
+    if "w3" in p:
+        c["u"] = linear(c["ln2"], p["w1"])
+        c["u3"] = linear(c["ln2"], p["w3"])
+        c["g"] = silu(c["u"]) * c["u3"]
+    else:
+        c["u"] = linear(c["ln2"], p["w1"], p["b1"])
+        c["g"] = gelu_tanh(c["u"])
     c["y"] = c["y1"] + linear(c["g"], p["w2"], p["b2"])
     return c
 
@@ -272,11 +296,19 @@ def layer_backward(params: Dict, cache: Dict[str, np.ndarray], dy, heads: int,
     gr["dw2"] = dy.T @ c["g"]
     gr["db2"] = dy.sum(axis=0)
     dg = dy @ p["w2"]
-    du = dg * gelu_tanh_grad(c["u"])
-    gr["du"] = du
-    gr["dw1"] = du.T @ c["ln2"]
-    gr["db1"] = du.sum(axis=0)
-    dln2 = du @ p["w1"]
+    if "w3" in p:
+        du = dg * c["u3"] * silu_grad(c["u"])
+        du3 = dg * silu(c["u"])
+        gr["du"], gr["du3"] = du, du3
+        gr["dw1"] = du.T @ c["ln2"]
+        gr["dw3"] = du3.T @ c["ln2"]
+        dln2 = du @ p["w1"] + du3 @ p["w3"]
+    else:
+        du = dg * gelu_tanh_grad(c["u"])
+        gr["du"] = du
+        gr["dw1"] = du.T @ c["ln2"]
+        gr["db1"] = du.sum(axis=0)
+        dln2 = du @ p["w1"]
     gr["dln2"] = dln2
     dy1_ln, gr["dln2_g"], gr["dln2_b"] = layernorm_backward(dln2, c["y1"], p["ln2_g"],
                                                             c["mu2"], c["rstd2"])
@@ -363,6 +395,8 @@ def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]]
     v["lse"] = fwd["lse"][r * (heads // tp):(r + 1) * (heads // tp)]
     v["proj_partial"] = fwd["ctx"][:, hc] @ p["wo"][:, hc].T
     v["u"] = fwd["u"][:, fc]
+    if "u3" in fwd:
+        v["u3"] = fwd["u3"][:, fc]
     v["g"] = fwd["g"][:, fc]
     v["fc2_partial"] = fwd["g"][:, fc] @ p["w2"][:, fc].T
     if grads is not None:
@@ -370,8 +404,13 @@ def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]]
         v["du"] = grads["du"][:, fc]
         v["dw2"] = grads["dw2"][:, fc]
         v["dw1"] = grads["dw1"][fc]
-        v["db1"] = grads["db1"][fc]
         v["fc1_dx_partial"] = grads["du"][:, fc] @ p["w1"][fc]
+        if "w3" in p:
+            v["du3"] = grads["du3"][:, fc]
+            v["dw3"] = grads["dw3"][fc]
+            v["fc1_dx_partial"] = v["fc1_dx_partial"] + grads["du3"][:, fc] @ p["w3"][fc]
+        else:
+            v["db1"] = grads["db1"][fc]
         v["dctx"] = grads["dctx"][:, hc]
         v["dwo"] = grads["dwo"][:, hc]
         v["dqkv"] = grads["dqkv"][:, qkv_cols]

@@ -62,6 +62,7 @@ class LayerConfig:
     seed: int = 0
     affine_random: bool = False  # draw non-trivial biases / LayerNorm affine
     sequence_parallel: bool = False  # per-token work on T/tp row blocks per rank
+    swiglu: bool = False         # SwiGLU FFN (gate w1, up w3), no FFN-input bias b1
     description: str = ""
 
     @property
@@ -98,6 +99,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         "7b_tp2_sp", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
         sequence_parallel=True,
         description="7B-style layer, one TP=2 rank shard with sequence parallelism, bf16"),
+    "7b_tp2_swiglu": LayerConfig(
+        "7b_tp2_swiglu", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        swiglu=True,
+        description="7B-style layer with a SwiGLU FFN (gate and up 11008 wide, no FFN-input "
+                    "bias), one TP=2 rank shard, bf16"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -132,6 +138,15 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_f32_tp4_sp": LayerConfig(
         "small_f32_tp4_sp", hidden=256, heads=4, ffn=1024, tp=4, seq_len=80, dtype="f32",
         affine_random=True, sequence_parallel=True),
+    "tiny_swiglu_tp2": LayerConfig(
+        "tiny_swiglu_tp2", hidden=256, heads=4, ffn=1024, tp=2, seq_len=128, dtype="f32",
+        swiglu=True, affine_random=True),
+    "small_bf16_swiglu_tp2": LayerConfig(
+        "small_bf16_swiglu_tp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=300, dtype="bf16",
+        swiglu=True, affine_random=True),
+    "small_bf16_swiglu_sp_tp4": LayerConfig(
+        "small_bf16_swiglu_sp_tp4", hidden=512, heads=8, ffn=2080, tp=4, seq_len=208,
+        dtype="bf16", swiglu=True, sequence_parallel=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }
@@ -187,6 +202,8 @@ def generate(cfg: LayerConfig, device: str = "cpu") -> Dict[str, object]:
         out[name] = normal((h, h), 0.02)
     out["w1"] = normal((f, h), 0.02)
     out["w2"] = normal((h, f), 0.02)
+    if cfg.swiglu:
+        out["w3"] = normal((f, h), 0.02)
     if cfg.vocab:
         out["emb"] = normal((cfg.vocab, h), 0.02)
         out["targets"] = torch.randint(0, cfg.vocab, (T,), generator=g, dtype=torch.int64).to(torch.int32)
@@ -208,6 +225,8 @@ def generate(cfg: LayerConfig, device: str = "cpu") -> Dict[str, object]:
         out["ln2_b"] = torch.zeros(h, dtype=dt)
         out["ln1_g"] = torch.ones(h, dtype=dt)
         out["ln2_g"] = torch.ones(h, dtype=dt)
+    if cfg.swiglu:
+        del out["b1"]  # the SwiGLU variant has no bias on the FFN input
     if device != "cpu":
         out = {k: v.to(device) for k, v in out.items()}
     return out

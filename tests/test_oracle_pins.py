@@ -99,6 +99,25 @@ def test_gelu_closed_forms_and_torch():
     assert abs(oracle.gelu_tanh_grad(np.array([0.0]))[0] - 0.5) < 1e-15
 
 
+def test_silu_closed_forms_and_torch():
+    """SiLU of the SwiGLU variant: SiLU(0) = 0, SiLU(z) -> z for large z and
+    -> 0 for very negative z, torch's silu on a grid, and the derivative
+    against central differences, autograd and SiLU'(0) = 1/2."""
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(oracle.silu(np.array([-40.0]))[0]) < 1e-14
+    z = np.linspace(-12, 12, 1201)
+    ref = F.silu(torch.tensor(z)).numpy()
+    assert np.max(np.abs(oracle.silu(z) - ref)) < 1e-14
+    eps = 1e-6
+    fd = (oracle.silu(z + eps) - oracle.silu(z - eps)) / (2 * eps)
+    assert np.max(np.abs(fd - oracle.silu_grad(z))) < 1e-8
+    zt = torch.tensor(z, requires_grad=True)
+    F.silu(zt).sum().backward()
+    assert np.max(np.abs(zt.grad.numpy() - oracle.silu_grad(z))) < 1e-13
+    assert abs(oracle.silu_grad(np.array([0.0]))[0] - 0.5) < 1e-15
+
+
 # ------------------------------------------------------------------ attention
 def _qkv(T, heads, d, seed):
     r = rng(seed)
@@ -223,9 +242,21 @@ PARAM_GRADS = [("x", "dx"), ("ln1_g", "dln1_g"), ("ln1_b", "dln1_b"), ("wq", "dw
                ("w2", "dw2"), ("b2", "db2")]
 
 
-def test_layer_gradients_finite_difference():
-    """Central differences of L = sum(dy * y) on the tiny config, in fp64."""
-    cfg, data, starts = _tiny()
+SWIGLU_PARAM_GRADS = [pg for pg in PARAM_GRADS if pg[0] != "b1"] + [("w3", "dw3")]
+
+
+@pytest.mark.parametrize("variant", ["gelu", "swiglu"])
+def test_layer_gradients_finite_difference(variant):
+    """Central differences of L = sum(dy * y) on the tiny config, in fp64
+    (GeLU FFN, and the SwiGLU FFN without its input bias)."""
+    if variant == "gelu":
+        cfg, data, starts = _tiny()
+        param_grads = PARAM_GRADS
+    else:
+        cfg = synth.get_config("tiny_swiglu_tp2")
+        data = synth.generate(cfg)
+        starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+        param_grads = SWIGLU_PARAM_GRADS
     p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
     dy = p64["dy"]
     cache = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
@@ -235,7 +266,7 @@ def test_layer_gradients_finite_difference():
         return float((oracle.layer_forward(pp, pp["x"], cfg.heads, cfg.eps, starts)["y"] * dy).sum())
     r = rng(12)
     eps = 1e-6
-    for pname, gname in PARAM_GRADS:
+    for pname, gname in param_grads:
         grad = grads[gname]
         # one random direction plus one sampled single entry per tensor
         dirs = [r.normal(size=grad.shape)]
@@ -251,10 +282,15 @@ def test_layer_gradients_finite_difference():
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (pname, fd, an)
 
 
-@pytest.mark.parametrize("tp", [1, 2, 4])
-def test_column_row_split_is_exact(tp):
+@pytest.mark.parametrize("tp,swiglu", [(1, False), (2, False), (4, False), (2, True), (4, True)])
+def test_column_row_split_is_exact(tp, swiglu):
     """Sum over ranks of the row-parallel partials equals the unsharded product."""
-    cfg, data, starts = _tiny(seed=3)
+    if swiglu:
+        cfg = synth.get_config("tiny_swiglu_tp2").replace(seed=3)
+        data = synth.generate(cfg)
+        starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    else:
+        cfg, data, starts = _tiny(seed=3)
     p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
     c = oracle.layer_forward(p64, p64["x"], cfg.heads, cfg.eps, starts)
     g = oracle.layer_backward(p64, c, p64["dy"], cfg.heads, starts)
