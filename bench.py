@@ -64,7 +64,8 @@ def shard_flops(cfg, cu) -> dict:
     """Model FLOPs of one rank shard, forward + backward (3x forward)."""
     T, h, t = cfg.tokens, cfg.hidden, cfg.tp
     hl, fl, al, d = h // t, cfg.ffn // t, cfg.heads // t, cfg.head_dim
-    gemm_fwd = 2 * T * (3 * h * hl + hl * h + 2 * h * fl)
+    f1 = 2 * fl if cfg.swiglu else fl  # FC1 output width (SwiGLU: gate and up)
+    gemm_fwd = 2 * T * (3 * h * hl + hl * h + h * f1 + h * fl)
     attn_fwd = 4 * d * al * seq_pairs(cu)
     vocab_fwd = 2 * T * h * (cfg.vocab // t) if cfg.vocab else 0
     return {
@@ -72,8 +73,8 @@ def shard_flops(cfg, cu) -> dict:
         "gemm": 3 * gemm_fwd, "attn": 3 * attn_fwd, "vocab": 3 * vocab_fwd,
         # per-call flops (M*N*K*2) of the GEMMs whose launches are probed
         "call": {"qkv_fwd": 2 * T * 3 * hl * h, "proj_fwd": 2 * T * hl * h,
-                 "fc1_fwd": 2 * T * h * fl, "fc2_fwd": 2 * T * fl * h,
-                 "fc2_wgrad": 2 * h * fl * T, "fc1_wgrad": 2 * fl * h * T,
+                 "fc1_fwd": 2 * T * h * f1, "fc2_fwd": 2 * T * fl * h,
+                 "fc2_wgrad": 2 * h * fl * T, "fc1_wgrad": 2 * f1 * h * T,
                  "proj_wgrad": 2 * h * hl * T, "qkv_wgrad": 2 * 3 * hl * h * T},
     }
 

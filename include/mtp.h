@@ -68,7 +68,11 @@ typedef enum {
     MTP_PROJ = 1,  /* row parallel:    [T,h_l] -> partial [T,h]                   */
     MTP_FC1 = 2,   /* column parallel: [T,h] -> [T,f_l], GeLU-tanh applied         */
     MTP_FC2 = 3,   /* row parallel:    [T,f_l] -> partial [T,h]                   */
-    MTP_VOCAB = 4  /* column parallel vocab head: [T,h] -> fp32 logits [T,V_l]   */
+    MTP_VOCAB = 4, /* column parallel vocab head: [T,h] -> fp32 logits [T,V_l]   */
+    /* SwiGLU FFN without a bias on its input (page "Megatron-LM 3D
+     * parallelism guide", §3.3: --swiglu --disable-bias-linear):          */
+    MTP_FC1_SWIGLU = 5, /* column parallel: [T,h] -> gate|up [T,2f_l] -> SiLU(gate)*up [T,f_l] */
+    MTP_FC2_SWIGLU = 6  /* row parallel: [T,f_l] -> partial [T,h] (as MTP_FC2)  */
 } mtp_linear_kind;
 
 /* Operation ids for mtp_workspace_size(). */
@@ -147,6 +151,12 @@ int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_part
  *                   receives u = x w^T + b and y [T,f_l] receives GeLU_tanh(u).
  *   kind MTP_VOCAB: x [T,h], w = vocab shard [V_l,h], b [V_l] nullable,
  *                   y = fp32 logits [T,V_l]; preact must be NULL.
+ *   kind MTP_FC1_SWIGLU: x [T,h]; w [2f_l,h] holds the rank's gate rows
+ *                   (of W1) and up rows (of W3) interleaved in groups of 4:
+ *                   rows 8j..8j+3 = gate rows 4j..4j+3, rows 8j+4..8j+7 = up
+ *                   rows 4j..4j+3.  b must be NULL.  preact [T,2f_l] receives
+ *                   x w^T in that interleaved column order and y [T,f_l]
+ *                   receives SiLU(gate) * up, SiLU(z) = z / (1 + e^-z).
  */
 int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, const void* w,
                        const void* b, void* y, void* preact, void* stream);
@@ -158,6 +168,8 @@ int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, cons
  *   dx_partial [T,h] dtype (out): this rank's partial of the input gradient.
  *     The input fed every rank, so the full gradient is the sum of all ranks'
  *     partials (mtp_partial_sum).  Nullable (skipped).
+ *   For MTP_FC1_SWIGLU, out_l = 2 f_l in the interleaved order of the
+ *   forward's w and preact, dw comes out in that order and db must be NULL.
  *   dw [out_l,h] fp32, db [out_l] fp32, both nullable (skipped): overwritten,
  *     or incremented when accumulate != 0.  Each of dx_partial, dw, db is an
  *     independent product, so one map's backward may be split over calls.
@@ -171,8 +183,8 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
  * RowParallelLinear with an already-sharded input (input_is_parallel=True,
  * same snippet); the output is this rank's partial of the full product.  The
  * pages sum the partials with an all-reduce; here mtp_partial_sum does it.
- *   kind MTP_PROJ: x_local [T,h_l], w [h,h_l];  kind MTP_FC2: x_local
- *   [T,f_l], w [h,f_l].  partial [T,h] dtype.  No bias: the row-parallel bias
+ *   kind MTP_PROJ: x_local [T,h_l], w [h,h_l];  kind MTP_FC2 and
+ *   MTP_FC2_SWIGLU: x_local [T,f_l], w [h,f_l].  partial [T,h] dtype.  No bias: the row-parallel bias
  *   is added once, after the sum (mtp_partial_sum).                          */
 int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local,
                        const void* w, void* partial, void* stream);
@@ -184,6 +196,11 @@ int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local
  *     GeLU_tanh(gelu_preact) and dx_local receives the gradient w.r.t. the
  *     pre-activation, (dy w) * GeLU_tanh'(gelu_preact), ready for
  *     mtp_col_linear_bwd(MTP_FC1).  Otherwise dx_local = dy w.
+ *   For MTP_FC2_SWIGLU, gelu_preact is instead the interleaved gate|up
+ *     preact [T,2f_l] of mtp_col_linear_fwd(MTP_FC1_SWIGLU); when given,
+ *     dx_local [T,2f_l] receives, in the same interleaved order, the
+ *     gradients w.r.t. gate, (dy w) * up * SiLU'(gate), and w.r.t. up,
+ *     (dy w) * SiLU(gate), ready for mtp_col_linear_bwd(MTP_FC1_SWIGLU).
  *   dx_local [T,in_l] dtype (out), nullable.
  *   dw [h,in_l] fp32 nullable; db [h] fp32 nullable (the row-parallel bias
  *     belongs to one rank: pass it on exactly one).  accumulate as above.

@@ -64,6 +64,7 @@ int64_t col_out(const Shard& s, int kind) {
   switch (kind) {
     case MTP_QKV: return 3LL * s.hl;
     case MTP_FC1: return s.fl;
+    case MTP_FC1_SWIGLU: return 2LL * s.fl;
     case MTP_VOCAB: return s.Vl;
     default: return 0;
   }
@@ -73,6 +74,7 @@ int64_t row_in(const Shard& s, int kind) {
   switch (kind) {
     case MTP_PROJ: return s.hl;
     case MTP_FC2: return s.fl;
+    case MTP_FC2_SWIGLU: return s.fl;
     default: return 0;
   }
 }
@@ -169,14 +171,17 @@ int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, cons
   const int64_t n = col_out(s, kind);
   if (n <= 0) return MTP_ERR_INVALID_ARG;
   if (!ok_ptr(x) || !ok_ptr(w) || !ok_opt(b) || !ok_ptr(y)) return MTP_ERR_INVALID_ARG;
-  if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
+  const bool swiglu = kind == MTP_FC1_SWIGLU;
+  if ((kind == MTP_FC1 || swiglu) ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
+  if (swiglu && b != nullptr) return MTP_ERR_INVALID_ARG;
   GemmDesc g{};
   g.A = x; g.lda = s.h; g.a_kmajor = true;
   g.B = w; g.ldb = s.h; g.b_kmajor = true;
   g.M = static_cast<int>(s.T); g.N = static_cast<int>(n); g.K = s.h;
-  g.C = y; g.ldc = n; g.bias = b;
+  g.C = y; g.ldc = swiglu ? s.fl : n; g.bias = b;
   g.aux = preact; g.ld_aux = n;
-  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : kind == MTP_VOCAB ? mtp::kEpiF32 : mtp::kEpiStore;
+  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : swiglu ? mtp::kEpiSwiGLU
+        : kind == MTP_VOCAB ? mtp::kEpiF32 : mtp::kEpiStore;
   g.tile = tile_override();
   return hip_status(gemm(s, g, static_cast<hipStream_t>(stream)));
 }
@@ -191,6 +196,7 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
   if (n <= 0) return MTP_ERR_INVALID_ARG;
   if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(w) || !ok_opt(dx_partial) || !ok_opt(dw) || !ok_opt(db))
     return MTP_ERR_INVALID_ARG;
+  if (kind == MTP_FC1_SWIGLU && db != nullptr) return MTP_ERR_INVALID_ARG;
   if (db) {
     const size_t need = mtp::column_sum_ws_bytes(s.T, n);
     if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
@@ -247,7 +253,8 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
   if (!ok_ptr(dy) || !ok_ptr(x_local) || !ok_ptr(w) || !ok_opt(dx_local) || !ok_opt(dw) ||
       !ok_opt(db) || !ok_opt(gelu_preact))
     return MTP_ERR_INVALID_ARG;
-  if (gelu_preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
+  if (gelu_preact && kind != MTP_FC2 && kind != MTP_FC2_SWIGLU) return MTP_ERR_INVALID_ARG;
+  const bool swiglu = kind == MTP_FC2_SWIGLU && gelu_preact != nullptr;
   if (db) {
     const size_t need = mtp::column_sum_ws_bytes(s.T, s.h);
     if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
@@ -259,9 +266,9 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.A = dy; g.lda = s.h; g.a_kmajor = true;
     g.B = w; g.ldb = k; g.b_kmajor = false;
     g.M = static_cast<int>(s.T); g.N = static_cast<int>(k); g.K = s.h;
-    g.C = dx_local; g.ldc = k;
-    g.aux = const_cast<void*>(gelu_preact); g.ld_aux = k;
-    g.epi = gelu_preact ? mtp::kEpiDGelu : mtp::kEpiStore;
+    g.C = dx_local; g.ldc = swiglu ? 2 * k : k;
+    g.aux = const_cast<void*>(gelu_preact); g.ld_aux = swiglu ? 2 * k : k;
+    g.epi = swiglu ? mtp::kEpiDSwiGLU : gelu_preact ? mtp::kEpiDGelu : mtp::kEpiStore;
     g.tile = tile_override();
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;

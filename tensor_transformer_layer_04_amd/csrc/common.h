@@ -117,6 +117,13 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
   return s * fmaf(u * (1.0f - s) * (2.0f * kGeluC), fmaf(3.0f * kGeluA * u, u, 1.0f), 1.0f);
 }
 
+// SiLU(z) = z s, s = 1 / (1 + e^-z) (one v_exp_f32, one v_rcp_f32), and
+// SiLU'(z) = s (1 + z (1 - s)).
+constexpr float kNegLog2e = -1.4426950408889634f;
+__device__ __forceinline__ float silu_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNegLog2e * z));
+}
+
 // v combined with the value of lane ^ 32: v_permlane32_swap exchanges the
 // two 32-lane halves without an LDS round trip; the pair it returns holds,
 // in every lane, the lower-half value first and the upper-half value second.

@@ -185,6 +185,22 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] *= gelu_tanh_grad(u[c]);
     store4(static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + n, v);
+  } else if (EPI == kEpiDSwiGLU) {
+    // v = dg at columns n..n+3 (n % 4 == 0): gate and up of these columns
+    // sit at interleaved columns 2n..2n+3 and 2n+4..2n+7.
+    const int64_t a = static_cast<int64_t>(m) * p.ld_aux + 2 * n;
+    float gt[4], up[4], dgate[4], dup[4];
+    load4(static_cast<const ElemT*>(p.aux) + a, gt);
+    load4(static_cast<const ElemT*>(p.aux) + a + 4, up);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float sg = silu_sigmoid(gt[c]);
+      dup[c] = v[c] * gt[c] * sg;
+      dgate[c] = v[c] * up[c] * sg * fmaf(gt[c], 1.0f - sg, 1.0f);
+    }
+    ElemT* o = static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + 2 * n;
+    store4(o, dgate);
+    store4(o + 4, dup);
   } else if (EPI == kEpiF32) {
     store4(static_cast<float*>(p.C) + static_cast<int64_t>(m) * p.ldc + n, v);
   } else {  // kEpiF32Acc
@@ -194,6 +210,22 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] += o[i];
     store4(c, v);
+  }
+}
+
+// SwiGLU forward epilogue of columns n..n+3 (n % 4 == 0) of the interleaved
+// gate|up product: v holds them, pv the partner group (n ^ 4).  Both lanes
+// store their group as the pre-activation; the gate lane (n % 8 == 0)
+// writes SiLU(gate) * up to output columns n/2 .. n/2+3.
+template <typename ElemT>
+__device__ __forceinline__ void epi_swiglu(const GemmParams& p, int m, int n, const float v[4],
+                                           const float pv[4]) {
+  store4(static_cast<ElemT*>(p.aux) + static_cast<int64_t>(m) * p.ld_aux + n, v);
+  if ((n & 4) == 0) {
+    float o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = v[c] * silu_sigmoid(v[c]) * pv[c];
+    store4(static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + n / 2, o);
   }
 }
 
@@ -224,10 +256,24 @@ __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, con
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
   const int n = nb + sc;
+  if constexpr (EPI == kEpiSwiGLU) {
+    // lanes l and l ^ 1 hold the gate and up groups of one row
+    float pv[4][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = mb + 8 * r + sr;
-    if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pv[r][c] = __shfl_xor(v[r][c], 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + 8 * r + sr;
+      if (m < p.M && n < p.N) epi_swiglu<bf16_t>(p, m, n, v[r], pv[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + 8 * r + sr;
+      if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
+    }
   }
 }
 
@@ -565,7 +611,15 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmParams p, const float
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i, n = n0 + tx * 4;
-    if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i]);
+    if constexpr (EPI == kEpiSwiGLU) {
+      // threads tx and tx ^ 1 (lanes l and l ^ 1) hold the gate and up groups
+      float pv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pv[c] = __shfl_xor(acc[i][c], 1);
+      if (m < p.M && n < p.N) epi_swiglu<float>(p, m, n, acc[i], pv);
+    } else {
+      if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i]);
+    }
   }
 }
 
@@ -600,8 +654,8 @@ GemmParams to_params(const GemmDesc& g) {
 }  // namespace
 
 // Layout / epilogue combinations the layer uses:
-//   forward (k-major, k-major):  Store, Gelu, F32
-//   dgrad   (k-major, n-major):  Store, DGelu
+//   forward (k-major, k-major):  Store, Gelu, SwiGLU, F32
+//   dgrad   (k-major, n-major):  Store, DGelu, DSwiGLU
 //   wgrad   (m-major, n-major):  F32, F32Acc
 hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
@@ -621,6 +675,7 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     switch (g.epi) {
       case kEpiStore: return dispatch_tile<true, true, kEpiStore>(p, tile, s);
       case kEpiGelu: return dispatch_tile<true, true, kEpiGelu>(p, tile, s);
+      case kEpiSwiGLU: return dispatch_tile<true, true, kEpiSwiGLU>(p, tile, s);
       case kEpiF32: return dispatch_tile<true, true, kEpiF32>(p, tile, s);
       default: break;
     }
@@ -628,6 +683,7 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     switch (g.epi) {
       case kEpiStore: return dispatch_tile<true, false, kEpiStore>(p, tile, s);
       case kEpiDGelu: return dispatch_tile<true, false, kEpiDGelu>(p, tile, s);
+      case kEpiDSwiGLU: return dispatch_tile<true, false, kEpiDSwiGLU>(p, tile, s);
       default: break;
     }
   } else if (!g.a_kmajor && !g.b_kmajor) {
@@ -647,6 +703,7 @@ hipError_t gemm_f32(const GemmDesc& g, hipStream_t s) {
     switch (g.epi) {
       case kEpiStore: return launch_f32<true, true, kEpiStore>(p, s);
       case kEpiGelu: return launch_f32<true, true, kEpiGelu>(p, s);
+      case kEpiSwiGLU: return launch_f32<true, true, kEpiSwiGLU>(p, s);
       case kEpiF32: return launch_f32<true, true, kEpiF32>(p, s);
       default: break;
     }
@@ -654,6 +711,7 @@ hipError_t gemm_f32(const GemmDesc& g, hipStream_t s) {
     switch (g.epi) {
       case kEpiStore: return launch_f32<true, false, kEpiStore>(p, s);
       case kEpiDGelu: return launch_f32<true, false, kEpiDGelu>(p, s);
+      case kEpiDSwiGLU: return launch_f32<true, false, kEpiDSwiGLU>(p, s);
       default: break;
     }
   } else if (!g.a_kmajor && !g.b_kmajor) {

@@ -18,6 +18,10 @@ enum Epilogue : int {
   kEpiDGelu = 2,    // C = acc * GeLU_tanh'(aux)               C, aux elem type
   kEpiF32 = 3,      // C = acc (+ bias[n])                     C fp32
   kEpiF32Acc = 4,   // C += acc                                C fp32
+  // SwiGLU, columns interleaved in groups of 4 (gate 8j..8j+3, up 8j+4..8j+7):
+  kEpiSwiGLU = 5,   // aux = acc; C[n/2 + i] = SiLU(gate) * up   C, aux elem type
+  kEpiDSwiGLU = 6,  // acc = dg [.., N]: C/aux [.., 2N] interleaved:
+                    //   C(gate) = dg * up * SiLU'(gate), C(up) = dg * SiLU(gate)
 };
 
 struct GemmDesc {

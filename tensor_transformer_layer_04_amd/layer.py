@@ -77,14 +77,37 @@ def pack_rank_weights(full: Dict[str, torch.Tensor], cfg, rank: int,
         "bqkv": dev(torch.cat([full["bqkv"][:h][hs], full["bqkv"][h:2 * h][hs],
                                full["bqkv"][2 * h:][hs]], 0)),
         "wo": dev(full["wo"][:, hs]),
-        "w1": dev(full["w1"][fs]),
-        "b1": dev(full["b1"][fs]),
         "w2": dev(full["w2"][:, fs]),
     }
+    if getattr(cfg, "swiglu", False):
+        # gate rows (W1) and up rows (W3) interleaved in groups of 4, the
+        # layout MTP_FC1_SWIGLU takes
+        w["w1"] = dev(swiglu_interleave(full["w1"][fs], full["w3"][fs]))
+    else:
+        w["w1"] = dev(full["w1"][fs])
+        w["b1"] = dev(full["b1"][fs])
     if cfg.vocab:
         vl = cfg.vocab // t
         w["emb"] = dev(full["emb"][rank * vl:(rank + 1) * vl])
     return w
+
+
+def swiglu_interleave(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+    """Rows (or, for a [T, f] activation, columns via .T) of gate and up
+    interleaved in groups of 4: [g0..g3, u0..u3, g4..g7, u4..u7, ...]."""
+    f = gate.shape[0]
+    return torch.stack([gate.reshape(f // 4, 4, *gate.shape[1:]),
+                        up.reshape(f // 4, 4, *up.shape[1:])], 1).reshape(2 * f, *gate.shape[1:])
+
+
+def swiglu_split(x: torch.Tensor, dim: int = 0):
+    """Inverse of ``swiglu_interleave`` along ``dim``: (gate, up)."""
+    x = x.movedim(dim, 0)
+    f2 = x.shape[0]
+    v = x.reshape(f2 // 8, 2, 4, *x.shape[1:])
+    gate = v[:, 0].reshape(f2 // 2, *x.shape[1:]).movedim(0, dim)
+    up = v[:, 1].reshape(f2 // 2, *x.shape[1:]).movedim(0, dim)
+    return gate, up
 
 
 def replicated_params(full: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch.Tensor]:
@@ -137,6 +160,9 @@ class TPLayer(_Probed):
         # ``overlap`` they run on a second stream (default priority) next to
         # the data gradients, joined back before backward() returns.
         self.side = torch.cuda.Stream(device=self.device) if overlap else None
+        self.swiglu = bool(getattr(cfg, "swiglu", False))
+        self.k_fc1 = mtp.MTP_FC1_SWIGLU if self.swiglu else mtp.MTP_FC1
+        self.k_fc2 = mtp.MTP_FC2_SWIGLU if self.swiglu else mtp.MTP_FC2
         self.sp = bool(getattr(cfg, "sequence_parallel", False)) and cfg.tp > 1
         if self.sp:
             # Each rank's row block must start on a 16-byte boundary of the
@@ -162,12 +188,14 @@ class TPLayer(_Probed):
         self.ln1, self.y1, self.ln2, self.y = E(T, h), E(T, h), E(T, h), E(T, h)
         self.mu1, self.rs1, self.mu2, self.rs2 = (E(T, d=torch.float32) for _ in range(4))
         self.a: Dict[int, Dict[str, torch.Tensor]] = {}
+        # SwiGLU: the FC1 output (and its gradient) is the interleaved gate|up pair
+        ul = 2 * fl if self.swiglu else fl
         for r in self.ranks:
             self.a[r] = {
                 "qkv": E(T, 3 * hl), "ctx": E(T, hl), "lse": E(al, T, d=torch.float32),
-                "p": E(T, h), "u": E(T, fl), "g": E(T, fl), "q": E(T, h),
+                "p": E(T, h), "u": E(T, ul), "g": E(T, fl), "q": E(T, h),
                 # backward
-                "du": E(T, fl), "dln2": E(T, h), "dctx": E(T, hl), "dqkv": E(T, 3 * hl),
+                "du": E(T, ul), "dln2": E(T, h), "dctx": E(T, hl), "dqkv": E(T, 3 * hl),
                 "dln1": E(T, h),
             }
         self.dy1, self.dx = E(T, h), E(T, h)
@@ -176,8 +204,10 @@ class TPLayer(_Probed):
         for r in self.ranks:
             self.grads[r] = {
                 "dwqkv": E(3 * hl, h, d=f32), "dbqkv": E(3 * hl, d=f32), "dwo": E(h, hl, d=f32),
-                "dw1": E(fl, h, d=f32), "db1": E(fl, d=f32), "dw2": E(h, fl, d=f32),
+                "dw1": E(ul, h, d=f32), "dw2": E(h, fl, d=f32),
             }
+            if not self.swiglu:
+                self.grads[r]["db1"] = E(fl, d=f32)
         self.rgrads = {k: E(h, d=f32) for k in ("dln1_g", "dln1_b", "dln2_g", "dln2_b", "dbo", "db2")}
         d = self.d0
         ws = max(
@@ -242,9 +272,10 @@ class TPLayer(_Probed):
         for r in self.ranks:
             d, w, a = self.descs[r], self.w[r], self.a[r]
             with T("fc1_fwd"):
-                mtp.mtp_col_linear_fwd(d, mtp.MTP_FC1, self.ln2, w["w1"], w["b1"], a["g"], a["u"])
+                mtp.mtp_col_linear_fwd(d, self.k_fc1, self.ln2, w["w1"], w.get("b1"), a["g"],
+                                       a["u"])
             with T("fc2_fwd"):
-                mtp.mtp_row_linear_fwd(d, mtp.MTP_FC2, a["g"], w["w2"], a["q"])
+                mtp.mtp_row_linear_fwd(d, self.k_fc2, a["g"], w["w2"], a["q"])
         parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
         if self.sp:
             for r in self.ranks:
@@ -281,30 +312,30 @@ class TPLayer(_Probed):
             d, w, a, g = self.descs[r], self.w[r], self.a[r], self.grads[r]
             db2 = self.rgrads["db2"] if (r == self.owns_bias and not self.sp) else None
             with T("fc2_dgrad"):
-                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], a["u"], a["du"], None,
+                mtp.mtp_row_linear_bwd(d, self.k_fc2, dy, a["g"], w["w2"], a["u"], a["du"], None,
                                        None, 0, ws, wsb)
             with on_side(), T("fc2_wgrad", side):
-                mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, g["dw2"],
+                mtp.mtp_row_linear_bwd(d, self.k_fc2, dy, a["g"], w["w2"], None, None, g["dw2"],
                                        None, 0, wss, wsb)
             if db2 is not None:
                 with on_side(), T("fc2_bias", side):
-                    mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
+                    mtp.mtp_row_linear_bwd(d, self.k_fc2, dy, a["g"], w["w2"], None, None, None,
                                            db2, 0, wss, wsb)
             if self.sp:
                 # row-parallel bias: this rank's column sums of dy over its rows
                 s = self.rows[r]
                 with on_side(), T("fc2_bias", side):
-                    mtp.mtp_row_linear_bwd(self.rdesc[r], mtp.MTP_FC2, dy[s], a["g"][s], w["w2"],
+                    mtp.mtp_row_linear_bwd(self.rdesc[r], self.k_fc2, dy[s], a["g"][s], w["w2"],
                                            None, None, None, self.rgrads["db2"],
                                            int(r != self.ranks[0]), wss, wsb)
             # FC1's weight gradient needs only du: it is queued as soon as
             # du exists, beside FC1's data gradient.
             fork()
             with on_side(), T("fc1_wgrad", side):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, g["dw1"],
-                                       g["db1"], 0, wss, wsb)
+                mtp.mtp_col_linear_bwd(d, self.k_fc1, a["du"], self.ln2, w["w1"], None, g["dw1"],
+                                       g.get("db1"), 0, wss, wsb)
             with T("fc1_dgrad"):
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], a["dln2"], None,
+                mtp.mtp_col_linear_bwd(d, self.k_fc1, a["du"], self.ln2, w["w1"], a["dln2"], None,
                                        None, 0, ws, wsb)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
         if self.sp:

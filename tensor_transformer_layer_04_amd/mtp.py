@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmtp.so")
 
 MTP_OK, MTP_ERR_INVALID_ARG, MTP_ERR_UNSUPPORTED, MTP_ERR_WORKSPACE, MTP_ERR_HIP = range(5)
 MTP_F32, MTP_BF16 = 0, 1
-MTP_QKV, MTP_PROJ, MTP_FC1, MTP_FC2, MTP_VOCAB = range(5)
+MTP_QKV, MTP_PROJ, MTP_FC1, MTP_FC2, MTP_VOCAB, MTP_FC1_SWIGLU, MTP_FC2_SWIGLU = range(7)
 (MTP_OP_LAYERNORM_BWD, MTP_OP_COL_LINEAR_BWD, MTP_OP_ROW_LINEAR_BWD, MTP_OP_ATTN_BWD,
  MTP_OP_VOCAB_CE) = range(5)
 

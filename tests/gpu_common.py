@@ -85,17 +85,33 @@ def compare_layer(cfg, L, c, g, data, report, rows=None, ranks=None):
         check(f"r{r}.ctx", cpu(a["ctx"])[sl], v["ctx"][sl], tol, report)
         check(f"r{r}.lse", cpu(a["lse"])[:, sl], v["lse"][:, sl], tol, report)
         check(f"r{r}.proj_partial", cpu(a["p"])[sl], v["proj_partial"][sl], tol, report)
-        check(f"r{r}.u", cpu(a["u"])[sl], v["u"][sl], tol, report)
+        if getattr(cfg, "swiglu", False):
+            from tensor_transformer_layer_04_amd.layer import swiglu_split
+            ug, uu = swiglu_split(cpu(a["u"]), 1)
+            check(f"r{r}.u_gate", ug[sl], v["u"][sl], tol, report)
+            check(f"r{r}.u_up", uu[sl], v["u3"][sl], tol, report)
+        else:
+            check(f"r{r}.u", cpu(a["u"])[sl], v["u"][sl], tol, report)
         check(f"r{r}.g", cpu(a["g"])[sl], v["g"][sl], tol, report)
         check(f"r{r}.fc2_partial", cpu(a["q"])[sl], v["fc2_partial"][sl], tol, report)
-        check(f"r{r}.du", cpu(a["du"])[sl], v["du"][sl], tol, report)
+        if getattr(cfg, "swiglu", False):
+            dg_, du_ = swiglu_split(cpu(a["du"]), 1)
+            check(f"r{r}.du_gate", dg_[sl], v["du"][sl], tol, report)
+            check(f"r{r}.du_up", du_[sl], v["du3"][sl], tol, report)
+        else:
+            check(f"r{r}.du", cpu(a["du"])[sl], v["du"][sl], tol, report)
         check(f"r{r}.fc1_dx_partial", cpu(a["dln2"])[sl], v["fc1_dx_partial"][sl], tol, report)
         check(f"r{r}.dctx", cpu(a["dctx"])[sl], v["dctx"][sl], tol, report)
         check(f"r{r}.dqkv", cpu(a["dqkv"])[sl], v["dqkv"][sl], tol, report)
         check(f"r{r}.qkv_dx_partial", cpu(a["dln1"])[sl], v["qkv_dx_partial"][sl], tol, report)
         check(f"r{r}.dw2", cpu(gr["dw2"]), v["dw2"], tol, report)
-        check(f"r{r}.dw1", cpu(gr["dw1"]), v["dw1"], tol, report)
-        check(f"r{r}.db1", cpu(gr["db1"]), v["db1"], tol, report)
+        if getattr(cfg, "swiglu", False):
+            w1g, w3g = swiglu_split(cpu(gr["dw1"]), 0)
+            check(f"r{r}.dw1", w1g, v["dw1"], tol, report)
+            check(f"r{r}.dw3", w3g, v["dw3"], tol, report)
+        else:
+            check(f"r{r}.dw1", cpu(gr["dw1"]), v["dw1"], tol, report)
+            check(f"r{r}.db1", cpu(gr["db1"]), v["db1"], tol, report)
         check(f"r{r}.dwo", cpu(gr["dwo"]), v["dwo"], tol, report)
         check(f"r{r}.dwqkv", cpu(gr["dwqkv"]), v["dwqkv"], tol, report)
         check(f"r{r}.dbqkv", cpu(gr["dbqkv"]), v["dbqkv"], tol, report)

@@ -84,6 +84,15 @@ def test_kind_and_workspace_errors():
                                   None) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_row_linear_fwd(ctypes.byref(d), mtp.MTP_QKV, FAKE, FAKE, FAKE,
                                   None) == mtp.MTP_ERR_INVALID_ARG
+    # the SwiGLU maps take no FFN-input bias and need the pre-activation
+    assert lib.mtp_col_linear_fwd(ctypes.byref(d), mtp.MTP_FC1_SWIGLU, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_col_linear_fwd(ctypes.byref(d), mtp.MTP_FC1_SWIGLU, FAKE, FAKE, None, FAKE,
+                                  None, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_col_linear_bwd(ctypes.byref(d), mtp.MTP_FC1_SWIGLU, FAKE, FAKE, FAKE, None,
+                                  None, FAKE, 0, FAKE, 1 << 30, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_col_linear_fwd(ctypes.byref(d), 7, FAKE, FAKE, None, FAKE, None,
+                                  None) == mtp.MTP_ERR_INVALID_ARG
     # FC1 needs the pre-activation buffer, QKV must not get one
     assert lib.mtp_col_linear_fwd(ctypes.byref(d), mtp.MTP_FC1, FAKE, FAKE, None, FAKE, None,
                                   None) == mtp.MTP_ERR_INVALID_ARG
