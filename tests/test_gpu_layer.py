@@ -55,6 +55,22 @@ def test_layer_parity_7b_tp2_full():
     log(f"  worst: {fmt_report(report)}")
 
 
+@pytest.mark.parametrize("name", ["7b_tp2_sp", "7b_tp2_swiglu"])
+def test_layer_parity_7b_variants_full(name):
+    """The 7B-style TP=2 layer with sequence parallelism and with the SwiGLU
+    FFN: both shards at full size against the full oracle."""
+    require_gpu()
+    cfg = synth.CONFIGS[name]
+    log(f"layer parity {name} (full size, both ranks)")
+    data = synth.generate(cfg)
+    L = run_gpu_layer(cfg, data)
+    log("  GPU done; running oracle")
+    c, g = oracle_layer(cfg, data)
+    report = {}
+    compare_layer(cfg, L, c, g, data, report)
+    log(f"  worst: {fmt_report(report)}")
+
+
 def _prefix_case(name, P):
     require_gpu()
     cfg = synth.CONFIGS[name]
