@@ -239,6 +239,43 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                  const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* ------------------------------------------ context-parallel attention
+ * The sequence split into chunks whose attention runs block pair by block
+ * pair, each partial result merged through its log-sum-exp (context
+ * parallelism, named among the parallel strategies in §4 of page
+ * "Megatron-LM / Megatron Core README digest"; the pages give no algorithm,
+ * the chunked, log-sum-exp merged form is the plain reading of splitting
+ * the sequence dimension of attention; here all chunks are computed on one
+ * device, one pair per call).  bf16 shards, one sequence
+ * (micro_batch 1, no cu_seqlens), else MTP_ERR_UNSUPPORTED.
+ *
+ * mtp_attn_fwd_block: queries at rows [q_lo, q_hi) of qkv attend to the keys
+ *   at rows [k_lo, k_hi) with the causal mask of their absolute positions:
+ *   either the diagonal block (q_lo == k_lo, q_hi == k_hi) or a block whose
+ *   keys all precede the queries (k_hi <= q_lo), else MTP_ERR_INVALID_ARG.
+ *   Writes rows [q_lo, q_hi) of ctx [T,h_l] and columns [q_lo, q_hi) of lse
+ *   [a_l,T] (natural log of each row's sum of exp(score)) and nothing else. */
+int mtp_attn_fwd_block(const mtp_shard_desc* desc, const void* qkv, int64_t q_lo, int64_t q_hi,
+                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse, void* stream);
+
+/* mtp_attn_merge: rows [row_lo, row_hi) of (ctx, lse) become the attention
+ *   over the union of the key sets of (ctx, lse) and (ctx_part, lse_part),
+ *   two results of mtp_attn_fwd_block for the same queries and disjoint keys:
+ *   lse = log(e^lse + e^lse_part), ctx = (e^lse ctx + e^lse_part ctx_part) /
+ *   e^lse_new, per row and head.  In place on (ctx, lse).                   */
+int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void* ctx_part,
+                   const float* lse_part, int64_t row_lo, int64_t row_hi, void* stream);
+
+/* mtp_attn_bwd_block: the backward of one block pair given the merged ctx and
+ *   lse of the queries (the whole rows' softmax): writes (accumulate == 0) or
+ *   adds to (accumulate != 0) the dQ columns of dqkv at the query rows and
+ *   the dK, dV columns at the key rows; q_hi - q_lo must equal k_hi - k_lo.
+ *   Needs the workspace of mtp_attn_bwd.                                    */
+int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
+                       const float* lse, const void* dctx, void* dqkv, int64_t q_lo,
+                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate, void* ws,
+                       size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ partial sum
  * The sum that the pages perform with a tensor-parallel all-reduce (page
  * "Megatron-LM 3D parallelism guide", §2.1: the row-split output projection's

@@ -63,6 +63,7 @@ class LayerConfig:
     affine_random: bool = False  # draw non-trivial biases / LayerNorm affine
     sequence_parallel: bool = False  # per-token work on T/tp row blocks per rank
     swiglu: bool = False         # SwiGLU FFN (gate w1, up w3), no FFN-input bias b1
+    context_parallel: int = 1    # attention over this many sequence chunks, pair by pair
     description: str = ""
 
     @property
@@ -104,6 +105,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         swiglu=True,
         description="7B-style layer with a SwiGLU FFN (gate and up 11008 wide, no FFN-input "
                     "bias), one TP=2 rank shard, bf16"),
+    "7b_tp2_cp2": LayerConfig(
+        "7b_tp2_cp2", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        context_parallel=2,
+        description="7B-style layer, one TP=2 rank shard, attention as 2 context-parallel "
+                    "chunks merged by log-sum-exp, bf16"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -147,6 +153,12 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_bf16_swiglu_sp_tp4": LayerConfig(
         "small_bf16_swiglu_sp_tp4", hidden=512, heads=8, ffn=2080, tp=4, seq_len=208,
         dtype="bf16", swiglu=True, sequence_parallel=True),
+    "small_bf16_tp2_cp2": LayerConfig(
+        "small_bf16_tp2_cp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=300, dtype="bf16",
+        affine_random=True, context_parallel=2),
+    "small_bf16_d64_cp4": LayerConfig(
+        "small_bf16_d64_cp4", hidden=512, heads=8, ffn=2080, tp=4, seq_len=264, dtype="bf16",
+        context_parallel=4),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

@@ -81,6 +81,19 @@ int64_t row_in(const Shard& s, int kind) {
 
 int tile_override() { return -1; }
 
+// A (query rows, key rows) block of the context-parallel entry points: the
+// diagonal block of one chunk, or keys entirely before the queries.  The
+// path is the bf16 MFMA one, over one sequence (micro_batch 1).
+int check_block(const Shard& s, const mtp_shard_desc* desc, int64_t q_lo, int64_t q_hi,
+                int64_t k_lo, int64_t k_hi) {
+  if (!s.bf16 || desc->micro_batch != 1) return MTP_ERR_UNSUPPORTED;
+  if (q_lo < 0 || q_hi > s.T || q_lo >= q_hi || k_lo < 0 || k_hi > s.T || k_lo >= k_hi)
+    return MTP_ERR_INVALID_ARG;
+  const bool diagonal = q_lo == k_lo && q_hi == k_hi;
+  const bool before = k_hi <= q_lo;
+  return (diagonal || before) ? MTP_OK : MTP_ERR_INVALID_ARG;
+}
+
 }  // namespace
 
 extern "C" {
@@ -317,6 +330,58 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, c
   a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
   a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_attn_fwd_block(const mtp_shard_desc* desc, const void* qkv, int64_t q_lo, int64_t q_hi,
+                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
+  st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
+  if (st != MTP_OK) return st;
+  mtp::AttnDesc a{};
+  a.qkv = qkv; a.ctx = ctx; a.lse = lse;
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  a.q_lo = q_lo; a.q_hi = q_hi; a.k_lo = k_lo; a.k_hi = k_hi;
+  return hip_status(mtp::attn_fwd(s.bf16, a, static_cast<hipStream_t>(stream)));
+}
+int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void* ctx_part,
+                   const float* lse_part, int64_t row_lo, int64_t row_hi, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  if (!ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(ctx_part) || !ok_ptr(lse_part))
+    return MTP_ERR_INVALID_ARG;
+  if (row_lo < 0 || row_hi > s.T || row_lo > row_hi) return MTP_ERR_INVALID_ARG;
+  mtp::AttnDesc a{};
+  a.ctx = ctx; a.lse = lse;
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  return hip_status(mtp::attn_merge(a, ctx_part, lse_part, row_lo, row_hi,
+                                    static_cast<hipStream_t>(stream)));
+}
+int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
+                       const float* lse, const void* dctx, void* dqkv, int64_t q_lo,
+                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
+    return MTP_ERR_INVALID_ARG;
+  st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
+  if (st != MTP_OK) return st;
+  if (q_hi - q_lo != k_hi - k_lo) return MTP_ERR_INVALID_ARG;
+  const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
+  if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  mtp::AttnDesc a{};
+  a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
+  a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  a.q_lo = q_lo; a.q_hi = q_hi; a.k_lo = k_lo; a.k_hi = k_hi;
+  a.accumulate = accumulate != 0;
   return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -217,6 +217,37 @@ __global__ void __launch_bounds__(64) attn_dkv_f32(AttnParams p, int D) {
   if (lane + 64 < D) { out[p.hl + lane + 64] = dk1 * p.scale; out[2 * p.hl + lane + 64] = dv1; }
 }
 
+// Merge of two partial attention results of the same queries over disjoint
+// key sets (their union is the keys the query sees): with weights
+// w = e^(lse - max(lse_a, lse_b)), ctx = (w_a ctx_a + w_b ctx_b) / (w_a + w_b)
+// and lse = max + log(w_a + w_b) (natural log).  One thread per (row, head)
+// reads both partials of its row and head before writing either output, so
+// the accumulated pair may be updated in place.
+__global__ void __launch_bounds__(256) attn_merge_kernel(bf16_t* ctx, float* lse,
+                                                         const bf16_t* ctx_p, const float* lse_p,
+                                                         int T, int hl, int heads, int D,
+                                                         int row_lo, int rows) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(rows) * heads) return;
+  const int r = row_lo + static_cast<int>(idx / heads), h = static_cast<int>(idx % heads);
+  const int64_t li = static_cast<int64_t>(h) * T + r;
+  const float la = lse[li], lb = lse_p[li];
+  const float m = fmaxf(la, lb);
+  const float wa = __expf(la - m), wb = __expf(lb - m);
+  const float inv = 1.0f / (wa + wb);
+  bf16_t* o = ctx + static_cast<int64_t>(r) * hl + h * D;
+  const bf16_t* q = ctx_p + static_cast<int64_t>(r) * hl + h * D;
+  for (int c = 0; c < D; c += 8) {
+    float a[8], b[8];
+    load8(o + c, a);
+    load8(q + c, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (wa * a[e] + wb * b[e]) * inv;
+    store8(o + c, a);
+  }
+  lse[li] = m + __logf(wa + wb);
+}
+
 AttnParams make_params(const AttnDesc& a) {
   AttnParams p{};
   p.qkv = a.qkv; p.ld = 3LL * a.heads * a.head_dim;
@@ -240,6 +271,19 @@ hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_fwd_f32, dim3(static_cast<unsigned>(a.T * a.heads)), dim3(64), 0, s,
                        p, a.head_dim);
   }
+  return hipGetLastError();
+}
+
+hipError_t attn_merge(const AttnDesc& a, const void* ctx_part, const float* lse_part,
+                      int64_t row_lo, int64_t row_hi, hipStream_t s) {
+  const int64_t rows = row_hi - row_lo;
+  if (rows <= 0 || a.heads == 0) return hipSuccess;
+  const int64_t n = rows * a.heads;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, static_cast<bf16_t*>(a.ctx), a.lse,
+                     static_cast<const bf16_t*>(ctx_part), lse_part, static_cast<int>(a.T),
+                     a.heads * a.head_dim, a.heads, a.head_dim, static_cast<int>(row_lo),
+                     static_cast<int>(rows));
   return hipGetLastError();
 }
 

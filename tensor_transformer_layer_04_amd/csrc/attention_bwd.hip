@@ -46,6 +46,8 @@ struct BwdParams {
   const int32_t* cu;
   int n_seqs;
   int T, seq_len, heads, nblk;
+  int q_lo, q_hi, k_lo, k_hi;  // query and key row ranges (absolute)
+  int accumulate;              // add into dqkv instead of storing
   float scale, scale_log2;
   uint32_t qkv_bytes, dctx_bytes, stat_bytes;
 };
@@ -96,10 +98,10 @@ __device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t rs, char* tile
 // Copy stat[head][r0..r0+63] (lse or delta, fp32) into the first 256 bytes
 // of a 1 KB LDS block (one copy; lanes 16..63 fetch zeros).
 __device__ __forceinline__ void issue_stat(__amdgpu_buffer_rsrc_t rs, char* dst, int lane, int head,
-                                           int r0, int T) {
+                                           int r0, int T, int rmax) {
   const int r = r0 + 4 * lane;
   const uint32_t off =
-      (lane < 16 && r >= 0 && r < T) ? (static_cast<uint32_t>(head) * T + r) * 4u : kOOB;
+      (lane < 16 && r >= 0 && r < rmax) ? (static_cast<uint32_t>(head) * T + r) * 4u : kOOB;
   copy16_to_lds(rs, dst, off);
 }
 
@@ -180,7 +182,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int 
                                           char* st1) {
   constexpr int KS = D / 16, DB = D / 32;
   const int T = p.T;
-  const int k0 = kblk * kBT;
+  const int k0 = p.k_lo + kblk * kBT;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -188,13 +190,14 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int 
   const int lk = lane & 31, g = lane >> 5;
   const int ka = k0 + kg * 32;  // first key of this wave
   const int kj = ka + lk;       // this lane's key
-  const bool kvalid = kj < T;
-  const int ka_last = min(ka + 31, T - 1);
-  // queries that see this lane's key: [kj, kend); wend <= every lane's kend
-  const int kend = kvalid ? seq_end(p, kj) : kj;
-  const int wend = (ka + 31 < T) ? seq_end(p, ka) : 0;
-  const int q_lo = k0;
-  const int q_hi = seq_end(p, min(k0 + kBT - 1, T - 1));
+  const bool kvalid = kj < p.k_hi;
+  const int ka_last = min(ka + 31, p.k_hi - 1);
+  // queries that see this lane's key: [kj, kend) within the query range;
+  // wend <= every lane's kend
+  const int kend = kvalid ? min(seq_end(p, kj), p.q_hi) : kj;
+  const int wend = (ka + 31 < p.k_hi) ? min(seq_end(p, ka), p.q_hi) : 0;
+  const int q_lo = max(k0, p.q_lo);
+  const int q_hi = min(seq_end(p, min(k0 + kBT - 1, T - 1)), p.q_hi);
   const int nt = (((q_hi - q_lo + kBT - 1) / kBT) + 1) & ~1;
   const int rb = qh * 32;
 
@@ -228,16 +231,17 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int 
     for (int e = 0; e < 16; ++e) acc[d][e] = 0.0f;
 
   auto issue = [&](char* tq, char* to, char* ts, int r0) {
-    issue_rows<D>(rq, tq, wave, lane, r0, T, head * D, ld_bytes);
-    issue_rows<D>(ro, to, wave, lane, r0, T, head * D, ldo_bytes);
+    issue_rows<D>(rq, tq, wave, lane, r0, p.q_hi, head * D, ld_bytes);
+    issue_rows<D>(ro, to, wave, lane, r0, p.q_hi, head * D, ldo_bytes);
     // waves 0/2 copy lse, 1/3 copy D (the pairs write identical bytes)
-    issue_stat((wave & 1) ? rd : rl, ts + (wave & 1) * 1024, lane, head, r0, T);
+    issue_stat((wave & 1) ? rd : rl, ts + (wave & 1) * 1024, lane, head, r0, T, p.q_hi);
   };
 
   auto compute = [&](const char* tq, const char* to, const char* ts, int r0) {
     const int qa = r0 + rb;  // first query row of this wave's half
     // wave-uniform skip: no query of the half sees a key of this wave
-    if (qa >= T || ka >= T || min(qa + 31, T - 1) < ka || ka_last < seq_start(p, min(qa, T - 1)))
+    if (qa >= p.q_hi || ka >= p.k_hi || min(qa + 31, p.q_hi - 1) < ka ||
+        ka_last < seq_start(p, min(qa, T - 1)))
       return;
     f32x16 s_acc, p_acc;
 #pragma unroll
@@ -354,6 +358,12 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int 
           const int e = 4 * a + c;
           w[c] = (acc[d][e] + park[(d * 16 + e) * 64 + lane]) * sc;
         }
+        if (p.accumulate) {
+          float o[4];
+          load4(out + 32 * d + 8 * a + 4 * g, o);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) w[c] += o[c];
+        }
         store4(out + 32 * d + 8 * a + 4 * g, w);
       }
   }
@@ -365,7 +375,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
                                          char* sk1, char* sv0, char* sv1) {
   constexpr int KS = D / 16, DB = D / 32;
   const int T = p.T;
-  const int q0 = qblk * kBT;
+  const int q0 = p.q_lo + qblk * kBT;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -373,13 +383,13 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
   const int lq = lane & 31, g = lane >> 5;
   const int qa = q0 + qg * 32;
   const int qi = qa + lq;
-  const bool qvalid = qi < T;
-  const int qstart = seq_start(p, min(qi, T - 1));
-  const int wq_last = min(qa + 31, T - 1);
-  const int w_start_lo = seq_start(p, min(qa, T - 1));
-  const int w_start_hi = seq_start(p, wq_last);
-  const int kv_lo = seq_start(p, min(q0, T - 1));
-  const int kv_hi = min(T, q0 + kBT);
+  const bool qvalid = qi < p.q_hi;
+  const int qstart = max(seq_start(p, min(qi, T - 1)), p.k_lo);
+  const int wq_last = min(qa + 31, p.q_hi - 1);
+  const int w_start_lo = max(seq_start(p, min(qa, T - 1)), p.k_lo);
+  const int w_start_hi = max(seq_start(p, wq_last), p.k_lo);
+  const int kv_lo = max(seq_start(p, min(q0, T - 1)), p.k_lo);
+  const int kv_hi = min(p.k_hi, q0 + kBT);
   const int nt = (((kv_hi - kv_lo + kBT - 1) / kBT) + 1) & ~1;
 
   const uint32_t ld_bytes = static_cast<uint32_t>(p.ld) * 2;
@@ -409,13 +419,13 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
     for (int e = 0; e < 16; ++e) dq[d][e] = 0.0f;
 
   auto issue = [&](char* tk, char* tv, int k0) {
-    issue_rows<D>(rs, tk, wave, lane, k0, T, p.hl + head * D, ld_bytes);
-    issue_rows<D>(rs, tv, wave, lane, k0, T, 2 * p.hl + head * D, ld_bytes);
+    issue_rows<D>(rs, tk, wave, lane, k0, p.k_hi, p.hl + head * D, ld_bytes);
+    issue_rows<D>(rs, tv, wave, lane, k0, p.k_hi, 2 * p.hl + head * D, ld_bytes);
   };
 
   auto compute = [&](const char* tk, const char* tv, int j0) {
     const int ja = j0 + kh * 32;
-    if (qa >= T || ja > wq_last || ja + 31 < w_start_lo) return;
+    if (qa >= p.q_hi || ja > wq_last || ja + 31 < w_start_lo) return;
     const int rb = kh * 32;
     f32x16 s_acc, p_acc;
 #pragma unroll
@@ -435,13 +445,15 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
       window_schedule<2 * KS>();
     }
     // Rows: key ja + 8 (e/4) + 4 g + e%4; column: query qi.
-    const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
+    // keys past the key range (the next chunk's, or past T) are masked too
+    const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < p.q_hi) &&
+                      (ja + 31 < p.k_hi);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[e], p.scale_log2, -lse2));
       if (!full) {
         const int j = ja + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (!(qvalid && j <= qi && j >= qstart)) pe = 0.0f;
+        if (!(qvalid && j <= qi && j >= qstart && j < p.k_hi)) pe = 0.0f;
       }
       p_acc[e] = pe * (p_acc[e] - dlt);
     }
@@ -495,6 +507,12 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
           const int e = 4 * a + c;
           v[c] = (dq[d][e] + park[(d * 16 + e) * 64 + lane]) * p.scale;
         }
+        if (p.accumulate) {
+          float o[4];
+          load4(out + 32 * d + 8 * a + 4 * g, o);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] += o[c];
+        }
         store4(out + 32 * d + 8 * a + 4 * g, v);
       }
   }
@@ -544,7 +562,15 @@ hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.T = static_cast<int>(a.T);
   p.seq_len = a.seq_len;
   p.heads = a.heads;
-  p.nblk = static_cast<int>((a.T + kBT - 1) / kBT);
+  p.q_lo = static_cast<int>(a.q_lo);
+  p.q_hi = static_cast<int>(a.q_hi < 0 ? a.T : a.q_hi);
+  p.k_lo = static_cast<int>(a.k_lo);
+  p.k_hi = static_cast<int>(a.k_hi < 0 ? a.T : a.k_hi);
+  p.accumulate = a.accumulate ? 1 : 0;
+  // one rank (and so one dK/dV and one dQ block) per 64 rows; the two
+  // ranges have equal lengths (whole sequence, or equal chunks)
+  p.nblk = (p.q_hi - p.q_lo + kBT - 1) / kBT;
+  if (p.nblk <= 0) return hipSuccess;
   p.scale = 1.0f / sqrtf(static_cast<float>(a.head_dim));
   p.scale_log2 = p.scale * kLog2e;
   const int64_t qb = a.T * p.ld * 2, ob = a.T * p.hl * 2, sb = a.T * a.heads * 4;

@@ -60,6 +60,7 @@ struct FwdParams {
   const int32_t* cu;
   int n_seqs;
   int T, seq_len, heads, nqb;
+  int q_lo, q_hi, k_lo, k_hi;  // query and key row ranges (absolute)
   float scale_log2;
   uint32_t qkv_bytes;
 };
@@ -121,7 +122,7 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
   const int item = blockIdx.x;
   const int head = item % p.heads;
   const int qblk = p.nqb - 1 - item / p.heads;
-  const int q0 = qblk * kFQ;
+  const int q0 = p.q_lo + qblk * kFQ;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,13 +130,15 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
   const int lq = lane & 31, g = lane >> 5;
   const int qa = q0 + qg * 32;            // first query of this wave
   const int qi = qa + lq;                 // this lane's query
-  const bool qvalid = qi < T;
-  const int qstart = seq_start(p, min(qi, T - 1));
-  const int wq_last = min(qa + 31, T - 1);
-  const int w_start_lo = seq_start(p, min(qa, T - 1));
-  const int w_start_hi = seq_start(p, wq_last);
-  const int kv_lo = seq_start(p, min(q0, T - 1));
-  const int kv_hi = min(T, q0 + kFQ);
+  const bool qvalid = qi < p.q_hi;
+  // keys visible to a query: from the start of its sequence (and of the
+  // key range) up to itself
+  const int qstart = max(seq_start(p, min(qi, T - 1)), p.k_lo);
+  const int wq_last = min(qa + 31, p.q_hi - 1);
+  const int w_start_lo = max(seq_start(p, min(qa, T - 1)), p.k_lo);
+  const int w_start_hi = max(seq_start(p, wq_last), p.k_lo);
+  const int kv_lo = max(seq_start(p, min(q0, T - 1)), p.k_lo);
+  const int kv_hi = min(p.k_hi, q0 + kFQ);
   const int nt = (((kv_hi - kv_lo + kFK - 1) / kFK) + 1) & ~1;
 
   const uint32_t ld_bytes = static_cast<uint32_t>(p.ld) * 2;
@@ -162,13 +165,17 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
     for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
   float m = -INFINITY, l = 0.0f;
 
-  auto issue_k = [&](char* tk, int k0) { issue_kv<D, false>(rs, tk, wave, lane, k0, T, kcol, ld_bytes); };
-  auto issue_v = [&](char* tv, int k0) { issue_kv<D, true>(rs, tv, wave, lane, k0, T, vcol, ld_bytes); };
+  auto issue_k = [&](char* tk, int k0) {
+    issue_kv<D, false>(rs, tk, wave, lane, k0, p.k_hi, kcol, ld_bytes);
+  };
+  auto issue_v = [&](char* tv, int k0) {
+    issue_kv<D, true>(rs, tv, wave, lane, k0, p.k_hi, vcol, ld_bytes);
+  };
   // Wave-uniform: does any (query, key) pair of this wave's part of the tile
   // at key j0 exist?
   auto visible = [&](int j0) {
     const int ja = j0 + kh * 32;
-    return !(qa >= T || ja > wq_last || ja + 31 < w_start_lo);
+    return !(qa >= p.q_hi || ja > wq_last || ja + 31 < w_start_lo);
   };
 
   // S^T of this wave's part of the tile at key j0 (K rows from LDS).
@@ -211,12 +218,15 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
         vfr[t][d] = cat_bf16x8(lo, hi);
       }
     }
-    const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < T);
+    // keys past the key range (the next chunk's, or past T) are masked
+    // too: they may precede the query
+    const bool full = (ja + 31 <= qa) && (ja >= w_start_hi) && (qa + 31 < p.q_hi) &&
+                      (ja + 31 < p.k_hi);
     if (!full) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = ja + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (!(qvalid && j <= qi && j >= qstart)) sacc[e] = -INFINITY;
+        if (!(qvalid && j <= qi && j >= qstart && j < p.k_hi)) sacc[e] = -INFINITY;
       }
     }
     float mt = sacc[0];
@@ -373,7 +383,12 @@ hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.T = static_cast<int>(a.T);
   p.seq_len = a.seq_len;
   p.heads = a.heads;
-  p.nqb = static_cast<int>((a.T + kFQ - 1) / kFQ);
+  p.q_lo = static_cast<int>(a.q_lo);
+  p.q_hi = static_cast<int>(a.q_hi < 0 ? a.T : a.q_hi);
+  p.k_lo = static_cast<int>(a.k_lo);
+  p.k_hi = static_cast<int>(a.k_hi < 0 ? a.T : a.k_hi);
+  p.nqb = (p.q_hi - p.q_lo + kFQ - 1) / kFQ;
+  if (p.nqb <= 0) return hipSuccess;
   p.scale_log2 = kLog2e / sqrtf(static_cast<float>(a.head_dim));
   const int64_t bytes = a.T * p.ld * 2;
   if (bytes >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;

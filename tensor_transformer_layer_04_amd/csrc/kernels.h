@@ -74,11 +74,20 @@ struct AttnDesc {
   const void* dctx; void* dqkv; float* delta;  // backward
   const int32_t* cu_seqlens; int n_seqs;        // nullable -> fixed seq_len
   int64_t T; int seq_len; int heads; int head_dim;
+  // Query rows [q_lo, q_hi) attend to key rows [k_lo, k_hi) (absolute
+  // positions, causal mask unchanged); a whole-sequence call uses 0..T for
+  // both.  With accumulate, the backward adds into dqkv instead of storing.
+  int64_t q_lo = 0, q_hi = -1, k_lo = 0, k_hi = -1;
+  bool accumulate = false;
 };
 hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t stream);
 hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t stream);
 hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t stream);
 hipError_t attn_bwd(bool bf16, const AttnDesc& a, hipStream_t stream);
+// Merge a partial attention result into an accumulated one over rows
+// [row_lo, row_hi): lse = log(e^lse_acc + e^lse_part), ctx = weighted mean.
+hipError_t attn_merge(const AttnDesc& acc, const void* ctx_part, const float* lse_part,
+                      int64_t row_lo, int64_t row_hi, hipStream_t stream);
 
 // ------------------------------------------------------------ vocab CE
 hipError_t ce_stats(const float* logits, const int32_t* targets, float* m, float* s, float* zt,

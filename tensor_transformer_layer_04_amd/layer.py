@@ -163,6 +163,16 @@ class TPLayer(_Probed):
         self.swiglu = bool(getattr(cfg, "swiglu", False))
         self.k_fc1 = mtp.MTP_FC1_SWIGLU if self.swiglu else mtp.MTP_FC1
         self.k_fc2 = mtp.MTP_FC2_SWIGLU if self.swiglu else mtp.MTP_FC2
+        # Context parallelism: the attention of each rank's heads runs over
+        # cp chunks of the sequence, block pair by block pair (the keys of a
+        # chunk and of every earlier chunk), the partials merged through
+        # their log-sum-exp; bf16, one fixed-length sequence.
+        self.cp = int(getattr(cfg, "context_parallel", 1))
+        if self.cp > 1:
+            if cfg.dtype != "bf16" or cfg.varlen_tokens or cfg.micro_batch != 1:
+                raise ValueError("context parallelism needs one bf16 sequence (micro_batch 1)")
+            if self.T % self.cp:
+                raise ValueError(f"context parallelism needs T ({self.T}) divisible by {self.cp}")
         self.sp = bool(getattr(cfg, "sequence_parallel", False)) and cfg.tp > 1
         if self.sp:
             # Each rank's row block must start on a 16-byte boundary of the
@@ -198,6 +208,9 @@ class TPLayer(_Probed):
                 "du": E(T, ul), "dln2": E(T, h), "dctx": E(T, hl), "dqkv": E(T, 3 * hl),
                 "dln1": E(T, h),
             }
+            if self.cp > 1:  # one partial attention result (ctx, lse) to merge
+                self.a[r]["ctx_p"] = E(T, hl)
+                self.a[r]["lse_p"] = E(al, T, d=torch.float32)
         self.dy1, self.dx = E(T, h), E(T, h)
         f32 = torch.float32
         self.grads: Dict[int, Dict[str, torch.Tensor]] = {}
@@ -254,7 +267,10 @@ class TPLayer(_Probed):
                 mtp.mtp_col_linear_fwd(d, mtp.MTP_QKV, self.ln1, w["wqkv"], w["bqkv"], a["qkv"],
                                        None)
             with T("attn_fwd"):
-                mtp.mtp_attn_fwd(d, a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
+                if self.cp > 1:
+                    self._attn_fwd_cp(d, a)
+                else:
+                    mtp.mtp_attn_fwd(d, a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
             with T("proj_fwd"):
                 mtp.mtp_row_linear_fwd(d, mtp.MTP_PROJ, a["ctx"], w["wo"], a["p"])
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
@@ -369,8 +385,11 @@ class TPLayer(_Probed):
                                            w["wo"], None, None, None, self.rgrads["dbo"],
                                            int(r != self.ranks[0]), wss, wsb)
             with T("attn_bwd"):
-                mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
-                                 self.n_seqs, ws, wsb)
+                if self.cp > 1:
+                    self._attn_bwd_cp(d, a, ws, wsb)
+                else:
+                    mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"],
+                                     self.cu, self.n_seqs, ws, wsb)
             with T("qkv_dgrad"):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], a["dln1"],
                                        None, None, 0, ws, wsb)
@@ -396,6 +415,37 @@ class TPLayer(_Probed):
         if side is not None:
             main.wait_stream(side)
         return self.dx
+
+    # ------------------------------------------------ context parallelism
+    def _chunks(self):
+        L = self.T // self.cp
+        return [(c * L, (c + 1) * L) for c in range(self.cp)]
+
+    def _attn_fwd_cp(self, d, a):
+        """Chunk j (a context-parallel rank) attends to its own keys (the
+        diagonal block), then, ring step by ring step, to the keys of chunks
+        j-1, ..., 0; each partial is merged into (ctx, lse) of j's rows."""
+        ch = self._chunks()
+        for j, (q0, q1) in enumerate(ch):
+            mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, q0, q1, a["ctx"], a["lse"])
+            for i in range(j - 1, -1, -1):
+                k0, k1 = ch[i]
+                mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, k0, k1, a["ctx_p"], a["lse_p"])
+                mtp.mtp_attn_merge(d, a["ctx"], a["lse"], a["ctx_p"], a["lse_p"], q0, q1)
+
+    def _attn_bwd_cp(self, d, a, ws, wsb):
+        """Backward of every block pair with the merged ctx and lse: the
+        diagonal pairs first (they write each chunk's dQ rows and dK/dV rows),
+        then the pairs below the diagonal, which add into them."""
+        ch = self._chunks()
+        for (q0, q1) in ch:
+            mtp.mtp_attn_bwd_block(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], q0, q1,
+                                   q0, q1, 0, ws, wsb)
+        for j, (q0, q1) in enumerate(ch):
+            for i in range(j - 1, -1, -1):
+                k0, k1 = ch[i]
+                mtp.mtp_attn_bwd_block(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"],
+                                       q0, q1, k0, k1, 1, ws, wsb)
 
     def partials(self) -> Dict[str, List[torch.Tensor]]:
         """This object's partial outputs, to be passed as ``external`` to a

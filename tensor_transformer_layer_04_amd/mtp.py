@@ -55,6 +55,10 @@ _SIGS = {
                            + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
     "mtp_attn_fwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int32, _VP]),
     "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
+    "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4 + [_VP, _VP, _VP]),
+    "mtp_attn_merge": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int64] * 2 + [_VP]),
+    "mtp_attn_bwd_block": (ctypes.c_int, [_VP] + [_VP] * 5 + [ctypes.c_int64] * 4
+                           + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
     "mtp_partial_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
     "mtp_partial_sum_layernorm": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8 + [_VP]),
     "mtp_layernorm_bwd_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8
@@ -178,6 +182,23 @@ def mtp_attn_bwd(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, ws, ws_byt
     return _call("mtp_attn_bwd", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
                  _addr(dctx), _addr(dqkv), _addr(cu_seqlens), int(n_seqs), _addr(ws), ws_bytes,
                  _stream(stream))
+
+
+def mtp_attn_fwd_block(desc, qkv, q_lo, q_hi, k_lo, k_hi, ctx, lse, stream=None):
+    return _call("mtp_attn_fwd_block", ctypes.byref(desc), _addr(qkv), q_lo, q_hi, k_lo, k_hi,
+                 _addr(ctx), _addr(lse), _stream(stream))
+
+
+def mtp_attn_merge(desc, ctx, lse, ctx_part, lse_part, row_lo, row_hi, stream=None):
+    return _call("mtp_attn_merge", ctypes.byref(desc), _addr(ctx), _addr(lse), _addr(ctx_part),
+                 _addr(lse_part), row_lo, row_hi, _stream(stream))
+
+
+def mtp_attn_bwd_block(desc, qkv, ctx, lse, dctx, dqkv, q_lo, q_hi, k_lo, k_hi, accumulate, ws,
+                       ws_bytes, stream=None):
+    return _call("mtp_attn_bwd_block", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
+                 _addr(dctx), _addr(dqkv), q_lo, q_hi, k_lo, k_hi, accumulate, _addr(ws),
+                 ws_bytes, _stream(stream))
 
 
 def mtp_partial_sum(desc, partials, bias, residual, out, stream=None):

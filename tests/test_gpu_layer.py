@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_tp2", "small_f32_tp4", "small_bf16_tp2", "small_bf16_d64_tp4", "small_bf16_mb2",
          "small_varlen_tp1", "one_token_bf16", "small_bf16_tp2_sp", "small_f32_tp4_sp",
-         "tiny_swiglu_tp2", "small_bf16_swiglu_tp2", "small_bf16_swiglu_sp_tp4"]
+         "tiny_swiglu_tp2", "small_bf16_swiglu_tp2", "small_bf16_swiglu_sp_tp4",
+         "small_bf16_tp2_cp2", "small_bf16_d64_cp4"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -55,7 +56,7 @@ def test_layer_parity_7b_tp2_full():
     log(f"  worst: {fmt_report(report)}")
 
 
-@pytest.mark.parametrize("name", ["7b_tp2_sp", "7b_tp2_swiglu"])
+@pytest.mark.parametrize("name", ["7b_tp2_sp", "7b_tp2_swiglu", "7b_tp2_cp2"])
 def test_layer_parity_7b_variants_full(name):
     """The 7B-style TP=2 layer with sequence parallelism and with the SwiGLU
     FFN: both shards at full size against the full oracle."""
