@@ -352,3 +352,48 @@ def test_vocab_ce_zero_logits_golden():
     loss, _, _ = oracle.vocab_ce_forward(np.ones((T, h)), np.zeros((V, h)), np.array([0, 7, V - 1]))
     assert abs(loss - gold["zero_logit_cross_entropy"]["value"]) < 1e-12
     assert abs(loss - 17 * math.log(2)) < 1e-12
+
+
+# ------------------------------------------------------------------- FP8
+def test_e4m3_round_matches_torch_and_format():
+    """E4M3 rounding against torch's float8_e4m3fn conversion (a library
+    special case) on a grid with every tie, subnormal and binade edge, and
+    the format's closed forms."""
+    from oracle import fp8
+    codes = np.arange(256)
+    vals = fp8.e4m3_decode(codes)
+    finite = np.sort(np.unique(vals[np.isfinite(vals)]))
+    assert finite.max() == 448.0 and finite.min() == -448.0
+    assert np.min(finite[finite > 0]) == 2.0 ** -9
+    mids = (finite[1:] + finite[:-1]) / 2          # every tie between neighbours
+    r = rng(21)
+    grid = np.concatenate([finite, mids, r.uniform(-448, 448, 4000),
+                           r.uniform(-0.02, 0.02, 4000)])
+    ref = torch.tensor(grid, dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.e4m3_round(grid)
+    assert np.array_equal(got, ref)
+    # encode / decode are inverse on every finite value
+    enc = fp8.e4m3_encode(finite)
+    assert np.array_equal(fp8.e4m3_decode(enc), finite)
+    assert fp8.e4m3_encode(np.array([448.0]))[0] == 0x7E
+    assert fp8.e4m3_encode(np.array([-2.0 ** -9]))[0] == 0x81
+
+
+def test_quantize_per_tensor_scale_and_linear():
+    from oracle import fp8
+    r = rng(22)
+    x = r.normal(size=(37, 64)).astype(np.float32) * 3.0
+    q, s = fp8.quantize_per_tensor(x)
+    assert s == np.float32(np.max(np.abs(x)) / np.float32(448.0))
+    assert np.max(np.abs(q)) == 448.0                  # amax maps to the largest value
+    # dequantized values are within half an E4M3 step (relative 2^-4) of x
+    big = np.abs(x) > 2.0 ** -6 * s
+    assert np.all(np.abs(q * s - x)[big] <= np.abs(x)[big] * 2.0 ** -4 * 1.0001)
+    qz, sz = fp8.quantize_per_tensor(np.zeros((3, 8), np.float32))
+    assert sz == 1.0 and not qz.any()
+    w = r.normal(size=(9, 64)).astype(np.float32)
+    qw, sw = fp8.quantize_per_tensor(w)
+    y = fp8.fp8_linear(q, s, qw, sw)
+    brute = np.array([[sum(q[i, k] * qw[j, k] for k in range(64)) for j in range(9)]
+                      for i in range(37)]) * (float(s) * float(sw))
+    assert np.max(np.abs(y - brute)) <= 1e-12 * np.max(np.abs(brute))
