@@ -239,6 +239,33 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                  const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* ---------------------------------------------------------- FP8 GEMMs
+ * Forward linear maps with E4M3 operands and one fp32 scale per tensor (FP8
+ * among the training precisions of page "Megatron-LM / Megatron Core README
+ * digest", §2; reading: OCP E4M3 without infinities, s = amax / 448), on
+ * the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4).  bf16 shards
+ * only, else MTP_ERR_UNSUPPORTED.
+ *
+ * mtp_quantize_fp8: x holds n values of the shard dtype, n % 8 == 0; scale
+ *   points to 2 fp32 values in device memory: scale[1] receives amax = max
+ *   |x|, scale[0] s = amax / 448 (1 when amax is 0); q[i] receives the E4M3
+ *   code of round-to-nearest-even(clamp(x[i] / s, -448, 448)), the quotient
+ *   correctly rounded in fp32.                                               */
+int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8_t* q,
+                     float* scale, void* stream);
+
+/* mtp_linear_fwd_fp8: y = (x8 w8^T) * x_scale[0] * w_scale[0] (+ b), with x8,
+ *   w8 the codes and scales of mtp_quantize_fp8 of the layouts of
+ *   mtp_col_linear_fwd / mtp_row_linear_fwd: kind MTP_QKV (x8 [T,h], w8
+ *   [3h_l,h], b nullable, y [T,3h_l]), MTP_FC1 (w8 [f_l,h]; preact [T,f_l]
+ *   receives u, y GeLU_tanh(u)), MTP_PROJ (x8 [T,h_l], w8 [h,h_l], y the
+ *   partial [T,h], b NULL) or MTP_FC2 (x8 [T,f_l], w8 [h,f_l], b NULL).  y
+ *   and preact in the shard dtype; the inner width must be a multiple of 16
+ *   (else MTP_ERR_UNSUPPORTED).                                              */
+int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
+                       const float* x_scale, const uint8_t* w8, const float* w_scale,
+                       const void* b, void* y, void* preact, void* stream);
+
 /* ------------------------------------------ context-parallel attention
  * The sequence split into chunks whose attention runs block pair by block
  * pair, each partial result merged through its log-sum-exp (context

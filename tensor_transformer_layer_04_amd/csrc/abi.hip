@@ -385,6 +385,50 @@ int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* 
   return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));
 }
 
+int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8_t* q,
+                     float* scale, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  if (n < 0 || (n & 7)) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(x) || !ok_ptr(q) || !ok_ptr(scale)) return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::quantize_fp8(x, n, q, scale, static_cast<hipStream_t>(stream)));
+}
+int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
+                       const float* x_scale, const uint8_t* w8, const float* w_scale,
+                       const void* b, void* y, void* preact, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  // column-parallel QKV / FC1 (GeLU) or row-parallel PROJ / FC2 (partial)
+  int64_t n = 0, k = 0;
+  switch (kind) {
+    case MTP_QKV: n = 3LL * s.hl; k = s.h; break;
+    case MTP_FC1: n = s.fl; k = s.h; break;
+    case MTP_PROJ: n = s.h; k = s.hl; break;
+    case MTP_FC2: n = s.h; k = s.fl; break;
+    default: return MTP_ERR_INVALID_ARG;
+  }
+  if (!ok_ptr(x8) || !ok_ptr(x_scale) || !ok_ptr(w8) || !ok_ptr(w_scale) || !ok_opt(b) ||
+      !ok_ptr(y))
+    return MTP_ERR_INVALID_ARG;
+  if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
+  if ((kind == MTP_PROJ || kind == MTP_FC2) && b != nullptr) return MTP_ERR_INVALID_ARG;
+  if (k % 16 != 0) return MTP_ERR_UNSUPPORTED;
+  GemmDesc g{};
+  g.A = x8; g.lda = k; g.a_kmajor = true;
+  g.B = w8; g.ldb = k; g.b_kmajor = true;
+  g.M = static_cast<int>(s.T); g.N = static_cast<int>(n); g.K = static_cast<int>(k);
+  g.C = y; g.ldc = n; g.bias = b;
+  g.aux = preact; g.ld_aux = n;
+  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : mtp::kEpiStore;
+  g.tile = tile_override();
+  g.fp8 = true; g.scale_a = x_scale; g.scale_b = w_scale;
+  return hip_status(mtp::gemm_bf16(g, static_cast<hipStream_t>(stream)));
+}
+
 int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials, int32_t n_partials,
                     const void* bias, const void* residual, void* out, void* stream) {
   Shard s;

@@ -32,6 +32,8 @@
 //    consecutive n of one row m (8- or 16-byte stores in the epilogue).
 //  * Tiles are ordered so that the workgroups of one XCD (dispatched
 //    round-robin over the 8 XCDs) share operand panels in their L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -52,7 +54,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kGroupM = 8;
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 struct GemmParams {
+  const float* scale_a; const float* scale_b;  // FP8 kernels: per-tensor scales
   const bf16_t* A; int64_t lda;
   const bf16_t* B; int64_t ldb;
   int M, N, K;
@@ -146,6 +151,17 @@ __device__ __forceinline__ void lds_barrier() {
 // MFMA operand (8 consecutive k of one row) from a k-major LDS tile.
 __device__ __forceinline__ bf16x8 frag_k(const char* t, int row, int c) {
   return *reinterpret_cast<const bf16x8*>(t + row * 128 + ((c ^ swz_k(row)) << 4));
+}
+
+// FP8 MFMA operand (32 bytes: 32 consecutive k of one row) of k-step s
+// (64 k) of a k-major LDS tile whose rows hold 128 one-byte elements: lane
+// group g takes chunks 4s + 2g and 4s + 2g + 1.  Any split of the 64 k over
+// the lanes serves, as long as both operands use the same one.
+__device__ __forceinline__ i32x8 frag_k8(const char* t, int row, int s, int g) {
+  const bf16x8 lo = frag_k(t, row, 4 * s + 2 * g);
+  const bf16x8 hi = frag_k(t, row, 4 * s + 2 * g + 1);
+  const bf16x8 v[2] = {lo, hi};
+  return __builtin_bit_cast(i32x8, v);
 }
 
 // MFMA operand from an m/n-major LDS tile of R columns: lane l gets
@@ -277,9 +293,14 @@ __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, con
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
+// F8: operands are E4M3 bytes staged exactly like bf16 pairs (the host
+// passes K and the leading dimensions in 2-byte units), multiplied by
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) in two 64-k steps per
+// 128-byte k-tile; the epilogue applies the two per-tensor scales.
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false>
 __global__ void __launch_bounds__(WGM * WGN * 64, (WGM * WGN + 3) / 4)
 gemm_bf16_kernel(GemmParams p) {
+  static_assert(!F8 || (AK && BKM), "FP8 operands: forward layout only");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -325,20 +346,35 @@ gemm_bf16_kernel(GemmParams p) {
     issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
     issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
   };
-  // Operand fragments of one k-step (16 k): FM A blocks and FN B blocks.
-  struct Frags { bf16x8 a[FM], b[FN]; };
+  // Operand fragments of one k-step (16 k, or 64 with F8): FM A blocks and
+  // FN B blocks.
+  using FragT = std::conditional_t<F8, i32x8, bf16x8>;
+  struct Frags { FragT a[FM], b[FN]; };
+  auto mma = [&](const FragT& b, const FragT& a, const f32x16& c) {
+    if constexpr (F8)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+  };
   auto load_frags = [&](const char* ta, const char* tb, int kk, Frags& f) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      f.a[i] = AK ? frag_k(ta, wm * WTM + i * 32 + lrow, kk * 2 + lk)
-                  : frag_m<BM>(ta, wm * WTM + i * 32, kk, lane);
+      for (int i = 0; i < FM; ++i) f.a[i] = frag_k8(ta, wm * WTM + i * 32 + lrow, kk, lk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      f.b[j] = BKM ? frag_k(tb, wn * WTN + j * 32 + lrow, kk * 2 + lk)
-                   : frag_m<BN>(tb, wn * WTN + j * 32, kk, lane);
+      for (int j = 0; j < FN; ++j) f.b[j] = frag_k8(tb, wn * WTN + j * 32 + lrow, kk, lk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        f.a[i] = AK ? frag_k(ta, wm * WTM + i * 32 + lrow, kk * 2 + lk)
+                    : frag_m<BM>(ta, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        f.b[j] = BKM ? frag_k(tb, wn * WTN + j * 32 + lrow, kk * 2 + lk)
+                     : frag_m<BN>(tb, wn * WTN + j * 32, kk, lane);
+    }
   };
   // LDS reads per k-step (transpose reads come in pairs).
-  constexpr int kReads = FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
+  constexpr int kReads = F8 ? 2 * (FM + FN) : FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
   constexpr int kPerMfma = (kReads + FM * FN - 1) / (FM * FN);
   // MFMAs of one k-step with the fragment reads of the next step spread
   // between them, so LDS latency hides behind the matrix pipeline.
@@ -349,7 +385,7 @@ gemm_bf16_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mma(f.b[j], f.a[i], acc[i][j]);
     if (prefetch) {
 #ifdef MTP_READS_FIRST
       __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
@@ -404,7 +440,7 @@ gemm_bf16_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mma(f.b[j], f.a[i], acc[i][j]);
 #pragma unroll
     for (int t = 0; t < FM * FN; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -443,8 +479,10 @@ gemm_bf16_kernel(GemmParams p) {
       step_c(f0, ca, cb, 1, f1, [&] { copy_a(sa(IntTag<J + 2>{}), (kt + 2) * kBK); },
              IntTag<kCopiesA>{});
     }
-    step(f1, true, ca, cb, 2, f0);
-    step(f0, true, ca, cb, 3, f1);
+    if constexpr (!F8) {  // bf16: four 16-k steps per tile, FP8: two 64-k steps
+      step(f1, true, ca, cb, 2, f0);
+      step(f0, true, ca, cb, 3, f1);
+    }
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(kInFlight) : "memory");
     lds_barrier();
     if constexpr (kSym) {
@@ -491,16 +529,21 @@ gemm_bf16_kernel(GemmParams p) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      epi_block<EPI>(p, stage, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
+      if constexpr (F8) {
+        const f32x16 v = acc[i][j] * (p.scale_a[0] * p.scale_b[0]);
+        epi_block<EPI>(p, stage, v, m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
+      } else {
+        epi_block<EPI>(p, stage, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
+      }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false>
 hipError_t launch_bf16(const GemmParams& p0, hipStream_t s) {
   GemmParams p = p0;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const int blocks = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKM, EPI>), dim3(blocks),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, F8>), dim3(blocks),
                      dim3(WGM * WGN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -560,6 +603,23 @@ hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
     case kTile256x192: return launch_bf16<256, 192, 4, 2, AK, BKM, EPI>(p, s);
     case kTile192x256: return launch_bf16<192, 256, 2, 4, AK, BKM, EPI>(p, s);
     default: return launch_bf16<256, 256, 2, 4, AK, BKM, EPI>(p, s);
+  }
+}
+
+// FP8 tiles: 128x256, 256x128 and 128x128 (the doubled fragments of the
+// larger tiles do not fit the registers of two waves per SIMD).
+int pick_tile_fp8(int M, int N) {
+  const int t = pick_tile(M, N);
+  if (t == kTile256x128 || t == kTile128x256 || t == kTile128x128) return t;
+  return M > N ? kTile256x128 : kTile128x256;
+}
+
+template <int EPI>
+hipError_t dispatch_fp8(const GemmParams& p, int tile, hipStream_t s) {
+  switch (tile) {
+    case kTile256x128: return launch_bf16<256, 128, 4, 2, true, true, EPI, true>(p, s);
+    case kTile128x128: return launch_bf16<128, 128, 2, 2, true, true, EPI, true>(p, s);
+    default: return launch_bf16<128, 256, 2, 4, true, true, EPI, true>(p, s);
   }
 }
 
@@ -643,6 +703,7 @@ int64_t operand_bytes(bool kmajor, int rows, int K, int64_t ld) {
 
 GemmParams to_params(const GemmDesc& g) {
   GemmParams p{};
+  p.scale_a = g.scale_a; p.scale_b = g.scale_b;
   p.A = static_cast<const bf16_t*>(g.A); p.lda = g.lda;
   p.B = static_cast<const bf16_t*>(g.B); p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
@@ -659,6 +720,22 @@ GemmParams to_params(const GemmDesc& g) {
 //   wgrad   (m-major, n-major):  F32, F32Acc
 hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (g.fp8) {
+    // bytes staged as bf16 pairs: K and the leading dimensions in 2-byte units
+    if (!g.a_kmajor || !g.b_kmajor || (g.K & 15) || (g.lda & 15) || (g.ldb & 15) || (g.N & 3) ||
+        !g.scale_a || !g.scale_b || (g.epi != kEpiStore && g.epi != kEpiGelu))
+      return hipErrorInvalidValue;
+    GemmDesc h = g;
+    h.K = g.K / 2; h.lda = g.lda / 2; h.ldb = g.ldb / 2;
+    GemmParams p = to_params(h);
+    const int64_t ab = operand_bytes(true, h.M, h.K, h.lda);
+    const int64_t bb = operand_bytes(true, h.N, h.K, h.ldb);
+    if (ab >= static_cast<int64_t>(kOOB) || bb >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;
+    p.a_bytes = static_cast<uint32_t>(ab);
+    p.b_bytes = static_cast<uint32_t>(bb);
+    const int tile = pick_tile_fp8(g.M, g.N);
+    return g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu>(p, tile, s) : dispatch_fp8<kEpiStore>(p, tile, s);
+  }
   GemmParams p = to_params(g);
   // Buffer offsets are 32-bit and the edge handling needs every valid byte
   // offset below kOOB; the 16-byte chunks need 8-aligned rows.

@@ -33,10 +33,20 @@ struct GemmDesc {
   void* aux; int64_t ld_aux;
   int epi;
   int tile;            // tile-shape override for tuning (-1: heuristic)
+  // FP8 (E4M3) operands, forward layout only: A and B hold one byte per
+  // element and C = (A B^T) * scale_a[0] * scale_b[0] before the epilogue.
+  bool fp8 = false;
+  const float* scale_a = nullptr;
+  const float* scale_b = nullptr;
 };
 
 hipError_t gemm_bf16(const GemmDesc& g, hipStream_t stream);
 hipError_t gemm_f32(const GemmDesc& g, hipStream_t stream);
+
+// Per-tensor E4M3 quantization of n bf16 values (n % 8 == 0): scale[1]
+// receives amax, scale[0] s = amax / 448 (1 for a zero tensor), q the codes
+// of round-to-nearest-even(clamp(x / s, -448, 448)).
+hipError_t quantize_fp8(const void* x, int64_t n, uint8_t* q, float* scale, hipStream_t stream);
 
 // Column sums of a [rows, cols] matrix into fp32 out[cols] (= or +=).
 // ws must hold column_sum_ws_bytes(rows, cols) bytes.

@@ -3,6 +3,8 @@
 // and the vocab-parallel cross-entropy pieces.  All loads and stores are
 // 16-byte vectors of 8 consecutive elements along the contiguous axis;
 // every reduction accumulates in fp32 in a fixed order (deterministic).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -381,6 +383,65 @@ colsum_part_kernel(const T* __restrict__ x, int64_t rows, int64_t cols, int rpb,
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = red[0][tx * 8 + e] + red[1][tx * 8 + e] + red[2][tx * 8 + e] + red[3][tx * 8 + e];
     store8(part + static_cast<int64_t>(blockIdx.y) * cols + c, o);
+  }
+}
+
+// ------------------------------------------------------ FP8 quantization
+// Per-tensor E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities, largest finite value 448): s = amax / 448 in fp32, code =
+// round-to-nearest-even(clamp(x / s, -448, 448)), with the fp32 quotient
+// correctly rounded.  The rounding is done here from the format's
+// definition rather than by a conversion instruction, so that the codes are
+// those of that definition for every input.
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), kE4M3Max);
+  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xff) - 127;  // a > 0: floor(log2 a)
+  if (e < -6) {
+    // subnormal grid 2^-9 (and zero); 8 steps = 2^-6, which is code 0x08
+    return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+  }
+  // normal: a = m * 2^(e-3), m in [8, 16); rintf rounds half to even
+  const uint32_t m = static_cast<uint32_t>(rintf(a * __uint_as_float(static_cast<uint32_t>(127 + 3 - e) << 23)));
+  // m == 16 carries into the exponent: (e + 7) * 8 + 8 == (e + 8) * 8 + 0
+  return sign | (static_cast<uint32_t>(e + 7) * 8u + (m - 8u));
+}
+
+__global__ void __launch_bounds__(64) fp8_amax_init_kernel(float* scale) { scale[1] = 0.0f; }
+
+__global__ void __launch_bounds__(256) fp8_amax_kernel(const bf16_t* __restrict__ x, int64_t nvec,
+                                                       float* scale) {
+  float m = 0.0f;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+       v += static_cast<int64_t>(gridDim.x) * 256) {
+    float t[8];
+    load8(x + v * 8, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(t[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // non-negative floats order like their bit patterns
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(scale + 1), __float_as_uint(m));
+}
+
+__global__ void __launch_bounds__(256) fp8_quant_kernel(const bf16_t* __restrict__ x, int64_t nvec,
+                                                        uint8_t* __restrict__ q, float* scale) {
+  const float amax = scale[1];
+  const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+       v += static_cast<int64_t>(gridDim.x) * 256) {
+    float t[8];
+    load8(x + v * 8, t);
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = e4m3_code(t[e] / s);
+    const uint2 w = make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                               c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    *reinterpret_cast<uint2*>(q + v * 8) = w;
   }
 }
 
@@ -1057,6 +1118,20 @@ hipError_t ce_bwd(bool bf16, const float* logits, const int32_t* targets, const 
   else
     hipLaunchKernelGGL(ce_bwd_kernel<float>, g, dim3(256), 0, s, logits, targets, M, S, scale,
                        static_cast<float*>(dlogits), V_l, v0, bpr);
+  return hipGetLastError();
+}
+
+hipError_t quantize_fp8(const void* x, int64_t n, uint8_t* q, float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(fp8_amax_init_kernel, dim3(1), dim3(64), 0, s, scale);
+  if (n <= 0) {
+    hipLaunchKernelGGL(fp8_quant_kernel, dim3(1), dim3(256), 0, s, cptr<bf16_t>(x), int64_t{0}, q,
+                       scale);
+    return hipGetLastError();
+  }
+  const int64_t nvec = n / 8;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((nvec + 255) / 256, 2048));
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3(grid), dim3(256), 0, s, cptr<bf16_t>(x), nvec, scale);
+  hipLaunchKernelGGL(fp8_quant_kernel, dim3(grid), dim3(256), 0, s, cptr<bf16_t>(x), nvec, q, scale);
   return hipGetLastError();
 }
 

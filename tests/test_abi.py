@@ -21,7 +21,7 @@ GOLDEN = os.path.join(ROOT, "tests", "golden", "page_constants.json")
 def declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mtp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
