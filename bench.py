@@ -187,6 +187,77 @@ def prefix_cu(cu, P):
     return out if out[0] == 0 else [0] + out
 
 
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
+
+
+def fp8_gemm_probe(cfg, L, reps: int = 20) -> dict:
+    """The four forward GEMMs of the timed shard with E4M3 operands and
+    per-tensor scales, against the same calls in bf16, each call timed alone
+    (median of ``reps``) on the layer's own inputs: the FP8 GEMM by itself,
+    and with the quantization of its activation (the weights' codes are
+    made once, as a training step would after its update)."""
+    import torch
+    from tensor_transformer_layer_04_amd import mtp
+    r = L.ranks[0]
+    d, w, a = L.descs[r], L.w[r], L.a[r]
+    T, h = cfg.tokens, cfg.hidden
+    hl, fl = h // cfg.tp, cfg.ffn // cfg.tp
+
+    def q8(t):
+        q = torch.empty(t.numel(), dtype=torch.uint8, device=t.device)
+        s = torch.empty(2, dtype=torch.float32, device=t.device)
+        mtp.mtp_quantize_fp8(d, t, t.numel(), q, s)
+        return q, s
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)[reps // 2]
+
+    out_y = {"qkv": a["qkv"], "proj": a["p"], "fc1": a["g"], "fc2": a["q"]}
+    cases = {  # name: (kind, activation, weight, bias, flop)
+        "qkv": (mtp.MTP_QKV, L.ln1, w["wqkv"], w["bqkv"], 2 * T * 3 * hl * h),
+        "proj": (mtp.MTP_PROJ, a["ctx"], w["wo"], None, 2 * T * hl * h),
+        "fc1": (mtp.MTP_FC1, L.ln2, w["w1"], w["b1"], 2 * T * fl * h),
+        "fc2": (mtp.MTP_FC2, a["g"], w["w2"], None, 2 * T * fl * h),
+    }
+    res, tot = {}, {"bf16": 0.0, "fp8": 0.0, "fp8_with_quant": 0.0, "flop": 0}
+    for name, (kind, x, wt, b, flop) in cases.items():
+        y, u = out_y[name], (a["u"] if kind == mtp.MTP_FC1 else None)
+        qw, sw = q8(wt)
+        qx, sx = q8(x)
+        if kind in (mtp.MTP_QKV, mtp.MTP_FC1):
+            bf = lambda: mtp.mtp_col_linear_fwd(d, kind, x, wt, b, y, u)
+        else:
+            bf = lambda: mtp.mtp_row_linear_fwd(d, kind, x, wt, y)
+        f8 = lambda: mtp.mtp_linear_fwd_fp8(d, kind, qx, sx, qw, sw, b, y, u)
+
+        def f8q():
+            mtp.mtp_quantize_fp8(d, x, x.numel(), qx, sx)
+            f8()
+        t_bf, t_f8, t_f8q = timed(bf), timed(f8), timed(f8q)
+        res[name] = {"bf16_us": round(t_bf, 1), "fp8_us": round(t_f8, 1),
+                     "fp8_with_quant_us": round(t_f8q, 1),
+                     "fp8_tflops": round(flop / t_f8 / 1e6, 1)}
+        tot["bf16"] += t_bf
+        tot["fp8"] += t_f8
+        tot["fp8_with_quant"] += t_f8q
+        tot["flop"] += flop
+    ach = tot["flop"] / tot["fp8"] / 1e6
+    return {"per_gemm": res, "bf16_us": round(tot["bf16"], 1), "fp8_us": round(tot["fp8"], 1),
+            "fp8_with_quant_us": round(tot["fp8_with_quant"], 1),
+            "roofline": {"kernel": "gemm_bf16_kernel<..., F8> (E4M3 operands, forward layout)",
+                         "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4)}}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +451,9 @@ def main(argv=None) -> int:
         "roofline_wgrad_overlapped": roofline(WGRAD_KERNEL, WGRAD_TAGS, probes, fl["call"], ms,
                                               len(probed)),
     }
+    if cfg.dtype == "bf16" and not cfg.swiglu and cfg.tokens % 8 == 0:
+        # the same shard's forward GEMMs on the FP8 matrix cores (not part of the step)
+        out["fp8_forward_gemms"] = fp8_gemm_probe(cfg, L)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, data)
     print(json.dumps(out), flush=True)

@@ -423,8 +423,14 @@ __global__ void __launch_bounds__(256) fp8_amax_kernel(const bf16_t* __restrict_
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  // non-negative floats order like their bit patterns
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(scale + 1), __float_as_uint(m));
+  // one atomic per workgroup (non-negative floats order like their bits)
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(scale + 1), __float_as_uint(m));
+  }
 }
 
 __global__ void __launch_bounds__(256) fp8_quant_kernel(const bf16_t* __restrict__ x, int64_t nvec,
@@ -1130,7 +1136,8 @@ hipError_t quantize_fp8(const void* x, int64_t n, uint8_t* q, float* scale, hipS
   }
   const int64_t nvec = n / 8;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>((nvec + 255) / 256, 2048));
-  hipLaunchKernelGGL(fp8_amax_kernel, dim3(grid), dim3(256), 0, s, cptr<bf16_t>(x), nvec, scale);
+  const unsigned agrid = std::min(grid, 256u);  // at most 256 same-address atomics
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3(agrid), dim3(256), 0, s, cptr<bf16_t>(x), nvec, scale);
   hipLaunchKernelGGL(fp8_quant_kernel, dim3(grid), dim3(256), 0, s, cptr<bf16_t>(x), nvec, q, scale);
   return hipGetLastError();
 }
