@@ -53,6 +53,7 @@ PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
 FWD_KERNEL = "gemm_bf16_kernel, forward layout (k-major A and B, bf16 C, fused bias/GeLU)"
 WGRAD_KERNEL = "gemm_bf16_kernel, weight-gradient layout (m-major A, n-major B, fp32 C)"
+FP8_KERNEL = "gemm_bf16_kernel<..., F8> (E4M3 operands, forward layout)"
 
 
 def seq_pairs(cu) -> int:
@@ -253,9 +254,10 @@ def fp8_gemm_probe(cfg, L, reps: int = 20) -> dict:
     ach = tot["flop"] / tot["fp8"] / 1e6
     return {"per_gemm": res, "bf16_us": round(tot["bf16"], 1), "fp8_us": round(tot["fp8"], 1),
             "fp8_with_quant_us": round(tot["fp8_with_quant"], 1),
-            "roofline": {"kernel": "gemm_bf16_kernel<..., F8> (E4M3 operands, forward layout)",
+            "roofline": {"kernel": FP8_KERNEL,
                          "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                         "traffic": traffic_for(FP8_KERNEL)}}
 
 
 def main(argv=None) -> int:
