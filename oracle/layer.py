@@ -28,7 +28,7 @@ parallelism guide", §3.3 launch flags ``--swiglu --disable-bias-linear``):
 and its backward by the chain rule.  The rank view (which slice of each
 tensor a given rank computes) is in ``rank_view``.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent (each is a stated choice, not a fact of the pages):
 pre-LN; LayerNorm with population variance and eps inside the square root;
 score scale 1/sqrt(head_dim); the mask keeps key j for query i iff
 j <= i and j lies in i's document; GeLU is the tanh form; Wqkv stacks

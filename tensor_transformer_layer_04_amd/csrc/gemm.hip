@@ -377,9 +377,13 @@ gemm_bf16_kernel(GemmParams p) {
   constexpr int kReads = F8 ? 2 * (FM + FN) : FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
   constexpr int kPerMfma = (kReads + FM * FN - 1) / (FM * FN);
   // MFMAs of one k-step with the fragment reads of the next step spread
-  // between them, so LDS latency hides behind the matrix pipeline.
+  // between them, so LDS latency hides behind the matrix pipeline.  Each
+  // k-step runs at raised wave priority, dropped between steps, so that the
+  // SIMD's arbiter favours a wave with MFMAs ready over its neighbour at the
+  // barrier or in its copy issue (about 1% on the shard GEMMs, measured).
   auto step = [&](const Frags& f, bool prefetch, const char* ta, const char* tb, int kk,
                   Frags& nf) {
+    __builtin_amdgcn_s_setprio(1);
     if (prefetch) load_frags(ta, tb, kk, nf);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -399,6 +403,7 @@ gemm_bf16_kernel(GemmParams p) {
 #endif
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Pipeline over k-tiles (A stage kt % NA and B stage kt % NB hold tile
@@ -434,6 +439,7 @@ gemm_bf16_kernel(GemmParams p) {
   auto step_c = [&](const Frags& f, const char* ta, const char* tb, int kk, Frags& nf,
                     auto&& copies, auto nc_tag) {
     constexpr int nc = decltype(nc_tag)::v;
+    __builtin_amdgcn_s_setprio(1);
     copies();
     load_frags(ta, tb, kk, nf);
 #pragma unroll
@@ -449,6 +455,7 @@ gemm_bf16_kernel(GemmParams p) {
     }
     if constexpr (nc > FM * FN) __builtin_amdgcn_sched_group_barrier(0x020, nc - FM * FN, 0);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   auto copy_a = [&](char* sa, int k0) {
     issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
