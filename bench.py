@@ -436,11 +436,14 @@ def main(argv=None) -> int:
         "config": {
             "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard"
                         + (" with sequence parallelism" if L.sp else "")
+                        + (f", attention over {L.cp} context-parallel chunks"
+                           f" ({len(L.cp_pairs())} off-diagonal block pairs)" if L.cp > 1 else "")
                         + (" + vocab-parallel CE head" if cfg.vocab else "") + " fwd+bwd",
             "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn, "tp": cfg.tp,
             "rank": args.rank, "seq_len": cfg.seq_len, "micro_batch": cfg.micro_batch,
             "tokens": cfg.tokens, "global_batch": cfg.micro_batch,
-            "parallelism": f"tp{cfg.tp}" + ("-sp" if L.sp else "") + "-shard",
+            "parallelism": f"tp{cfg.tp}" + ("-sp" if L.sp else "")
+                           + (f"-cp{L.cp}" if L.cp > 1 else "") + "-shard",
         },
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),

@@ -273,8 +273,13 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
  * "Megatron-LM / Megatron Core README digest"; the pages give no algorithm,
  * the chunked, log-sum-exp merged form is the plain reading of splitting
  * the sequence dimension of attention; here all chunks are computed on one
- * device, one pair per call).  bf16 shards, one sequence
- * (micro_batch 1, no cu_seqlens), else MTP_ERR_UNSUPPORTED.
+ * device, one pair per call).  bf16 shards, micro_batch 1, else
+ * MTP_ERR_UNSUPPORTED.  The tokens are one sequence when cu_seqlens is NULL,
+ * else the packed documents of cu_seqlens (n_seqs+1 device offsets, as for
+ * mtp_attn_fwd; the chunks need not align with the documents): a query then
+ * sees only the keys of its own document, and a query with no visible key
+ * in a block gets ctx 0 and lse -inf from mtp_attn_fwd_block, which
+ * mtp_attn_merge treats as an empty part.
  *
  * mtp_attn_fwd_block: queries at rows [q_lo, q_hi) of qkv attend to the keys
  *   at rows [k_lo, k_hi) with the causal mask of their absolute positions:
@@ -283,13 +288,15 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
  *   Writes rows [q_lo, q_hi) of ctx [T,h_l] and columns [q_lo, q_hi) of lse
  *   [a_l,T] (natural log of each row's sum of exp(score)) and nothing else. */
 int mtp_attn_fwd_block(const mtp_shard_desc* desc, const void* qkv, int64_t q_lo, int64_t q_hi,
-                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse, void* stream);
+                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse,
+                       const int32_t* cu_seqlens, int32_t n_seqs, void* stream);
 
 /* mtp_attn_merge: rows [row_lo, row_hi) of (ctx, lse) become the attention
  *   over the union of the key sets of (ctx, lse) and (ctx_part, lse_part),
  *   two results of mtp_attn_fwd_block for the same queries and disjoint keys:
  *   lse = log(e^lse + e^lse_part), ctx = (e^lse ctx + e^lse_part ctx_part) /
- *   e^lse_new, per row and head.  In place on (ctx, lse).                   */
+ *   e^lse_new, per row and head.  In place on (ctx, lse).  A row whose
+ *   lse_part is -inf is left unchanged.                                     */
 int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void* ctx_part,
                    const float* lse_part, int64_t row_lo, int64_t row_hi, void* stream);
 
@@ -300,8 +307,9 @@ int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void
  *   Needs the workspace of mtp_attn_bwd.                                    */
 int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                        const float* lse, const void* dctx, void* dqkv, int64_t q_lo,
-                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate, void* ws,
-                       size_t ws_bytes, void* stream);
+                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate,
+                       const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* ------------------------------------------------------------ partial sum
  * The sum that the pages perform with a tensor-parallel all-reduce (page

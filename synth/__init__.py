@@ -114,6 +114,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
         description="packed variable-length batch, TP=1, bf16"),
+    "varlen_tp1_cp4": LayerConfig(
+        "varlen_tp1_cp4", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
+        varlen_tokens=16384, doc_min=256, doc_max=4096, context_parallel=4,
+        description="the packed variable-length batch, TP=1, attention as 4 context-parallel "
+                    "chunks of 4096 tokens (block pairs only where a document crosses), bf16"),
 }
 
 # Scaled-down cases with the same structure that the oracle finishes in
@@ -159,6 +164,14 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_bf16_d64_cp4": LayerConfig(
         "small_bf16_d64_cp4", hidden=512, heads=8, ffn=2080, tp=4, seq_len=264, dtype="bf16",
         context_parallel=4),
+    # packed documents over context-parallel chunks of 250 and 320 tokens:
+    # chunk edges fall inside documents and inside 64-row tiles
+    "small_varlen_cp4": LayerConfig(
+        "small_varlen_cp4", hidden=256, heads=2, ffn=1024, tp=1, seq_len=1000, dtype="bf16",
+        varlen_tokens=1000, doc_min=1, doc_max=300, context_parallel=4, affine_random=True),
+    "small_varlen_d64_tp2_cp3": LayerConfig(
+        "small_varlen_d64_tp2_cp3", hidden=512, heads=8, ffn=1376, tp=2, seq_len=960,
+        dtype="bf16", varlen_tokens=960, doc_min=1, doc_max=400, context_parallel=3),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

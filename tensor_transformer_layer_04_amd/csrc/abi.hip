@@ -334,15 +334,18 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, c
 }
 
 int mtp_attn_fwd_block(const mtp_shard_desc* desc, const void* qkv, int64_t q_lo, int64_t q_hi,
-                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse, void* stream) {
+                       int64_t k_lo, int64_t k_hi, void* ctx, float* lse,
+                       const int32_t* cu_seqlens, int32_t n_seqs, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
+  if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
   st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
   if (st != MTP_OK) return st;
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = ctx; a.lse = lse;
+  a.cu_seqlens = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : 0;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
   a.q_lo = q_lo; a.q_hi = q_hi; a.k_lo = k_lo; a.k_hi = k_hi;
   return hip_status(mtp::attn_fwd(s.bf16, a, static_cast<hipStream_t>(stream)));
@@ -364,13 +367,15 @@ int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void
 }
 int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                        const float* lse, const void* dctx, void* dqkv, int64_t q_lo,
-                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       int64_t q_hi, int64_t k_lo, int64_t k_hi, int accumulate,
+                       const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
+                       void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
     return MTP_ERR_INVALID_ARG;
+  if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
   st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
   if (st != MTP_OK) return st;
   if (q_hi - q_lo != k_hi - k_lo) return MTP_ERR_INVALID_ARG;
@@ -379,6 +384,7 @@ int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* 
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
   a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
+  a.cu_seqlens = cu_seqlens; a.n_seqs = cu_seqlens ? n_seqs : 0;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
   a.q_lo = q_lo; a.q_hi = q_hi; a.k_lo = k_lo; a.k_hi = k_hi;
   a.accumulate = accumulate != 0;

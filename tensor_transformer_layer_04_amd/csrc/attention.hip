@@ -232,6 +232,8 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(bf16_t* ctx, float* lse
   const int r = row_lo + static_cast<int>(idx / heads), h = static_cast<int>(idx % heads);
   const int64_t li = static_cast<int64_t>(h) * T + r;
   const float la = lse[li], lb = lse_p[li];
+  // an empty part (no visible key: lse -inf, ctx 0) leaves the row as it is
+  if (lb == -INFINITY) return;
   const float m = fmaxf(la, lb);
   const float wa = __expf(la - m), wb = __expf(lb - m);
   const float inv = 1.0f / (wa + wb);

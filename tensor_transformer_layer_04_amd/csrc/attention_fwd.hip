@@ -345,7 +345,10 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
       lt += lk[k] * ak[k];
     }
     if (qvalid) {
-      const float inv = 1.0f / lt;
+      // A query that sees no key of the range (possible in a block of keys
+      // that precede the queries when documents are packed) gets ctx 0 and
+      // lse -inf: the empty part of a log-sum-exp merge.
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
       bf16_t* out = p.ctx + static_cast<int64_t>(qi) * p.hl + head * D;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
@@ -364,7 +367,8 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
           store4(out + 32 * d + 8 * a + 4 * g, v);
         }
       if (g == 0)
-        p.lse[static_cast<int64_t>(head) * T + qi] = (mf + __builtin_amdgcn_logf(lt)) * kLn2;
+        p.lse[static_cast<int64_t>(head) * T + qi] =
+            lt > 0.0f ? (mf + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
   }
 }

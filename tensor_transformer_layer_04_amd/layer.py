@@ -39,12 +39,29 @@ added over the computed ranks in rank order.
 """
 from __future__ import annotations
 
+import bisect
 import contextlib
 from typing import Dict, List, Optional, Sequence
 
 import torch
 
 from . import mtp
+
+
+def cp_block_pairs(chunks, cu_host=None):
+    """The context-parallel block pairs (query chunk j, key chunk i < j) with
+    work in them, in ring order (i = j-1, ..., 0) for each j.  ``chunks`` are
+    consecutive (lo, hi) token ranges; ``cu_host`` the packed documents'
+    offsets (None: one sequence from token 0, every pair has work).  A query sees only
+    its own document's keys, and the earliest document start among a
+    chunk's queries is that of its first token, so chunk i's keys are
+    visible to some query of chunk j iff that start lies before the end of
+    chunk i; the other pairs are not launched."""
+    out = []
+    for j, (q0, _) in enumerate(chunks):
+        start = 0 if cu_host is None else cu_host[bisect.bisect_right(cu_host, q0) - 1]
+        out += [(j, i) for i in range(j - 1, -1, -1) if start < chunks[i][1]]
+    return out
 
 
 def desc_for(cfg, rank: int) -> mtp.mtp_shard_desc:
@@ -152,8 +169,10 @@ class TPLayer(_Probed):
         self.w = {r: pack_rank_weights(full, cfg, r, device) for r in self.ranks}
         self.rep = replicated_params(full, device)
         self.cu = None
+        self.cu_host = None
         self.n_seqs = 0
         if cu_seqlens is not None and cfg.varlen_tokens:
+            self.cu_host = [int(v) for v in cu_seqlens.cpu().tolist()]
             self.cu = cu_seqlens.to(device=self.device, dtype=torch.int32).contiguous()
             self.n_seqs = self.cu.numel() - 1
         # Weight and bias gradients are off the backward's critical path: with
@@ -164,13 +183,13 @@ class TPLayer(_Probed):
         self.k_fc1 = mtp.MTP_FC1_SWIGLU if self.swiglu else mtp.MTP_FC1
         self.k_fc2 = mtp.MTP_FC2_SWIGLU if self.swiglu else mtp.MTP_FC2
         # Context parallelism: the attention of each rank's heads runs over
-        # cp chunks of the sequence, block pair by block pair (the keys of a
-        # chunk and of every earlier chunk), the partials merged through
-        # their log-sum-exp; bf16, one fixed-length sequence.
+        # cp chunks of the token stream, block pair by block pair (the keys of
+        # a chunk and of every earlier chunk), the partials merged through
+        # their log-sum-exp; bf16, one sequence or packed documents.
         self.cp = int(getattr(cfg, "context_parallel", 1))
         if self.cp > 1:
-            if cfg.dtype != "bf16" or cfg.varlen_tokens or cfg.micro_batch != 1:
-                raise ValueError("context parallelism needs one bf16 sequence (micro_batch 1)")
+            if cfg.dtype != "bf16" or cfg.micro_batch != 1:
+                raise ValueError("context parallelism needs a bf16 shard with micro_batch 1")
             if self.T % self.cp:
                 raise ValueError(f"context parallelism needs T ({self.T}) divisible by {self.cp}")
         self.sp = bool(getattr(cfg, "sequence_parallel", False)) and cfg.tp > 1
@@ -421,31 +440,36 @@ class TPLayer(_Probed):
         L = self.T // self.cp
         return [(c * L, (c + 1) * L) for c in range(self.cp)]
 
+    def cp_pairs(self):
+        return cp_block_pairs(self._chunks(), self.cu_host)
+
     def _attn_fwd_cp(self, d, a):
         """Chunk j (a context-parallel rank) attends to its own keys (the
-        diagonal block), then, ring step by ring step, to the keys of chunks
-        j-1, ..., 0; each partial is merged into (ctx, lse) of j's rows."""
+        diagonal block), then, ring step by ring step, to the keys of the
+        earlier chunks its documents reach; each partial is merged into
+        (ctx, lse) of j's rows."""
         ch = self._chunks()
-        for j, (q0, q1) in enumerate(ch):
-            mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, q0, q1, a["ctx"], a["lse"])
-            for i in range(j - 1, -1, -1):
-                k0, k1 = ch[i]
-                mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, k0, k1, a["ctx_p"], a["lse_p"])
-                mtp.mtp_attn_merge(d, a["ctx"], a["lse"], a["ctx_p"], a["lse_p"], q0, q1)
+        cu, n = self.cu, self.n_seqs
+        for (q0, q1) in ch:
+            mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, q0, q1, a["ctx"], a["lse"], cu, n)
+        for j, i in self.cp_pairs():
+            (q0, q1), (k0, k1) = ch[j], ch[i]
+            mtp.mtp_attn_fwd_block(d, a["qkv"], q0, q1, k0, k1, a["ctx_p"], a["lse_p"], cu, n)
+            mtp.mtp_attn_merge(d, a["ctx"], a["lse"], a["ctx_p"], a["lse_p"], q0, q1)
 
     def _attn_bwd_cp(self, d, a, ws, wsb):
         """Backward of every block pair with the merged ctx and lse: the
         diagonal pairs first (they write each chunk's dQ rows and dK/dV rows),
         then the pairs below the diagonal, which add into them."""
         ch = self._chunks()
+        cu, n = self.cu, self.n_seqs
         for (q0, q1) in ch:
             mtp.mtp_attn_bwd_block(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], q0, q1,
-                                   q0, q1, 0, ws, wsb)
-        for j, (q0, q1) in enumerate(ch):
-            for i in range(j - 1, -1, -1):
-                k0, k1 = ch[i]
-                mtp.mtp_attn_bwd_block(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"],
-                                       q0, q1, k0, k1, 1, ws, wsb)
+                                   q0, q1, 0, ws, wsb, cu, n)
+        for j, i in self.cp_pairs():
+            (q0, q1), (k0, k1) = ch[j], ch[i]
+            mtp.mtp_attn_bwd_block(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"],
+                                   q0, q1, k0, k1, 1, ws, wsb, cu, n)
 
     def partials(self) -> Dict[str, List[torch.Tensor]]:
         """This object's partial outputs, to be passed as ``external`` to a

@@ -57,10 +57,11 @@ _SIGS = {
     "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "mtp_quantize_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 7 + [_VP]),
-    "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4 + [_VP, _VP, _VP]),
+    "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4
+                           + [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "mtp_attn_merge": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int64] * 2 + [_VP]),
     "mtp_attn_bwd_block": (ctypes.c_int, [_VP] + [_VP] * 5 + [ctypes.c_int64] * 4
-                           + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
+                           + [ctypes.c_int, _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "mtp_partial_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
     "mtp_partial_sum_layernorm": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8 + [_VP]),
     "mtp_layernorm_bwd_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8
@@ -196,9 +197,10 @@ def mtp_linear_fwd_fp8(desc, kind, x8, x_scale, w8, w_scale, b, y, preact, strea
                  _addr(w8), _addr(w_scale), _addr(b), _addr(y), _addr(preact), _stream(stream))
 
 
-def mtp_attn_fwd_block(desc, qkv, q_lo, q_hi, k_lo, k_hi, ctx, lse, stream=None):
+def mtp_attn_fwd_block(desc, qkv, q_lo, q_hi, k_lo, k_hi, ctx, lse, cu_seqlens=None, n_seqs=0,
+                       stream=None):
     return _call("mtp_attn_fwd_block", ctypes.byref(desc), _addr(qkv), q_lo, q_hi, k_lo, k_hi,
-                 _addr(ctx), _addr(lse), _stream(stream))
+                 _addr(ctx), _addr(lse), _addr(cu_seqlens), int(n_seqs), _stream(stream))
 
 
 def mtp_attn_merge(desc, ctx, lse, ctx_part, lse_part, row_lo, row_hi, stream=None):
@@ -207,10 +209,10 @@ def mtp_attn_merge(desc, ctx, lse, ctx_part, lse_part, row_lo, row_hi, stream=No
 
 
 def mtp_attn_bwd_block(desc, qkv, ctx, lse, dctx, dqkv, q_lo, q_hi, k_lo, k_hi, accumulate, ws,
-                       ws_bytes, stream=None):
+                       ws_bytes, cu_seqlens=None, n_seqs=0, stream=None):
     return _call("mtp_attn_bwd_block", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
-                 _addr(dctx), _addr(dqkv), q_lo, q_hi, k_lo, k_hi, accumulate, _addr(ws),
-                 ws_bytes, _stream(stream))
+                 _addr(dctx), _addr(dqkv), q_lo, q_hi, k_lo, k_hi, accumulate,
+                 _addr(cu_seqlens), int(n_seqs), _addr(ws), ws_bytes, _stream(stream))
 
 
 def mtp_partial_sum(desc, partials, bias, residual, out, stream=None):

@@ -148,10 +148,11 @@ def test_context_parallel_block_validation():
     any device work."""
     lib = mtp.lib()
     d = valid(seq_len=2048)
-    fwd = lambda q0, q1, k0, k1, desc=d: lib.mtp_attn_fwd_block(
-        ctypes.byref(desc), FAKE, q0, q1, k0, k1, FAKE, FAKE, None)
-    bwd = lambda q0, q1, k0, k1: lib.mtp_attn_bwd_block(
-        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, q0, q1, k0, k1, 0, FAKE, 1 << 30, None)
+    fwd = lambda q0, q1, k0, k1, desc=d, cu=None, n=0: lib.mtp_attn_fwd_block(
+        ctypes.byref(desc), FAKE, q0, q1, k0, k1, FAKE, FAKE, cu, n, None)
+    bwd = lambda q0, q1, k0, k1, cu=None, n=0: lib.mtp_attn_bwd_block(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, q0, q1, k0, k1, 0, cu, n, FAKE, 1 << 30,
+        None)
     assert fwd(1024, 2048, 512, 1536) == mtp.MTP_ERR_INVALID_ARG    # keys overlap queries
     assert fwd(0, 1024, 1024, 2048) == mtp.MTP_ERR_INVALID_ARG      # keys after queries
     assert fwd(1024, 3000, 0, 1024) == mtp.MTP_ERR_INVALID_ARG      # past T
@@ -159,6 +160,9 @@ def test_context_parallel_block_validation():
     assert fwd(0, 1024, 0, 1024, valid(seq_len=2048, dtype=mtp.MTP_F32)) == mtp.MTP_ERR_UNSUPPORTED
     assert fwd(0, 1024, 0, 1024, valid(seq_len=1024, micro_batch=2)) == mtp.MTP_ERR_UNSUPPORTED
     assert bwd(1024, 2048, 0, 512) == mtp.MTP_ERR_INVALID_ARG       # unequal lengths
+    # packed documents need at least one document
+    assert fwd(1024, 2048, 0, 1024, cu=FAKE, n=0) == mtp.MTP_ERR_INVALID_ARG
+    assert bwd(1024, 2048, 0, 1024, cu=FAKE, n=0) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_attn_merge(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 100, 50,
                               None) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_attn_merge(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, 4096,

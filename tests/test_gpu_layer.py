@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_tp2", "small_f32_tp4", "small_bf16_tp2", "small_bf16_d64_tp4", "small_bf16_mb2",
          "small_varlen_tp1", "one_token_bf16", "small_bf16_tp2_sp", "small_f32_tp4_sp",
          "tiny_swiglu_tp2", "small_bf16_swiglu_tp2", "small_bf16_swiglu_sp_tp4",
-         "small_bf16_tp2_cp2", "small_bf16_d64_cp4"]
+         "small_bf16_tp2_cp2", "small_bf16_d64_cp4", "small_varlen_cp4",
+         "small_varlen_d64_tp2_cp3"]
 
 
 @pytest.mark.parametrize("name", SMALL)
