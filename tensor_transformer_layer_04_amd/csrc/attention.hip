@@ -56,8 +56,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // delta[n][i] = sum_d dctx[i, n*D + d] * ctx[i, n*D + d]  (= rowsum(P * dP)),
 // and (bf16 path) lse2[n][i] = lse[n][i] * log2(e) right after delta in the
 // workspace, so the MFMA passes get exp(S - lse) as exp2(S*scale*log2e - lse2).
+// Rows [row_lo, row_lo + rows) only: the query rows of the block being
+// differentiated (all T rows for the whole attention).
 template <typename T>
-__global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D) {
+__global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D, int row_lo,
+                                                         int rows) {
   const int per_row = D / 8;                 // threads per (token, head)
   const int pairs_per_block = 256 / per_row;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * pairs_per_block + threadIdx.x / per_row;
@@ -65,8 +68,8 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D) {
   float acc = 0.0f;
   int64_t i = 0;
   int n = 0;
-  if (pair < static_cast<int64_t>(p.T) * p.heads) {
-    i = pair / p.heads;
+  if (pair < static_cast<int64_t>(rows) * p.heads) {
+    i = row_lo + pair / p.heads;
     n = static_cast<int>(pair % p.heads);
     float a[8], b[8];
     load8(static_cast<const T*>(p.dctx) + i * p.hl + n * D + c * 8, a);
@@ -75,7 +78,7 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D) {
     for (int e = 0; e < 8; ++e) acc += a[e] * b[e];
   }
   for (int o = per_row / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-  if (c == 0 && pair < static_cast<int64_t>(p.T) * p.heads) {
+  if (c == 0 && pair < static_cast<int64_t>(rows) * p.heads) {
     const int64_t at = static_cast<int64_t>(n) * p.T + i;
     p.delta[at] = acc;
     if (sizeof(T) == 2) p.delta[static_cast<int64_t>(p.heads) * p.T + at] = p.lse[at] * kLog2e;
@@ -293,11 +296,19 @@ hipError_t attn_bwd(bool bf16, const AttnDesc& a, hipStream_t s) {
   if (a.T == 0 || a.heads == 0) return hipSuccess;
   const AttnParams p = make_params(a);
   const int per_row = a.head_dim / 8;
-  const int64_t pairs = a.T * a.heads;
+  // D and lse*log2(e) are read only at the query rows of the range
+  const int row_lo = static_cast<int>(a.q_lo);
+  const int rows = static_cast<int>((a.q_hi < 0 ? a.T : a.q_hi) - a.q_lo);
+  if (rows <= 0) return hipSuccess;
+  const int64_t pairs = static_cast<int64_t>(rows) * a.heads;
   const int pairs_per_block = 256 / per_row;
   const dim3 dgrid(static_cast<unsigned>((pairs + pairs_per_block - 1) / pairs_per_block));
-  if (bf16) hipLaunchKernelGGL(attn_delta_kernel<bf16_t>, dgrid, dim3(256), 0, s, p, a.head_dim);
-  else hipLaunchKernelGGL(attn_delta_kernel<float>, dgrid, dim3(256), 0, s, p, a.head_dim);
+  if (bf16)
+    hipLaunchKernelGGL(attn_delta_kernel<bf16_t>, dgrid, dim3(256), 0, s, p, a.head_dim, row_lo,
+                       rows);
+  else
+    hipLaunchKernelGGL(attn_delta_kernel<float>, dgrid, dim3(256), 0, s, p, a.head_dim, row_lo,
+                       rows);
   if (bf16) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
