@@ -485,6 +485,40 @@ partial_sum_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
   }
 }
 
+// The same sum for a compile-time number of partials N: every load of the
+// thread's vector (the N partials, bias, residual) is issued before the first
+// add, so the latency of one load is paid once per vector rather than once per
+// operand.  Same fp32 order as partial_sum_kernel, so the same bits.
+template <typename T, int N>
+__global__ void __launch_bounds__(256)
+partial_sum_n_kernel(PartialPtrs parts, const T* __restrict__ bias,
+                     const T* __restrict__ residual, T* out, int64_t total, int h) {
+  const int64_t nvec = total / 8;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+       v += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t off = v * 8;
+    float t[N][8], tb[8], tr[8];
+#pragma unroll
+    for (int i = 0; i < N; ++i) load8(static_cast<const T*>(parts.p[i]) + off, t[i]);
+    if (bias) load8(bias + (off % h), tb);
+    if (residual) load8(residual + off, tr);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += t[i][e];
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += tb[e];
+    }
+    if (residual) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += tr[e];
+    }
+    store8(out + off, acc);
+  }
+}
+
 // Round 8 fp32 values to the storage type T in place (identity for fp32,
 // round-to-nearest-even bf16 otherwise): the value a store + load would give.
 template <typename T> __device__ __forceinline__ void round8(float v[8]) {
@@ -505,7 +539,10 @@ template <typename T> __device__ __forceinline__ void round8(float v[8]) {
 // row in registers.  One wave per row, four rows per workgroup, h = 512*NC
 // (lane l owns the 16-byte chunks l, l+64, ...).  A lane reads every
 // element it writes before writing it, so out may alias an input.
-template <typename T, int NC>
+// NP > 0 (bf16 only): NP partials known at compile time, and every load of
+// the row (partials, bias, residual) is issued before the first add; the adds
+// keep the order of the general path, so the bits are the same.
+template <typename T, int NC, int NP = 0>
 __global__ void __launch_bounds__(256)
 sum_layernorm_fwd_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
                          const T* residual, T* out, const T* __restrict__ gamma,
@@ -516,31 +553,63 @@ sum_layernorm_fwd_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
   if (row >= T_rows) return;
   const int64_t base = row * h;
   float v[NC][8];
-  load_row<T, NC>(static_cast<const T*>(parts.p[0]) + base, lane, v);
-  for (int i = 1; i < n; ++i) {
-    float t[NC][8];
-    load_row<T, NC>(static_cast<const T*>(parts.p[i]) + base, lane, t);
+  if constexpr (NP > 0) {
+    static_assert(sizeof(T) == 2, "compile-time partial count: bf16 rows");
+    uint4 raw[NP][NC], rb[NC], rr[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < NP; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
-  }
-  if (bias) {
+      for (int c = 0; c < NC; ++c)
+        raw[i][c] = *reinterpret_cast<const uint4*>(static_cast<const T*>(parts.p[i]) + base +
+                                                    (lane + 64 * c) * 8);
+    if (bias) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float t[8];
-      load8(bias + (lane + 64 * c) * 8, t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] += t[e];
+      for (int c = 0; c < NC; ++c)
+        rb[c] = *reinterpret_cast<const uint4*>(bias + (lane + 64 * c) * 8);
     }
-  }
-  if (residual) {
-    float t[NC][8];
-    load_row<T, NC>(residual + base, lane, t);
+    if (residual) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        rr[c] = *reinterpret_cast<const uint4*>(residual + base + (lane + 64 * c) * 8);
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+      for (int e = 0; e < 8; ++e) {
+        float a = bfw(raw[0][c], e);
+#pragma unroll
+        for (int i = 1; i < NP; ++i) a += bfw(raw[i][c], e);
+        if (bias) a += bfw(rb[c], e);
+        if (residual) a += bfw(rr[c], e);
+        v[c][e] = a;
+      }
+  } else {
+    load_row<T, NC>(static_cast<const T*>(parts.p[0]) + base, lane, v);
+    for (int i = 1; i < n; ++i) {
+      float t[NC][8];
+      load_row<T, NC>(static_cast<const T*>(parts.p[i]) + base, lane, t);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+    }
+    if (bias) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float t[8];
+        load8(bias + (lane + 64 * c) * 8, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += t[e];
+      }
+    }
+    if (residual) {
+      float t[NC][8];
+      load_row<T, NC>(residual + base, lane, t);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+    }
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -950,18 +1019,27 @@ hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, cons
   PartialPtrs pp{};
   for (int i = 0; i < n; ++i) pp.p[i] = partials[i];
   const dim3 grid(static_cast<unsigned>((T + 3) / 4));
-#define MTP_SUM_LN(TT, NC)                                                                     \
-  hipLaunchKernelGGL((sum_layernorm_fwd_kernel<TT, NC>), grid, dim3(256), 0, s, pp, n,           \
+#define MTP_SUM_LN(TT, NC, NP)                                                                 \
+  hipLaunchKernelGGL((sum_layernorm_fwd_kernel<TT, NC, NP>), grid, dim3(256), 0, s, pp, n,       \
                      cptr<TT>(bias), cptr<TT>(residual), static_cast<TT*>(out), cptr<TT>(gamma), \
                      cptr<TT>(beta), static_cast<TT*>(y), mean, rstd, T, h, eps)
-#define MTP_SUM_LN_T(TT)                  \
-  switch (nc) {                           \
-    case 1: MTP_SUM_LN(TT, 1); break;     \
-    case 2: MTP_SUM_LN(TT, 2); break;     \
-    case 4: MTP_SUM_LN(TT, 4); break;     \
-    default: MTP_SUM_LN(TT, 8); break;    \
+#define MTP_SUM_LN_T(TT, NP)                  \
+  switch (nc) {                               \
+    case 1: MTP_SUM_LN(TT, 1, NP); break;     \
+    case 2: MTP_SUM_LN(TT, 2, NP); break;     \
+    case 4: MTP_SUM_LN(TT, 4, NP); break;     \
+    default: MTP_SUM_LN(TT, 8, NP); break;    \
   }
-  if (bf16) { MTP_SUM_LN_T(bf16_t) } else { MTP_SUM_LN_T(float) }
+  if (bf16) {
+    switch (n) {
+      case 1: MTP_SUM_LN_T(bf16_t, 1) break;
+      case 2: MTP_SUM_LN_T(bf16_t, 2) break;
+      case 4: MTP_SUM_LN_T(bf16_t, 4) break;
+      default: MTP_SUM_LN_T(bf16_t, 0) break;
+    }
+  } else {
+    MTP_SUM_LN_T(float, 0)
+  }
 #undef MTP_SUM_LN_T
 #undef MTP_SUM_LN
   return hipGetLastError();
@@ -1075,6 +1153,13 @@ hipError_t partial_sum(bool bf16, const void* const* partials, int n, const void
   for (int i = 0; i < n; ++i) pp.p[i] = partials[i];
   const int64_t total = T * h;
   const int grid = grid_for(total / 8);
+  if (bf16 && (n == 1 || n == 2 || n == 4)) {
+    auto* k = n == 1 ? partial_sum_n_kernel<bf16_t, 1>
+              : n == 2 ? partial_sum_n_kernel<bf16_t, 2> : partial_sum_n_kernel<bf16_t, 4>;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, pp, cptr<bf16_t>(bias),
+                       cptr<bf16_t>(residual), static_cast<bf16_t*>(out), total, h);
+    return hipGetLastError();
+  }
   if (bf16)
     hipLaunchKernelGGL(partial_sum_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, pp, n,
                        cptr<bf16_t>(bias), cptr<bf16_t>(residual), static_cast<bf16_t*>(out),
