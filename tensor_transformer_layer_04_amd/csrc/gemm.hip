@@ -582,12 +582,15 @@ int pick_tile(int M, int N) {
   const int per_cu[kNumTiles] = {1, 1, 1, 2, 1, 1, 1};
   const double eff[kNumTiles] = {1.0, 0.9, 0.92, 0.87, 0.0, 0.96, 0.96};
   constexpr double kEffAlone128 = 0.45;
+  // Equal costs go to the tile grid that pads less (M = 5504, N = 4096:
+  // 192x256 covers 1.2% padding, 256x192 5.5%; measured 90.6 vs 93.3 us).
   int best = 0;
-  double best_cost = 1e300;
+  double best_cost = 1e300, best_pad = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
     if (eff[t] <= 0.0) continue;
     const long tiles = static_cast<long>((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
     const double area = static_cast<double>(bm[t]) * bn[t];
+    const double pad = static_cast<double>(tiles) * area;
     double cost;
     if (per_cu[t] == 2 && tiles <= kCUs) {
       cost = area / kEffAlone128;
@@ -595,7 +598,11 @@ int pick_tile(int M, int N) {
       const long slots = static_cast<long>(kCUs) * per_cu[t];
       cost = static_cast<double>((tiles + slots - 1) / slots) * per_cu[t] * area / eff[t];
     }
-    if (cost < best_cost - 1e-9) { best_cost = cost; best = t; }
+    if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && pad < best_pad)) {
+      best_cost = cost;
+      best_pad = pad;
+      best = t;
+    }
   }
   return best;
 }
