@@ -172,6 +172,8 @@ ATTN_CASES = [
     ("bf16", 2, 128, 300, [0, 1, 2, 130, 130, 131, 300], 1),
     ("bf16", 1, 128, 520, [0, 129, 257, 520], 1),
     ("bf16", 2, 64, 1, None, 1),
+    # 16 query blocks, the last one ragged
+    ("bf16", 2, 128, 1000, None, 1),
     # sequences of a multiple of 64 tokens (blocks ranked per sequence), and
     # of a ragged length
     ("bf16", 2, 128, 384, None, 3),
