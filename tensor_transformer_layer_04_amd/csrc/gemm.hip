@@ -620,12 +620,27 @@ hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
   }
 }
 
-// FP8 tiles: 128x256, 256x128 and 128x128 (the doubled fragments of the
-// larger tiles do not fit the registers of two waves per SIMD).
+// FP8 tiles: 128x256, 256x128, 128x128 and 128x384 (the doubled fragments
+// of the 256-row tiles with more than 128 columns do not fit the registers
+// of two waves per SIMD; 128x384 has 64x96 wave tiles and fills the chip in
+// one round where 128x256 needs one and a half: M = 2048 with N = 6144 or
+// 5504).  Chosen by the cost of pick_tile: rounds x tile area / efficiency.
+constexpr int kTileF8_128x384 = kNumTiles;
 int pick_tile_fp8(int M, int N) {
-  const int t = pick_tile(M, N);
-  if (t == kTile256x128 || t == kTile128x256 || t == kTile128x128) return t;
-  return M > N ? kTile256x128 : kTile128x256;
+  constexpr int kCUs = 256;
+  const int cand[4] = {kTile128x256, kTile256x128, kTile128x128, kTileF8_128x384};
+  const int bm[4] = {128, 256, 128, 128}, bn[4] = {256, 128, 128, 384}, per_cu[4] = {1, 1, 2, 1};
+  const double eff[4] = {0.92, 0.9, 0.87, 0.92};
+  int best = kTile128x256;
+  double best_cost = 1e300;
+  for (int t = 0; t < 4; ++t) {
+    const long tiles = static_cast<long>((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
+    const long slots = static_cast<long>(kCUs) * per_cu[t];
+    const double cost = static_cast<double>((tiles + slots - 1) / slots) * per_cu[t] *
+                        bm[t] * bn[t] / eff[t];
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = cand[t]; }
+  }
+  return best;
 }
 
 template <int EPI>
@@ -633,6 +648,7 @@ hipError_t dispatch_fp8(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
     case kTile256x128: return launch_bf16<256, 128, 4, 2, true, true, EPI, true>(p, s);
     case kTile128x128: return launch_bf16<128, 128, 2, 2, true, true, EPI, true>(p, s);
+    case kTileF8_128x384: return launch_bf16<128, 384, 2, 4, true, true, EPI, true>(p, s);
     default: return launch_bf16<128, 256, 2, 4, true, true, EPI, true>(p, s);
   }
 }
