@@ -86,3 +86,16 @@ def test_context_parallel_pairs_match_brute_force(T, cp, seed):
         if trial == 0:
             assert got == []
     assert set(cp_block_pairs(chunks, None)) == {(j, i) for j in range(cp) for i in range(j)}
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; asked for more it exits with a message
+    before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
