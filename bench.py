@@ -452,6 +452,13 @@ def main(argv=None) -> int:
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "graph_replay_ms_per_step": graph_ms,
         "call_us_per_step": call_us,
+        # The step without the forward sums of the ranks' row-parallel partials
+        # (charged in full above): the FFN output sum, and the projection sum
+        # fused with LN2 less a LayerNorm of the same shape (ln1).  The
+        # backward sums are fused into the LayerNorm backward and stay in.
+        "ms_per_step_less_forward_tp_sums": (
+            round(ms - 1e-3 * (call_us["sum_fc2"] + call_us["sum_proj_ln2"] - call_us["ln1"]), 4)
+            if all(k in call_us for k in ("sum_fc2", "sum_proj_ln2", "ln1")) else None),
         "roofline": roofline(FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms, len(probed)),
         "roofline_wgrad_overlapped": roofline(WGRAD_KERNEL, WGRAD_TAGS, probes, fl["call"], ms,
                                               len(probed)),
