@@ -37,6 +37,11 @@
  *    any device work is enqueued, so an error return means nothing was
  *    launched, except MTP_ERR_HIP (a launch failed; earlier kernels of the
  *    same call may have been enqueued).  No call aborts the process.
+ *  - Size limit: the kernels address the GEMM operands (activations,
+ *    weights, their gradients and FP8 codes) and the attention inputs,
+ *    statistics and workspace through 32-bit buffer offsets, so each such
+ *    tensor must span less than 2 GiB.  A call whose tensors exceed that
+ *    returns MTP_ERR_UNSUPPORTED before anything is enqueued.
  *  - T = 0 is valid: the call is a no-op except that non-accumulating
  *    gradient outputs (dgamma/dbeta, dw, db) are set to zero.
  */
@@ -363,7 +368,8 @@ int mtp_vocab_ce_combine(const mtp_shard_desc* desc, const float* const* m,
 
 /* Gradient of dloss_scale * sum_t loss_t w.r.t. this shard's logits:
  * dlogits = dloss_scale * (exp(z - M)/S - [j == target]).  For the mean
- * loss pass dloss_scale = 1/T.  dlogits [T,V_l] dtype (out).               */
+ * loss pass dloss_scale = 1/T.  dlogits [T,V_l] dtype (out).  A token whose
+ * target id lies outside [0, V) gets a NaN row (its loss is NaN too).      */
 int mtp_vocab_ce_bwd(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,
                      const float* M, const float* S, float dloss_scale, void* dlogits,
                      void* stream);

@@ -53,6 +53,19 @@ int check_desc(const mtp_shard_desc* desc, Shard* s) {
   return MTP_OK;
 }
 
+// Operands that the kernels address through 32-bit buffer resources (the
+// GEMM operands, the attention inputs, statistics and workspace) must each
+// span less than 2 GiB.  Each entry point checks the ones it touches before
+// it enqueues anything, so an over-large shard returns MTP_ERR_UNSUPPORTED
+// with nothing launched.
+constexpr int64_t kMaxBufferBytes = int64_t{1} << 31;
+bool fits(int64_t rows, int64_t cols, int64_t esize) {
+  return rows * cols * esize < kMaxBufferBytes;
+}
+bool attn_fits(const Shard& s) {
+  return fits(s.T, 3LL * s.hl, s.esize) && fits(s.T, s.hl, s.esize) && fits(s.T, s.al, 4);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MTP_OK : MTP_ERR_HIP; }
 
 hipError_t gemm(const Shard& s, const GemmDesc& g, hipStream_t st) {
@@ -78,8 +91,6 @@ int64_t row_in(const Shard& s, int kind) {
     default: return 0;
   }
 }
-
-int tile_override() { return -1; }
 
 // A (query rows, key rows) block of the context-parallel entry points: the
 // diagonal block of one chunk, or keys entirely before the queries.  The
@@ -187,6 +198,7 @@ int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, cons
   const bool swiglu = kind == MTP_FC1_SWIGLU;
   if ((kind == MTP_FC1 || swiglu) ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
   if (swiglu && b != nullptr) return MTP_ERR_INVALID_ARG;
+  if (!fits(s.T, s.h, s.esize) || !fits(n, s.h, s.esize)) return MTP_ERR_UNSUPPORTED;
   GemmDesc g{};
   g.A = x; g.lda = s.h; g.a_kmajor = true;
   g.B = w; g.ldb = s.h; g.b_kmajor = true;
@@ -195,7 +207,7 @@ int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, cons
   g.aux = preact; g.ld_aux = n;
   g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : swiglu ? mtp::kEpiSwiGLU
         : kind == MTP_VOCAB ? mtp::kEpiF32 : mtp::kEpiStore;
-  g.tile = tile_override();
+ 
   return hip_status(gemm(s, g, static_cast<hipStream_t>(stream)));
 }
 
@@ -210,6 +222,8 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
   if (!ok_ptr(dy) || !ok_ptr(x) || !ok_ptr(w) || !ok_opt(dx_partial) || !ok_opt(dw) || !ok_opt(db))
     return MTP_ERR_INVALID_ARG;
   if (kind == MTP_FC1_SWIGLU && db != nullptr) return MTP_ERR_INVALID_ARG;
+  if (!fits(s.T, n, s.esize) || !fits(n, s.h, s.esize) || !fits(s.T, s.h, s.esize))
+    return MTP_ERR_UNSUPPORTED;
   if (db) {
     const size_t need = mtp::column_sum_ws_bytes(s.T, n);
     if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
@@ -221,7 +235,7 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.A = dy; g.lda = n; g.a_kmajor = true;
     g.B = w; g.ldb = s.h; g.b_kmajor = false;
     g.M = static_cast<int>(s.T); g.N = s.h; g.K = static_cast<int>(n);
-    g.C = dx_partial; g.ldc = s.h; g.epi = mtp::kEpiStore; g.tile = tile_override();
+    g.C = dx_partial; g.ldc = s.h; g.epi = mtp::kEpiStore;
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -231,7 +245,7 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.B = x; g.ldb = s.h; g.b_kmajor = false;
     g.M = static_cast<int>(n); g.N = s.h; g.K = static_cast<int>(s.T);
     g.C = dw; g.ldc = s.h; g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
-    g.tile = tile_override();
+   
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -247,11 +261,12 @@ int mtp_row_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x_local
   const int64_t k = row_in(s, kind);
   if (k <= 0) return MTP_ERR_INVALID_ARG;
   if (!ok_ptr(x_local) || !ok_ptr(w) || !ok_ptr(partial)) return MTP_ERR_INVALID_ARG;
+  if (!fits(s.T, k, s.esize) || !fits(s.h, k, s.esize)) return MTP_ERR_UNSUPPORTED;
   GemmDesc g{};
   g.A = x_local; g.lda = k; g.a_kmajor = true;
   g.B = w; g.ldb = k; g.b_kmajor = true;
   g.M = static_cast<int>(s.T); g.N = s.h; g.K = static_cast<int>(k);
-  g.C = partial; g.ldc = s.h; g.epi = mtp::kEpiStore; g.tile = tile_override();
+  g.C = partial; g.ldc = s.h; g.epi = mtp::kEpiStore;
   return hip_status(gemm(s, g, static_cast<hipStream_t>(stream)));
 }
 
@@ -268,6 +283,8 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     return MTP_ERR_INVALID_ARG;
   if (gelu_preact && kind != MTP_FC2 && kind != MTP_FC2_SWIGLU) return MTP_ERR_INVALID_ARG;
   const bool swiglu = kind == MTP_FC2_SWIGLU && gelu_preact != nullptr;
+  if (!fits(s.T, s.h, s.esize) || !fits(s.h, k, s.esize) || !fits(s.T, k, s.esize))
+    return MTP_ERR_UNSUPPORTED;
   if (db) {
     const size_t need = mtp::column_sum_ws_bytes(s.T, s.h);
     if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
@@ -282,7 +299,7 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.C = dx_local; g.ldc = swiglu ? 2 * k : k;
     g.aux = const_cast<void*>(gelu_preact); g.ld_aux = swiglu ? 2 * k : k;
     g.epi = swiglu ? mtp::kEpiDSwiGLU : gelu_preact ? mtp::kEpiDGelu : mtp::kEpiStore;
-    g.tile = tile_override();
+   
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -292,7 +309,7 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.B = x_local; g.ldb = k; g.b_kmajor = false;
     g.M = s.h; g.N = static_cast<int>(k); g.K = static_cast<int>(s.T);
     g.C = dw; g.ldc = k; g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
-    g.tile = tile_override();
+   
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -307,6 +324,7 @@ int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* 
   if (st != MTP_OK) return st;
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = ctx; a.lse = lse;
   a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
@@ -323,6 +341,7 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, c
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
     return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
   mtp::AttnDesc a{};
@@ -341,6 +360,7 @@ int mtp_attn_fwd_block(const mtp_shard_desc* desc, const void* qkv, int64_t q_lo
   if (st != MTP_OK) return st;
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
   if (st != MTP_OK) return st;
   mtp::AttnDesc a{};
@@ -359,6 +379,7 @@ int mtp_attn_merge(const mtp_shard_desc* desc, void* ctx, float* lse, const void
   if (!ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(ctx_part) || !ok_ptr(lse_part))
     return MTP_ERR_INVALID_ARG;
   if (row_lo < 0 || row_hi > s.T || row_lo > row_hi) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   mtp::AttnDesc a{};
   a.ctx = ctx; a.lse = lse;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
@@ -376,6 +397,7 @@ int mtp_attn_bwd_block(const mtp_shard_desc* desc, const void* qkv, const void* 
   if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
     return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   st = check_block(s, desc, q_lo, q_hi, k_lo, k_hi);
   if (st != MTP_OK) return st;
   if (q_hi - q_lo != k_hi - k_lo) return MTP_ERR_INVALID_ARG;
@@ -423,6 +445,7 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
   if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
   if ((kind == MTP_PROJ || kind == MTP_FC2) && b != nullptr) return MTP_ERR_INVALID_ARG;
   if (k % 16 != 0) return MTP_ERR_UNSUPPORTED;
+  if (!fits(s.T, k, 1) || !fits(n, k, 1)) return MTP_ERR_UNSUPPORTED;
   GemmDesc g{};
   g.A = x8; g.lda = k; g.a_kmajor = true;
   g.B = w8; g.ldb = k; g.b_kmajor = true;
@@ -430,7 +453,7 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
   g.C = y; g.ldc = n; g.bias = b;
   g.aux = preact; g.ld_aux = n;
   g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : mtp::kEpiStore;
-  g.tile = tile_override();
+ 
   g.fp8 = true; g.scale_a = x_scale; g.scale_b = w_scale;
   return hip_status(mtp::gemm_bf16(g, static_cast<hipStream_t>(stream)));
 }
@@ -503,7 +526,7 @@ int mtp_vocab_ce_bwd(const mtp_shard_desc* desc, const float* logits, const int3
     return MTP_ERR_INVALID_ARG;
   if (!isfinite(dloss_scale)) return MTP_ERR_INVALID_ARG;
   return hip_status(mtp::ce_bwd(s.bf16, logits, targets, M, S, dloss_scale, dlogits, s.T, s.Vl,
-                                s.r * s.Vl, static_cast<hipStream_t>(stream)));
+                                s.r * s.Vl, s.V, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -37,14 +37,8 @@
 namespace mtp {
 namespace {
 
-#ifndef MTP_FWD_QG
-#define MTP_FWD_QG 2
-#endif
-#ifndef MTP_FWD_KH
-#define MTP_FWD_KH 2
-#endif
-constexpr int kQG = MTP_FWD_QG;  // query groups of 32 per workgroup
-constexpr int kKH = MTP_FWD_KH;  // key parts of 32 per tile (waves per query group)
+constexpr int kQG = 2;  // query groups of 32 per workgroup
+constexpr int kKH = 2;  // key parts of 32 per tile (waves per query group)
 constexpr int kFQ = 32 * kQG;    // queries per workgroup
 constexpr int kFK = 32 * kKH;    // keys per tile
 constexpr int kFW = kQG * kKH;   // waves per workgroup

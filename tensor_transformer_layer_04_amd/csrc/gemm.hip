@@ -391,16 +391,11 @@ gemm_bf16_kernel(GemmParams p) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = mma(f.b[j], f.a[i], acc[i][j]);
     if (prefetch) {
-#ifdef MTP_READS_FIRST
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-#else
 #pragma unroll
       for (int t = 0; t < FM * FN; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, kPerMfma, 0);   // then LDS reads
       }
-#endif
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
@@ -561,33 +556,28 @@ enum TileShape : int {
   kTile256x128 = 1,  // 8 waves (4x2), three stages, 144 KB LDS
   kTile128x256 = 2,  // 8 waves (2x4), three stages, 144 KB LDS
   kTile128x128 = 3,  // 4 waves (2x2), 64 KB LDS
-  kTile256x256w4 = 4,  // 4 waves (2x2), one per SIMD, 128 KB LDS
-  kTile256x192 = 5,  // 8 waves (4x2), three A and two B stages, 144 KB LDS
-  kTile192x256 = 6,  // 8 waves (2x4), three A and two B stages, 136 KB LDS
-  kNumTiles = 7
+  kTile256x192 = 4,  // 8 waves (4x2), three A and two B stages, 144 KB LDS
+  kTile192x256 = 5,  // 8 waves (2x4), three A and two B stages, 136 KB LDS
+  kNumTiles = 6
 };
 
 int pick_tile(int M, int N) {
-#ifdef MTP_FORCE_TILE
-  if (MTP_FORCE_TILE >= 0) return MTP_FORCE_TILE;
-#endif
   // Cost = rounds of tiles over the 256 CUs x tile area / relative
   // efficiency (measured on the 7B shard shapes).  128x128 tiles run two
   // per CU, or one per CU when they fit in one round; one such round (two
   // stages, four waves) measured slower than a round of three-stage
   // 128x256 tiles of twice the area (2048 x 2048 x 4096: 46.7 vs 44.0 us).
   constexpr int kCUs = 256;
-  const int bm[kNumTiles] = {256, 256, 128, 128, 256, 256, 192};
-  const int bn[kNumTiles] = {256, 128, 256, 128, 256, 192, 256};
-  const int per_cu[kNumTiles] = {1, 1, 1, 2, 1, 1, 1};
-  const double eff[kNumTiles] = {1.0, 0.9, 0.92, 0.87, 0.0, 0.96, 0.96};
+  const int bm[kNumTiles] = {256, 256, 128, 128, 256, 192};
+  const int bn[kNumTiles] = {256, 128, 256, 128, 192, 256};
+  const int per_cu[kNumTiles] = {1, 1, 1, 2, 1, 1};
+  const double eff[kNumTiles] = {1.0, 0.9, 0.92, 0.87, 0.96, 0.96};
   constexpr double kEffAlone128 = 0.45;
   // Equal costs go to the tile grid that pads less (M = 5504, N = 4096:
   // 192x256 covers 1.2% padding, 256x192 5.5%; measured 90.6 vs 93.3 us).
   int best = 0;
   double best_cost = 1e300, best_pad = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
-    if (eff[t] <= 0.0) continue;
     const long tiles = static_cast<long>((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
     const double area = static_cast<double>(bm[t]) * bn[t];
     const double pad = static_cast<double>(tiles) * area;
@@ -613,7 +603,6 @@ hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
     case kTile256x128: return launch_bf16<256, 128, 4, 2, AK, BKM, EPI>(p, s);
     case kTile128x256: return launch_bf16<128, 256, 2, 4, AK, BKM, EPI>(p, s);
     case kTile128x128: return launch_bf16<128, 128, 2, 2, AK, BKM, EPI>(p, s);
-    case kTile256x256w4: return launch_bf16<256, 256, 2, 2, AK, BKM, EPI>(p, s);
     case kTile256x192: return launch_bf16<256, 192, 4, 2, AK, BKM, EPI>(p, s);
     case kTile192x256: return launch_bf16<192, 256, 2, 4, AK, BKM, EPI>(p, s);
     default: return launch_bf16<256, 256, 2, 4, AK, BKM, EPI>(p, s);
@@ -779,7 +768,7 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     return hipErrorInvalidValue;
   p.a_bytes = static_cast<uint32_t>(ab);
   p.b_bytes = static_cast<uint32_t>(bb);
-  const int tile = (g.tile >= 0 && g.tile < kNumTiles) ? g.tile : pick_tile(g.M, g.N);
+  const int tile = pick_tile(g.M, g.N);
   if (g.a_kmajor && g.b_kmajor) {
     switch (g.epi) {
       case kEpiStore: return dispatch_tile<true, true, kEpiStore>(p, tile, s);

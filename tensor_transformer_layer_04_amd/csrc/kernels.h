@@ -32,7 +32,6 @@ struct GemmDesc {
   const void* bias;    // [N] elem type, nullable
   void* aux; int64_t ld_aux;
   int epi;
-  int tile;            // tile-shape override for tuning (-1: heuristic)
   // FP8 (E4M3) operands, forward layout only: A and B hold one byte per
   // element and C = (A B^T) * scale_a[0] * scale_b[0] before the epilogue.
   bool fp8 = false;
@@ -107,6 +106,6 @@ hipError_t ce_combine(const float* const* m, const float* const* s, const float*
                       hipStream_t stream);
 hipError_t ce_bwd(bool bf16, const float* logits, const int32_t* targets, const float* M,
                   const float* S, float scale, void* dlogits, int64_t T, int64_t V_l, int64_t v0,
-                  hipStream_t stream);
+                  int64_t V, hipStream_t stream);
 
 }  // namespace mtp

@@ -864,13 +864,22 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 ce_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ targets,
               const float* __restrict__ M, const float* __restrict__ S, float scale,
-              T* __restrict__ dlogits, int64_t V_l, int64_t v0, int blocks_per_row) {
+              T* __restrict__ dlogits, int64_t V_l, int64_t v0, int64_t V, int blocks_per_row) {
   const int64_t row = blockIdx.x / blocks_per_row;
   const int64_t c = (static_cast<int64_t>(blockIdx.x % blocks_per_row) * 256 + threadIdx.x) * 8;
   if (c >= V_l) return;
-  const float m = M[row], inv = 1.0f / S[row];
-  const int64_t tg = static_cast<int64_t>(targets[row]) - v0;
+  const int64_t id = targets[row];
   float v[8];
+  if (id < 0 || id >= V) {
+    // an id outside the vocabulary has no gradient: the row is NaN, as its
+    // loss is in the stats
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
+    store8(dlogits + row * V_l + c, v);
+    return;
+  }
+  const float m = M[row], inv = 1.0f / S[row];
+  const int64_t tg = id - v0;
   load8(logits + row * V_l + c, v);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -1199,16 +1208,16 @@ hipError_t ce_combine(const float* const* m, const float* const* sm, const float
 
 hipError_t ce_bwd(bool bf16, const float* logits, const int32_t* targets, const float* M,
                   const float* S, float scale, void* dlogits, int64_t T, int64_t V_l, int64_t v0,
-                  hipStream_t s) {
+                  int64_t V, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int bpr = static_cast<int>((V_l / 8 + 255) / 256);
   const dim3 g(static_cast<unsigned>(T * bpr));
   if (bf16)
     hipLaunchKernelGGL(ce_bwd_kernel<bf16_t>, g, dim3(256), 0, s, logits, targets, M, S, scale,
-                       static_cast<bf16_t*>(dlogits), V_l, v0, bpr);
+                       static_cast<bf16_t*>(dlogits), V_l, v0, V, bpr);
   else
     hipLaunchKernelGGL(ce_bwd_kernel<float>, g, dim3(256), 0, s, logits, targets, M, S, scale,
-                       static_cast<float*>(dlogits), V_l, v0, bpr);
+                       static_cast<float*>(dlogits), V_l, v0, V, bpr);
   return hipGetLastError();
 }
 

@@ -167,3 +167,33 @@ def test_context_parallel_block_validation():
                               None) == mtp.MTP_ERR_INVALID_ARG
     assert lib.mtp_attn_merge(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, 4096,
                               None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_oversize_operands_refused_before_any_launch():
+    """A shard whose GEMM operands or attention inputs span 2 GiB or more
+    (the kernels' 32-bit buffer offsets) is refused with
+    MTP_ERR_UNSUPPORTED by the entry point itself, before the first kernel
+    of the call is enqueued."""
+    lib = mtp.lib()
+    # x [T, h] bf16 at T = 131072, h = 8192: exactly 2 GiB
+    d = valid(hidden=8192, heads=64, ffn=32768, tp_size=4, seq_len=131072)
+    U = mtp.MTP_ERR_UNSUPPORTED
+    assert lib.mtp_col_linear_fwd(ctypes.byref(d), mtp.MTP_QKV, FAKE, FAKE, None, FAKE, None,
+                                  None) == U
+    assert lib.mtp_col_linear_bwd(ctypes.byref(d), mtp.MTP_QKV, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None, 0, None, 0, None) == U
+    assert lib.mtp_row_linear_bwd(ctypes.byref(d), mtp.MTP_PROJ, FAKE, FAKE, FAKE, None, FAKE,
+                                  FAKE, None, 0, None, 0, None) == U
+    # (the row-parallel forward reads x [T, h_l] and W [h, h_l] only; its
+    # [T, h] output is written with 64-bit offsets)
+    # eight tokens fewer fit
+    d_ok = valid(hidden=8192, heads=64, ffn=32768, tp_size=4, seq_len=131064)
+    assert lib.mtp_row_linear_fwd(ctypes.byref(d_ok), mtp.MTP_PROJ, FAKE, 0, FAKE,
+                                  None) == mtp.MTP_ERR_INVALID_ARG  # reaches the pointer check
+    # attention: qkv [T, 3 h_l] at T = 2^20, h_l = 2048 spans 12 GiB
+    da = valid(seq_len=1 << 20)
+    assert lib.mtp_attn_fwd(ctypes.byref(da), FAKE, FAKE, FAKE, None, 0, None) == U
+    assert lib.mtp_attn_bwd(ctypes.byref(da), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                            1 << 40, None) == U
+    assert lib.mtp_attn_fwd_block(ctypes.byref(da), FAKE, 0, 1024, 0, 1024, FAKE, FAKE, None,
+                                  0, None) == U

@@ -282,6 +282,67 @@ def test_layer_gradients_finite_difference(variant):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (pname, fd, an)
 
 
+@pytest.mark.parametrize("name", ["tiny_tp2", "small_varlen_tp1"])
+def test_layer_matches_torch_encoder_layer(name):
+    """The whole layer's composition against a library special case: torch's
+    ``nn.TransformerEncoderLayer`` with the LayerNorm first, no dropout and
+    the tanh GeLU, in fp64 on the CPU, given the same weights and the causal
+    (per-document) mask, with its gradients by autograd.  Every output and
+    gradient of the oracle must agree to fp64 rounding."""
+    cfg = synth.get_config(name).replace(affine_random=True)
+    data = synth.generate(cfg)
+    T, h = cfg.tokens, cfg.hidden
+    p = {k: torch.as_tensor(oracle.to64(v)) for k, v in data.items()
+         if k not in ("cu_seqlens", "targets")}
+    layer = torch.nn.TransformerEncoderLayer(
+        d_model=h, nhead=cfg.heads, dim_feedforward=cfg.ffn, dropout=0.0,
+        activation=lambda u: F.gelu(u, approximate="tanh"), layer_norm_eps=cfg.eps,
+        batch_first=True, norm_first=True, dtype=torch.float64)
+    layer.train()
+    with torch.no_grad():
+        layer.self_attn.in_proj_weight.copy_(torch.cat([p["wq"], p["wk"], p["wv"]]))
+        layer.self_attn.in_proj_bias.copy_(p["bqkv"])
+        layer.self_attn.out_proj.weight.copy_(p["wo"])
+        layer.self_attn.out_proj.bias.copy_(p["bo"])
+        layer.linear1.weight.copy_(p["w1"])
+        layer.linear1.bias.copy_(p["b1"])
+        layer.linear2.weight.copy_(p["w2"])
+        layer.linear2.bias.copy_(p["b2"])
+        layer.norm1.weight.copy_(p["ln1_g"])
+        layer.norm1.bias.copy_(p["ln1_b"])
+        layer.norm2.weight.copy_(p["ln2_g"])
+        layer.norm2.bias.copy_(p["ln2_b"])
+    starts = oracle.doc_starts(data["cu_seqlens"], T)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    blocked = torch.as_tensor(~((j <= i) & (j >= starts[:, None])))  # True: not attended
+    x = p["x"].clone().requires_grad_(True)
+    y = layer(x[None], src_mask=blocked)[0]
+    (y * p["dy"]).sum().backward()
+    c = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts)
+    g = oracle.layer_backward(data, c, data["dy"], cfg.heads, starts)
+
+    def close(a, b, what):
+        a = a.detach().numpy() if isinstance(a, torch.Tensor) else a
+        err = np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel())
+        assert err <= 1e-10, f"{what}: rel {err:.2e}"
+    close(y, c["y"], "y")
+    close(x.grad, g["dx"], "dx")
+    sa = layer.self_attn
+    close(sa.in_proj_weight.grad, np.concatenate([g["dwq"], g["dwk"], g["dwv"]]), "dWqkv")
+    close(sa.in_proj_bias.grad, g["dbqkv"], "dbqkv")
+    close(sa.out_proj.weight.grad, g["dwo"], "dWo")
+    close(sa.out_proj.bias.grad, g["dbo"], "dbo")
+    close(layer.linear1.weight.grad, g["dw1"], "dW1")
+    close(layer.linear1.bias.grad, g["db1"], "db1")
+    close(layer.linear2.weight.grad, g["dw2"], "dW2")
+    close(layer.linear2.bias.grad, g["db2"], "db2")
+    close(layer.norm1.weight.grad, g["dln1_g"], "dln1_g")
+    close(layer.norm1.bias.grad, g["dln1_b"], "dln1_b")
+    close(layer.norm2.weight.grad, g["dln2_g"], "dln2_g")
+    close(layer.norm2.bias.grad, g["dln2_b"], "dln2_b")
+
+
 @pytest.mark.parametrize("tp,swiglu", [(1, False), (2, False), (4, False), (2, True), (4, True)])
 def test_column_row_split_is_exact(tp, swiglu):
     """Sum over ranks of the row-parallel partials equals the unsharded product."""
