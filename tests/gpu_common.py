@@ -34,13 +34,15 @@ def rel(got, ref) -> float:
 # Per-row bound: every row of a 2-D tensor (a token, a head's lse row, an
 # output feature of a weight gradient) must itself be within ROW_MULT x tol
 # of the oracle's row, relative to the larger of the row's own norm and
-# ROW_FLOOR x the tensor's RMS row norm (rows whose exact value is near zero,
-# such as the query gradient of a document's first token, are measured
-# against the tensor's scale).  A wrong row or tile, which the per-tensor
-# Frobenius error of a [2048, 4096] tensor could dilute below tol, gives a
-# row error near 1.
+# ROW_FLOOR x the tensor's RMS row norm.  Rows much smaller than the tensor's
+# scale are measured against that scale: the query gradient of a document's
+# second token, for one, is P0 P1 (dP0 - dP1)(k0 - k1)/sqrt(d), tiny when one
+# key dominates, while its rounding error (D = rowsum(dO * O) from the
+# stored O) is not.  A wrong row or tile, which the per-tensor Frobenius
+# error of a [2048, 4096] tensor could dilute below tol, gives a row error
+# near 1.
 ROW_MULT = 3.0
-ROW_FLOOR = 0.1
+ROW_FLOOR = 0.5
 
 
 def check(name: str, got, ref, tol: float, report: Dict[str, float], floor: float = 0.0) -> None:
