@@ -244,6 +244,23 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                  const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* The same attention backward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it takes no workspace.  Its two fp32 rows per local
+ * head and token live in a fixed 16 MiB device buffer of the library, one
+ * per GPU, held until the process ends; the call itself allocates nothing.
+ * Needs 8 * a_l * T <= 16 MiB (a_l * T <= 2^21), else MTP_ERR_WORKSPACE
+ * before any launch.  The buffer's device address is looked up on the first
+ * call on each device (the current device, which must be the stream's).
+ * Every call on one GPU shares that buffer and keeps the previous call's
+ * contents (nothing in it needs clearing: the call writes every row it
+ * reads), so calls that overlap in time on one GPU, on different streams or
+ * from different host threads, race; serialise them.  Results are
+ * bit-identical to mtp_attn_bwd's.                                           */
+int mtp_attn_bwd_noalloc(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
+                         const float* lse, const void* dctx, void* dqkv,
+                         const int32_t* cu_seqlens, int32_t n_seqs, void* stream);
+
 /* ---------------------------------------------------------- FP8 GEMMs
  * Forward linear maps with E4M3 operands and one fp32 scale per tensor (FP8
  * among the training precisions of page "Megatron-LM / Megatron Core README

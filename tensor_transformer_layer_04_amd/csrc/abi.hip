@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "mtp.h"
 
@@ -344,6 +346,61 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, c
   if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
+  mtp::AttnDesc a{};
+  a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
+  a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
+  a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
+  a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
+  return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));
+}
+
+// The attention backward for callers that cannot allocate: its preprocess
+// rows (D and lse * log2(e), two fp32 rows of T per local head) go to this
+// fixed device buffer instead of a caller workspace.  Every GPU the library
+// runs on holds its own copy until the process ends.
+}  // extern "C"
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  Host code passes this
+// address, never the array's name, to kernels.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MTP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MTP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MTP_OK;
+}
+}  // namespace
+extern "C" {
+
+int mtp_attn_bwd_noalloc(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
+                         const float* lse, const void* dctx, void* dqkv,
+                         const int32_t* cu_seqlens, int32_t n_seqs, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
+    return MTP_ERR_INVALID_ARG;
+  if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
+  const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
+  if (need > kNoAllocScratchBytes) return MTP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MTP_OK) return st;
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
   a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);

@@ -55,6 +55,7 @@ _SIGS = {
                            + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
     "mtp_attn_fwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int32, _VP]),
     "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
+    "mtp_attn_bwd_noalloc": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP]),
     "mtp_quantize_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 7 + [_VP]),
     "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4
@@ -185,6 +186,11 @@ def mtp_attn_bwd(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, ws, ws_byt
     return _call("mtp_attn_bwd", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
                  _addr(dctx), _addr(dqkv), _addr(cu_seqlens), int(n_seqs), _addr(ws), ws_bytes,
                  _stream(stream))
+
+
+def mtp_attn_bwd_noalloc(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, stream=None):
+    return _call("mtp_attn_bwd_noalloc", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
+                 _addr(dctx), _addr(dqkv), _addr(cu_seqlens), int(n_seqs), _stream(stream))
 
 
 def mtp_quantize_fp8(desc, x, n, q, scale, stream=None):

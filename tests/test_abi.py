@@ -197,3 +197,15 @@ def test_oversize_operands_refused_before_any_launch():
                             1 << 40, None) == U
     assert lib.mtp_attn_fwd_block(ctypes.byref(da), FAKE, 0, 1024, 0, 1024, FAKE, FAKE, None,
                                   0, None) == U
+
+
+def test_attn_bwd_noalloc_rejects_oversize_before_launch():
+    """The attention backward without a workspace: a_l * T above 2^21 does
+    not fit its 16 MiB device buffer, so it returns MTP_ERR_WORKSPACE before
+    any launch (the pointers are never dereferenced)."""
+    lib = mtp.lib()
+    d = mtp.make_desc(2048, 16, 0, 1, 0, (1 << 17) + 8, 1, mtp.MTP_BF16)
+    assert lib.mtp_attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                    None) == mtp.MTP_ERR_WORKSPACE
+    assert lib.mtp_attn_bwd_noalloc(ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, None, 0,
+                                    None) == mtp.MTP_ERR_INVALID_ARG
