@@ -264,7 +264,8 @@ int mtp_attn_bwd_noalloc(const mtp_shard_desc* desc, const void* qkv, const void
 /* ---------------------------------------------------------- FP8 GEMMs
  * Forward linear maps with E4M3 operands and one fp32 scale per tensor (FP8
  * among the training precisions of page "Megatron-LM / Megatron Core README
- * digest", §2; reading: OCP E4M3 without infinities, s = amax / 448), on
+ * digest", §0, and the --enable-fp8 flag of page "Megatron-LM 3D parallelism
+ * guide", §5.1; reading: OCP E4M3 without infinities, s = amax / 448), on
  * the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4).  bf16 shards
  * only, else MTP_ERR_UNSUPPORTED.
  *

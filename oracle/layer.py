@@ -28,6 +28,12 @@ parallelism guide", §3.3 launch flags ``--swiglu --disable-bias-linear``):
 and its backward by the chain rule.  The rank view (which slice of each
 tensor a given rank computes) is in ``rank_view``.
 
+With ``fp8=True`` the same layer runs its twelve products on FP8 codes with
+per-tensor scales (``oracle.fp8``): each forward map on the E4M3 codes of
+its input and weight, each data and weight gradient on the E5M2 codes of the
+incoming gradient and the forward's E4M3 codes; everything else (LayerNorm,
+attention, GeLU, residuals, bias gradients) stays as above.
+
 Readings where the pages are silent (each is a stated choice, not a fact of the pages):
 pre-LN; LayerNorm with population variance and eps inside the square root;
 score scale 1/sqrt(head_dim); the mask keeps key j for query i iff
@@ -260,42 +266,71 @@ def _params64(params: Dict) -> Dict[str, np.ndarray]:
             if k not in ("x", "dy", "targets", "cu_seqlens", "emb")}
 
 
-def layer_forward(params: Dict, x, heads: int, eps: float, starts) -> Dict[str, np.ndarray]:
-    """Forward of the unsharded pre-LN layer; returns every intermediate."""
+def _fwd_product(c, name, x, w, b, fp8: bool):
+    """y = x W^T + b, or on FP8 codes (E4M3 x and W, per-tensor scales),
+    whose codes are kept in c["fp8"][name] for the backward."""
+    if not fp8:
+        return linear(x, w, b)
+    from . import fp8 as f8
+    qx, sx = f8.quantize_per_tensor(x, "e4m3")
+    qw, sw = f8.quantize_per_tensor(w, "e4m3")
+    c.setdefault("fp8", {})[name] = {"qx": qx, "sx": sx, "qw": qw, "sw": sw}
+    return f8.fp8_linear(qx, sx, qw, sw, b)
+
+
+def layer_forward(params: Dict, x, heads: int, eps: float, starts,
+                  fp8: bool = False) -> Dict[str, np.ndarray]:
+    """Forward of the unsharded pre-LN layer; returns every intermediate.
+    ``fp8``: the four linear maps on FP8 codes (see the module docstring)."""
     p = _params64(params)
     x = to64(x)
     h = x.shape[1]
     c: Dict[str, np.ndarray] = {"x": x}
+    if fp8 and "w3" in p:
+        raise ValueError("the FP8 reading covers the GeLU FFN only")
     c["ln1"], c["mu1"], c["rstd1"] = layernorm(x, p["ln1_g"], p["ln1_b"], eps)
     wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
-    c["qkv"] = linear(c["ln1"], wqkv, p["bqkv"])
+    c["qkv"] = _fwd_product(c, "qkv", c["ln1"], wqkv, p["bqkv"], fp8)
     q, k, v = c["qkv"][:, :h], c["qkv"][:, h:2 * h], c["qkv"][:, 2 * h:]
     c["ctx"], c["lse"] = attention_forward(q, k, v, heads, starts)
-    c["y1"] = x + linear(c["ctx"], p["wo"], p["bo"])
+    c["y1"] = x + _fwd_product(c, "proj", c["ctx"], p["wo"], p["bo"], fp8)
     c["ln2"], c["mu2"], c["rstd2"] = layernorm(c["y1"], p["ln2_g"], p["ln2_b"], eps)
     if "w3" in p:
         c["u"] = linear(c["ln2"], p["w1"])
         c["u3"] = linear(c["ln2"], p["w3"])
         c["g"] = silu(c["u"]) * c["u3"]
     else:
-        c["u"] = linear(c["ln2"], p["w1"], p["b1"])
+        c["u"] = _fwd_product(c, "fc1", c["ln2"], p["w1"], p["b1"], fp8)
         c["g"] = gelu_tanh(c["u"])
-    c["y"] = c["y1"] + linear(c["g"], p["w2"], p["b2"])
+    c["y"] = c["y1"] + _fwd_product(c, "fc2", c["g"], p["w2"], p["b2"], fp8)
     return c
+
+
+def _bwd_products(c, gr, name, dy, x, w):
+    """(dy W, dy^T x): the data and weight gradients of y = x W^T, or on FP8
+    codes: dy in E5M2 (codes kept in gr["fp8"][name]) with the forward's E4M3
+    codes of W and x."""
+    if "fp8" not in c:
+        return dy @ w, dy.T @ x
+    from . import fp8 as f8
+    fw = c["fp8"][name]
+    qd, sd = f8.quantize_per_tensor(dy, "e5m2")
+    gr.setdefault("fp8", {})[name] = {"qdy": qd, "sdy": sd}
+    return f8.fp8_dgrad(qd, sd, fw["qw"], fw["sw"]), f8.fp8_wgrad(qd, sd, fw["qx"], fw["sx"])
 
 
 def layer_backward(params: Dict, cache: Dict[str, np.ndarray], dy, heads: int,
                    starts) -> Dict[str, np.ndarray]:
-    """Backward of ``layer_forward`` for upstream gradient dy (chain rule)."""
+    """Backward of ``layer_forward`` for upstream gradient dy (chain rule);
+    FP8 products when the forward ran with ``fp8``."""
     p = _params64(params)
     dy = to64(dy)
     c = cache
     h = dy.shape[1]
     gr: Dict[str, np.ndarray] = {}
     # MLP: y = y1 + g W2^T + b2
-    gr["dw2"] = dy.T @ c["g"]
+    dg, gr["dw2"] = _bwd_products(c, gr, "fc2", dy, c["g"], p["w2"])
     gr["db2"] = dy.sum(axis=0)
-    dg = dy @ p["w2"]
     if "w3" in p:
         du = dg * c["u3"] * silu_grad(c["u"])
         du3 = dg * silu(c["u"])
@@ -306,29 +341,25 @@ def layer_backward(params: Dict, cache: Dict[str, np.ndarray], dy, heads: int,
     else:
         du = dg * gelu_tanh_grad(c["u"])
         gr["du"] = du
-        gr["dw1"] = du.T @ c["ln2"]
+        dln2, gr["dw1"] = _bwd_products(c, gr, "fc1", du, c["ln2"], p["w1"])
         gr["db1"] = du.sum(axis=0)
-        dln2 = du @ p["w1"]
     gr["dln2"] = dln2
     dy1_ln, gr["dln2_g"], gr["dln2_b"] = layernorm_backward(dln2, c["y1"], p["ln2_g"],
                                                             c["mu2"], c["rstd2"])
     dy1 = dy + dy1_ln
     gr["dy1"] = dy1
     # attention block: y1 = x + ctx Wo^T + bo
-    gr["dwo"] = dy1.T @ c["ctx"]
+    dctx, gr["dwo"] = _bwd_products(c, gr, "proj", dy1, c["ctx"], p["wo"])
     gr["dbo"] = dy1.sum(axis=0)
-    dctx = dy1 @ p["wo"]
     gr["dctx"] = dctx
     q, k, v = c["qkv"][:, :h], c["qkv"][:, h:2 * h], c["qkv"][:, 2 * h:]
     dq, dk, dv = attention_backward(q, k, v, dctx, heads, starts)
     dqkv = np.concatenate([dq, dk, dv], axis=1)
     gr["dqkv"] = dqkv
-    gr["dwq"] = dq.T @ c["ln1"]
-    gr["dwk"] = dk.T @ c["ln1"]
-    gr["dwv"] = dv.T @ c["ln1"]
-    gr["dbqkv"] = dqkv.sum(axis=0)
     wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
-    dln1 = dqkv @ wqkv
+    dln1, dwqkv = _bwd_products(c, gr, "qkv", dqkv, c["ln1"], wqkv)
+    gr["dwq"], gr["dwk"], gr["dwv"] = dwqkv[:h], dwqkv[h:2 * h], dwqkv[2 * h:]
+    gr["dbqkv"] = dqkv.sum(axis=0)
     gr["dln1"] = dln1
     dx_ln, gr["dln1_g"], gr["dln1_b"] = layernorm_backward(dln1, c["x"], p["ln1_g"],
                                                            c["mu1"], c["rstd1"])
@@ -389,22 +420,33 @@ def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]]
     fc = slice(r * fl, (r + 1) * fl)
     qkv_cols = np.r_[r * hl:(r + 1) * hl, h + r * hl:h + (r + 1) * hl,
                      2 * h + r * hl:2 * h + (r + 1) * hl]
+    # operands of the partial products: the exact tensors, or with FP8 the
+    # dequantized codes (whose scales belong to the whole tensor)
+    f8 = fwd.get("fp8")
+    g8 = grads.get("fp8") if grads is not None else None
+
+    def opnd(exact, name, key):
+        if f8 is None:
+            return exact
+        src = g8[name] if key == "qdy" else f8[name]
+        return src[key] * float(src["sdy" if key == "qdy" else "s" + key[1]])
+    wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
     v: Dict[str, np.ndarray] = {}
     v["qkv"] = fwd["qkv"][:, qkv_cols]
     v["ctx"] = fwd["ctx"][:, hc]
     v["lse"] = fwd["lse"][r * (heads // tp):(r + 1) * (heads // tp)]
-    v["proj_partial"] = fwd["ctx"][:, hc] @ p["wo"][:, hc].T
+    v["proj_partial"] = opnd(fwd["ctx"], "proj", "qx")[:, hc] @ opnd(p["wo"], "proj", "qw")[:, hc].T
     v["u"] = fwd["u"][:, fc]
     if "u3" in fwd:
         v["u3"] = fwd["u3"][:, fc]
     v["g"] = fwd["g"][:, fc]
-    v["fc2_partial"] = fwd["g"][:, fc] @ p["w2"][:, fc].T
+    v["fc2_partial"] = opnd(fwd["g"], "fc2", "qx")[:, fc] @ opnd(p["w2"], "fc2", "qw")[:, fc].T
     if grads is not None:
-        wqkv_r = np.concatenate([p["wq"][hc], p["wk"][hc], p["wv"][hc]], axis=0)
+        wqkv_r = opnd(wqkv, "qkv", "qw")[qkv_cols]
         v["du"] = grads["du"][:, fc]
         v["dw2"] = grads["dw2"][:, fc]
         v["dw1"] = grads["dw1"][fc]
-        v["fc1_dx_partial"] = grads["du"][:, fc] @ p["w1"][fc]
+        v["fc1_dx_partial"] = opnd(grads["du"], "fc1", "qdy")[:, fc] @ opnd(p["w1"], "fc1", "qw")[fc]
         if "w3" in p:
             v["du3"] = grads["du3"][:, fc]
             v["dw3"] = grads["dw3"][fc]
@@ -416,5 +458,5 @@ def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]]
         v["dqkv"] = grads["dqkv"][:, qkv_cols]
         v["dwqkv"] = np.concatenate([grads["dwq"][hc], grads["dwk"][hc], grads["dwv"][hc]], axis=0)
         v["dbqkv"] = grads["dbqkv"][qkv_cols]
-        v["qkv_dx_partial"] = grads["dqkv"][:, qkv_cols] @ wqkv_r
+        v["qkv_dx_partial"] = opnd(grads["dqkv"], "qkv", "qdy")[:, qkv_cols] @ wqkv_r
     return v

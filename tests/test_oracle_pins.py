@@ -458,3 +458,150 @@ def test_quantize_per_tensor_scale_and_linear():
     brute = np.array([[sum(q[i, k] * qw[j, k] for k in range(64)) for j in range(9)]
                       for i in range(37)]) * (float(s) * float(sw))
     assert np.max(np.abs(y - brute)) <= 1e-12 * np.max(np.abs(brute))
+
+
+def test_e5m2_round_matches_torch_and_format():
+    """E5M2 rounding (the gradient format) against torch's float8_e5m2
+    conversion on every finite value, every tie between neighbours and
+    random values, and the format's closed forms."""
+    from oracle import fp8
+    codes = np.arange(256)
+    vals = fp8.fp8_decode(codes, "e5m2")
+    finite = np.sort(np.unique(vals[np.isfinite(vals)]))
+    assert finite.max() == 57344.0 and finite.min() == -57344.0
+    assert np.min(finite[finite > 0]) == 2.0 ** -16
+    assert np.isinf(fp8.fp8_decode(np.array([0x7C]), "e5m2")[0])
+    assert np.isnan(fp8.fp8_decode(np.array([0x7D]), "e5m2")[0])
+    mids = (finite[1:] + finite[:-1]) / 2
+    r = rng(23)
+    grid = np.concatenate([finite, mids, r.uniform(-57344, 57344, 4000),
+                           r.uniform(-1e-3, 1e-3, 4000)])
+    ref = torch.tensor(grid, dtype=torch.float64).to(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(fp8.fp8_round(grid, "e5m2"), ref)
+    enc = fp8.fp8_encode(finite, "e5m2")
+    assert np.array_equal(fp8.fp8_decode(enc, "e5m2"), finite)
+    assert fp8.fp8_encode(np.array([57344.0]), "e5m2")[0] == 0x7B
+    assert fp8.fp8_encode(np.array([-2.0 ** -16]), "e5m2")[0] == 0x81
+    # the two formats share nothing but the sign bit position
+    assert fp8.fp8_encode(np.array([1.0]), "e5m2")[0] == 0x3C
+    assert fp8.fp8_encode(np.array([1.0]), "e4m3")[0] == 0x38
+
+
+def test_quantize_e5m2_and_gradient_products():
+    from oracle import fp8
+    r = rng(24)
+    dy = r.normal(size=(33, 40)).astype(np.float32) * 0.01
+    q, s = fp8.quantize_per_tensor(dy, "e5m2")
+    assert s == np.float32(np.max(np.abs(dy)) / np.float32(57344.0))
+    assert np.max(np.abs(q)) == 57344.0
+    big = np.abs(dy) > 2.0 ** -14 * s
+    assert np.all(np.abs(q * s - dy)[big] <= np.abs(dy)[big] * 2.0 ** -3 * 1.0001)
+    w = r.normal(size=(40, 24)).astype(np.float32)       # y = x W^T with W [40, 24]
+    qw, sw = fp8.quantize_per_tensor(w, "e4m3")
+    x = r.normal(size=(33, 24)).astype(np.float32)
+    qx, sx = fp8.quantize_per_tensor(x, "e4m3")
+    dx = fp8.fp8_dgrad(q, s, qw, sw)
+    dw = fp8.fp8_wgrad(q, s, qx, sx)
+    brute_dx = np.array([[sum(q[i, n] * qw[n, k] for n in range(40)) for k in range(24)]
+                         for i in range(33)]) * (float(s) * float(sw))
+    brute_dw = np.array([[sum(q[t, n] * qx[t, k] for t in range(33)) for k in range(24)]
+                         for n in range(40)]) * (float(s) * float(sx))
+    assert np.max(np.abs(dx - brute_dx)) <= 1e-12 * np.max(np.abs(brute_dx))
+    assert np.max(np.abs(dw - brute_dw)) <= 1e-12 * np.max(np.abs(brute_dw))
+
+
+def _torch_fp8_quantize(x, fmt):
+    """Per-tensor quantization written with torch's own float8 casts."""
+    dt, mx = ((torch.float8_e4m3fn, 448.0) if fmt == "e4m3" else (torch.float8_e5m2, 57344.0))
+    x32 = x.detach().float()
+    amax = x32.abs().max()
+    s = amax / torch.tensor(mx, dtype=torch.float32) if amax > 0 else torch.tensor(1.0)
+    v = (x32 / s).clamp(-mx, mx)
+    return v.to(dt).to(torch.float64), s.double()
+
+
+class _TorchFP8Linear(torch.autograd.Function):
+    """y = x W^T + b on E4M3 codes; gradients on the E5M2 codes of dy."""
+
+    @staticmethod
+    def forward(ctx, x, w, b):
+        qx, sx = _torch_fp8_quantize(x, "e4m3")
+        qw, sw = _torch_fp8_quantize(w, "e4m3")
+        ctx.save_for_backward(qx, sx, qw, sw)
+        return (qx @ qw.T) * (sx * sw) + b
+
+    @staticmethod
+    def backward(ctx, gy):
+        qx, sx, qw, sw = ctx.saved_tensors
+        qg, sg = _torch_fp8_quantize(gy, "e5m2")
+        return (qg @ qw) * (sg * sw), (qg.T @ qx) * (sg * sx), gy.sum(0)
+
+
+@pytest.mark.parametrize("name", ["tiny_tp2", "small_varlen_tp1"])
+def test_fp8_layer_matches_torch_autograd(name):
+    """The FP8 layer (forward and backward) against an independent build of
+    it from torch library pieces: layer_norm, scaled_dot_product_attention
+    with the same mask, tanh GeLU, autograd for the chain rule, and an FP8
+    linear function on torch's float8 casts.  Agreement to fp64 rounding."""
+    import torch.nn.functional as F
+    cfg = synth.get_config(name).replace(affine_random=True, dtype="f32")
+    data = synth.generate(cfg)
+    T, h, a = cfg.tokens, cfg.hidden, cfg.heads
+    d = h // a
+    P = {k: torch.as_tensor(oracle.to64(v)).clone().requires_grad_(True) for k, v in data.items()
+         if k not in ("cu_seqlens", "targets", "x", "dy")}
+    x = torch.as_tensor(oracle.to64(data["x"])).clone().requires_grad_(True)
+    dy = torch.as_tensor(oracle.to64(data["dy"]))
+    starts = oracle.doc_starts(data["cu_seqlens"], T)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    allowed = torch.as_tensor((j <= i) & (j >= starts[:, None]))
+    wqkv = torch.cat([P["wq"], P["wk"], P["wv"]])
+    ln1 = F.layer_norm(x, (h,), P["ln1_g"], P["ln1_b"], cfg.eps)
+    qkv = _TorchFP8Linear.apply(ln1, wqkv, P["bqkv"])
+    q, k, v = (qkv[:, n * h:(n + 1) * h].reshape(T, a, d).transpose(0, 1) for n in range(3))
+    ctx = F.scaled_dot_product_attention(q, k, v, attn_mask=allowed).transpose(0, 1).reshape(T, h)
+    y1 = x + _TorchFP8Linear.apply(ctx, P["wo"], P["bo"])
+    ln2 = F.layer_norm(y1, (h,), P["ln2_g"], P["ln2_b"], cfg.eps)
+    g = F.gelu(_TorchFP8Linear.apply(ln2, P["w1"], P["b1"]), approximate="tanh")
+    y = y1 + _TorchFP8Linear.apply(g, P["w2"], P["b2"])
+    (y * dy).sum().backward()
+    c = oracle.layer_forward(data, data["x"], a, cfg.eps, starts, fp8=True)
+    gr = oracle.layer_backward(data, c, data["dy"], a, starts)
+    exact = oracle.layer_forward(data, data["x"], a, cfg.eps, starts)
+
+    def close(t, ref, what, tol=1e-10):
+        t = t.detach().numpy()
+        err = np.linalg.norm((t - ref).ravel()) / np.linalg.norm(ref.ravel())
+        assert err <= tol, f"{what}: rel {err:.2e}"
+    close(y, c["y"], "y")
+    close(x.grad, gr["dx"], "dx")
+    for pn, gn in PARAM_GRADS[1:]:
+        close(P[pn].grad, gr[gn], gn)
+    # the FP8 layer is not the exact one, but within the formats' error
+    e = np.linalg.norm(c["y"] - exact["y"]) / np.linalg.norm(exact["y"])
+    assert 1e-4 < e < 5e-2, e
+
+
+@pytest.mark.parametrize("tp", [2, 4])
+def test_fp8_column_row_split_is_exact(tp):
+    """With whole-tensor scales the ranks' FP8 partials still sum to the
+    unsharded FP8 products (forward and backward)."""
+    cfg, data, starts = _tiny(seed=4)
+    c = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts, fp8=True)
+    g = oracle.layer_backward(data, c, data["dy"], cfg.heads, starts)
+    p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
+    views = [oracle.rank_view(c, g, p64, cfg.heads, tp, r) for r in range(tp)]
+    proj = c["y1"] - p64["x"] - p64["bo"]
+    fc2 = c["y"] - c["y1"] - p64["b2"]
+    for key, ref in (("proj_partial", proj), ("fc2_partial", fc2)):
+        tot = sum(v[key] for v in views)
+        assert np.max(np.abs(tot - ref)) <= 1e-12 * np.max(np.abs(ref)), key
+    # the column-dgrad partials sum to the FP8 input gradients of FC1 and QKV
+    from oracle import fp8
+    f8, g8 = c["fp8"], g["fp8"]
+    dln2 = fp8.fp8_dgrad(g8["fc1"]["qdy"], g8["fc1"]["sdy"], f8["fc1"]["qw"], f8["fc1"]["sw"])
+    dln1 = fp8.fp8_dgrad(g8["qkv"]["qdy"], g8["qkv"]["sdy"], f8["qkv"]["qw"], f8["qkv"]["sw"])
+    for key, ref in (("fc1_dx_partial", dln2), ("qkv_dx_partial", dln1)):
+        tot = sum(v[key] for v in views)
+        assert np.max(np.abs(tot - ref)) <= 1e-12 * np.max(np.abs(ref)), key
