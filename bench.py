@@ -47,13 +47,15 @@ FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
 CALL_TAGS = ("ln1", "qkv_fwd", "attn_fwd", "proj_fwd", "sum_proj_ln2", "fc1_fwd", "fc2_fwd",
              "sum_fc2", "fc2_dgrad", "fc2_wgrad", "fc2_bias", "fc1_dgrad", "fc1_wgrad", "ln2_bwd",
              "proj_dgrad", "proj_wgrad", "proj_bias", "attn_bwd", "qkv_dgrad", "qkv_wgrad",
-             "ln1_bwd")
+             "ln1_bwd", "quant", "quant_w")
 HEAD_TAGS = ("vocab_fwd", "ce_stats", "ce_combine", "ce_bwd", "vocab_bwd", "sum_vocab_dy")
 PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")
 FWD_KERNEL = "gemm_bf16_kernel, forward layout (k-major A and B, bf16 C, fused bias/GeLU)"
 WGRAD_KERNEL = "gemm_bf16_kernel, weight-gradient layout (m-major A, n-major B, fp32 C)"
 FP8_KERNEL = "gemm_bf16_kernel<..., F8> (E4M3 operands, forward layout)"
+FP8_WGRAD_KERNEL = ("gemm_bf16_kernel<..., F8, A5> (E5M2 gradient x E4M3 activation codes, "
+                    "weight gradient, fp32 C)")
 
 
 def seq_pairs(cu) -> int:
@@ -97,20 +99,21 @@ def traffic_for(kernel: str):
     return t.get("bytes_per_launch", {}).get(kernel)
 
 
-def roofline(kernel, tags, probes, flops, ms, steps) -> dict:
+def roofline(kernel, tags, probes, flops, ms, steps, peak=None) -> dict:
     """Roofline entry of one GEMM family: model flops of its probed launches
     over their summed HIP-event durations (``steps``: the probed steps)."""
     dur_ms = sum(a.elapsed_time(b) for t in tags for a, b in probes[t])
     launches = sum(len(probes[t]) for t in tags)
     fl = sum(flops[t] * len(probes[t]) for t in tags)
     achieved = fl / (dur_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if peak is None else peak
     return {
         "kernel": kernel,
         "bound": "mfma",
         "achieved": round(achieved, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "frac": round(achieved / peak, 4),
         "traffic": traffic_for(kernel),
         "launches_per_step": launches // max(steps, 1),
         "avg_launch_us": round(1e3 * dur_ms / max(launches, 1), 2),
@@ -165,7 +168,8 @@ def cpu_baseline(cfg, data) -> dict:
     passes, total = 0, 0.0
     while passes < 4 and (passes == 0 or total < 10.0):
         t0 = time.perf_counter()
-        c = oracle.layer_forward(p64, x64, cfg.heads, cfg.eps, starts)
+        c = oracle.layer_forward(p64, x64, cfg.heads, cfg.eps, starts,
+                                 fp8=bool(getattr(cfg, "fp8", False)))
         oracle.layer_backward(p64, c, dy64, cfg.heads, starts)
         total += time.perf_counter() - t0
         passes += 1
@@ -431,14 +435,18 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": ("fp8/bf16" if getattr(cfg, "fp8", False)
+                  else "bf16" if cfg.dtype == "bf16" else "f32"),
         "data": "synthetic: seeded x, dy ~ N(0,1), weights ~ N(0,0.02), biases 0, LN gamma 1",
         "config": {
             "workload": f"{cfg.name}: TP rank {args.rank} of {cfg.tp}, pre-LN layer shard"
                         + (" with sequence parallelism" if L.sp else "")
                         + (f", attention over {L.cp} context-parallel chunks"
                            f" ({len(L.cp_pairs())} off-diagonal block pairs)" if L.cp > 1 else "")
-                        + (" + vocab-parallel CE head" if cfg.vocab else "") + " fwd+bwd",
+                        + (" + vocab-parallel CE head" if cfg.vocab else "")
+                        + (", twelve GEMMs on FP8 codes (E4M3 forward, E5M2 gradients, per-tensor "
+                           "scales; weights quantized inside the step)" if L.fp8 else "")
+                        + " fwd+bwd",
             "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn, "tp": cfg.tp,
             "rank": args.rank, "seq_len": cfg.seq_len, "micro_batch": cfg.micro_batch,
             "tokens": cfg.tokens, "global_batch": cfg.micro_batch,
@@ -459,11 +467,13 @@ def main(argv=None) -> int:
         "ms_per_step_less_forward_tp_sums": (
             round(ms - 1e-3 * (call_us["sum_fc2"] + call_us["sum_proj_ln2"] - call_us["ln1"]), 4)
             if all(k in call_us for k in ("sum_fc2", "sum_proj_ln2", "ln1")) else None),
-        "roofline": roofline(FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms, len(probed)),
-        "roofline_wgrad_overlapped": roofline(WGRAD_KERNEL, WGRAD_TAGS, probes, fl["call"], ms,
-                                              len(probed)),
+        "roofline": roofline(FP8_KERNEL if L.fp8 else FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms,
+                             len(probed), PEAK_FP8_TFLOPS if L.fp8 else None),
+        "roofline_wgrad_overlapped": roofline(FP8_WGRAD_KERNEL if L.fp8 else WGRAD_KERNEL,
+                                              WGRAD_TAGS, probes, fl["call"], ms, len(probed),
+                                              PEAK_FP8_TFLOPS if L.fp8 else None),
     }
-    if cfg.dtype == "bf16" and not cfg.swiglu and cfg.tokens % 8 == 0:
+    if cfg.dtype == "bf16" and not cfg.swiglu and not L.fp8 and cfg.tokens % 8 == 0:
         # the same shard's forward GEMMs on the FP8 matrix cores (not part of the step)
         out["fp8_forward_gemms"] = fp8_gemm_probe(cfg, L)
     if not args.no_cpu_baseline:

@@ -89,6 +89,9 @@ typedef enum {
     MTP_OP_VOCAB_CE = 4
 } mtp_op;
 
+/* FP8 formats (see the FP8 section below). */
+typedef enum { MTP_FP8_E4M3 = 0, MTP_FP8_E5M2 = 1 } mtp_fp8_format;
+
 /*
  * The problem statement of one shard.  Divisibility follows the pages
  * (page "Megatron-LM 3D parallelism guide", §3.2: hidden size and head
@@ -288,6 +291,48 @@ int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8
 int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
                        const float* x_scale, const uint8_t* w8, const float* w_scale,
                        const void* b, void* y, void* preact, void* stream);
+
+/* FP8 training step: per-tensor scales shared by every shard of a tensor
+ * (the ranks of a tensor-parallel group agree on the maximum of their
+ * shards' amax), E4M3 codes for activations and weights and E5M2 codes for
+ * gradients (reading of the FP8 precision named in README digest §0 and the
+ * --enable-fp8 flag of guide §5.1, which give no recipe).  Every FP8 GEMM
+ * reads both operands k-major, so the backward takes the transposed codes
+ * that mtp_fp8_quantize writes beside the row-major ones.
+ *
+ * mtp_fp8_amax: amax_parts [1024] fp32 (out) receives partial maxima of |x|
+ *   over the n values of x (dtype bf16, n % 8 == 0; 0 where a part saw no
+ *   value): max |x| is their maximum.  No atomics; the result is the same
+ *   on every call.
+ * mtp_fp8_quantize: the codes of x [rows, cols] (bf16, row-major, cols % 8
+ *   == 0) in format fmt with s = amax / max_fmt (448 for E4M3, 57344 for
+ *   E5M2; 1 when amax is 0), amax the maximum over the n_parts arrays of 1024
+ *   partial maxima in amax_parts (a HOST array of device pointers: one per
+ *   shard of the tensor, 1 <= n_parts <= 16).  Codes are
+ *   round-to-nearest-even(clamp(fl32(x / s), -max, max)).  q [rows, cols]
+ *   and/or q_t [cols, rows] (the transpose; nullable, not both NULL) receive
+ *   them; scale [1] fp32 (out) receives s.  With n = 0 or rows = 0, x, q
+ *   and q_t may be NULL.
+ * mtp_linear_bwd_fp8: the gradients of one of the linear maps of kind
+ *   (QKV, FC1, PROJ, FC2; out x in = 3h_l x h, f_l x h, h x h_l, h x f_l)
+ *   from FP8 codes:
+ *   dx [T, in] dtype (nullable) = (dy8 [T, out] E5M2) (w8_t [in, out] E4M3,
+ *     the transposed codes of W)^T * dy_scale * w_scale, times
+ *     GeLU_tanh'(preact) for FC2 with preact = u [T, f_l] (the FFN's du);
+ *     needs out % 16 == 0;
+ *   dw [out, in] fp32 (nullable; += when accumulate) = (dy8_t [out, T] E5M2,
+ *     the transposed codes of dy) (x8_t [in, T] E4M3, those of the forward
+ *     input)^T * dy_scale * x_scale; needs T % 16 == 0.
+ *   Scales are [1] fp32 device values as written by mtp_fp8_quantize.     */
+int mtp_fp8_amax(const mtp_shard_desc* desc, const void* x, int64_t n, float* amax_parts,
+                 void* stream);
+int mtp_fp8_quantize(const mtp_shard_desc* desc, int fmt, const void* x, int64_t rows,
+                     int64_t cols, const float* const* amax_parts, int32_t n_parts, uint8_t* q,
+                     uint8_t* q_t, float* scale, void* stream);
+int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
+                       const uint8_t* dy8_t, const float* dy_scale, const uint8_t* w8_t,
+                       const float* w_scale, const uint8_t* x8_t, const float* x_scale,
+                       const void* preact, void* dx, float* dw, int accumulate, void* stream);
 
 /* ------------------------------------------ context-parallel attention
  * The sequence split into chunks whose attention runs block pair by block

@@ -64,6 +64,7 @@ class LayerConfig:
     sequence_parallel: bool = False  # per-token work on T/tp row blocks per rank
     swiglu: bool = False         # SwiGLU FFN (gate w1, up w3), no FFN-input bias b1
     context_parallel: int = 1    # attention over this many sequence chunks, pair by pair
+    fp8: bool = False            # the four linear maps and their gradients on FP8 codes
     description: str = ""
 
     @property
@@ -110,6 +111,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         context_parallel=2,
         description="7B-style layer, one TP=2 rank shard, attention as 2 context-parallel "
                     "chunks merged by log-sum-exp, bf16"),
+    "7b_tp2_fp8": LayerConfig(
+        "7b_tp2_fp8", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        fp8=True,
+        description="7B-style layer, one TP=2 rank shard, its twelve GEMMs on FP8 codes (E4M3 "
+                    "activations and weights, E5M2 gradients, per-tensor scales), bf16 elsewhere"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -172,6 +178,14 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_varlen_d64_tp2_cp3": LayerConfig(
         "small_varlen_d64_tp2_cp3", hidden=512, heads=8, ffn=1376, tp=2, seq_len=960,
         dtype="bf16", varlen_tokens=960, doc_min=1, doc_max=400, context_parallel=3),
+    # FP8 layer steps: token counts and reduction widths multiples of 16
+    # (the FP8 GEMMs' 16-byte k chunks), ragged against the tiles otherwise
+    "small_fp8_tp2": LayerConfig(
+        "small_fp8_tp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        affine_random=True, fp8=True),
+    "small_fp8_d64_tp4": LayerConfig(
+        "small_fp8_d64_tp4", hidden=512, heads=8, ffn=2176, tp=4, seq_len=208, dtype="bf16",
+        fp8=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

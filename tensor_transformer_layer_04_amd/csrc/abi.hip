@@ -515,6 +515,87 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
   return hip_status(mtp::gemm_bf16(g, static_cast<hipStream_t>(stream)));
 }
 
+int mtp_fp8_amax(const mtp_shard_desc* desc, const void* x, int64_t n, float* amax_parts,
+                 void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  if (n < 0 || (n & 7)) return MTP_ERR_INVALID_ARG;
+  if ((n > 0 && !ok_ptr(x)) || !ok_ptr(amax_parts)) return MTP_ERR_INVALID_ARG;
+  return hip_status(mtp::fp8_amax(x, n, amax_parts, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_fp8_quantize(const mtp_shard_desc* desc, int fmt, const void* x, int64_t rows,
+                     int64_t cols, const float* const* amax_parts, int32_t n_parts, uint8_t* q,
+                     uint8_t* q_t, float* scale, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  if (fmt != MTP_FP8_E4M3 && fmt != MTP_FP8_E5M2) return MTP_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || (cols & 7) || cols > (int64_t{1} << 30)) return MTP_ERR_INVALID_ARG;
+  if (!amax_parts || n_parts < 1 || n_parts > mtp::kMaxPartials) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_parts; ++i)
+    if (!ok_ptr(amax_parts[i])) return MTP_ERR_INVALID_ARG;
+  // with no rows there is nothing to read or write but the scale
+  if (!ok_opt(x) || !ok_opt(q) || !ok_opt(q_t) || !ok_ptr(scale)) return MTP_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || (!q && !q_t))) return MTP_ERR_INVALID_ARG;
+  if (!fits(rows, cols, 1) || (rows + 127) / 128 > 65535) return MTP_ERR_UNSUPPORTED;
+  return hip_status(mtp::fp8_quantize(fmt == MTP_FP8_E5M2 ? mtp::kFp8E5M2 : mtp::kFp8E4M3, x,
+                                      rows, static_cast<int>(cols), amax_parts, n_parts, q, q_t,
+                                      scale, static_cast<hipStream_t>(stream)));
+}
+
+int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
+                       const uint8_t* dy8_t, const float* dy_scale, const uint8_t* w8_t,
+                       const float* w_scale, const uint8_t* x8_t, const float* x_scale,
+                       const void* preact, void* dx, float* dw, int accumulate, void* stream) {
+  Shard s;
+  int st = check_desc(desc, &s);
+  if (st != MTP_OK) return st;
+  if (!s.bf16) return MTP_ERR_UNSUPPORTED;
+  int64_t out = 0, in = 0;
+  switch (kind) {
+    case MTP_QKV: out = 3LL * s.hl; in = s.h; break;
+    case MTP_FC1: out = s.fl; in = s.h; break;
+    case MTP_PROJ: out = s.h; in = s.hl; break;
+    case MTP_FC2: out = s.h; in = s.fl; break;
+    default: return MTP_ERR_INVALID_ARG;
+  }
+  if (!ok_ptr(dy_scale) || !ok_opt(dx) || !ok_opt(dw) || !ok_opt(preact)) return MTP_ERR_INVALID_ARG;
+  if (preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
+  if (dx && (!ok_ptr(dy8) || !ok_ptr(w8_t) || !ok_ptr(w_scale))) return MTP_ERR_INVALID_ARG;
+  if (dw && (!ok_ptr(dy8_t) || !ok_ptr(x8_t) || !ok_ptr(x_scale))) return MTP_ERR_INVALID_ARG;
+  // 16-byte k chunks: the reduction lengths (out for the data gradient, T
+  // for the weight gradient) must be multiples of 16
+  if ((dx && (out & 15)) || (dw && (s.T & 15))) return MTP_ERR_UNSUPPORTED;
+  if (!fits(s.T, out, 1) || !fits(in, out, 1) || !fits(in, s.T, 1)) return MTP_ERR_UNSUPPORTED;
+  hipStream_t str = static_cast<hipStream_t>(stream);
+  if (dx) {
+    GemmDesc g{};
+    g.A = dy8; g.lda = out; g.a_kmajor = true;
+    g.B = w8_t; g.ldb = out; g.b_kmajor = true;
+    g.M = static_cast<int>(s.T); g.N = static_cast<int>(in); g.K = static_cast<int>(out);
+    g.C = dx; g.ldc = in;
+    g.aux = const_cast<void*>(preact); g.ld_aux = in;
+    g.epi = preact ? mtp::kEpiDGelu : mtp::kEpiStore;
+    g.fp8 = true; g.a_e5m2 = true; g.scale_a = dy_scale; g.scale_b = w_scale;
+    if (mtp::gemm_bf16(g, str) != hipSuccess) return MTP_ERR_HIP;
+  }
+  if (dw) {
+    GemmDesc g{};
+    g.A = dy8_t; g.lda = s.T; g.a_kmajor = true;
+    g.B = x8_t; g.ldb = s.T; g.b_kmajor = true;
+    g.M = static_cast<int>(out); g.N = static_cast<int>(in); g.K = static_cast<int>(s.T);
+    g.C = dw; g.ldc = in;
+    g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
+    g.fp8 = true; g.a_e5m2 = true; g.scale_a = dy_scale; g.scale_b = x_scale;
+    if (mtp::gemm_bf16(g, str) != hipSuccess) return MTP_ERR_HIP;
+  }
+  return MTP_OK;
+}
+
 int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials, int32_t n_partials,
                     const void* bias, const void* residual, void* out, void* stream) {
   Shard s;

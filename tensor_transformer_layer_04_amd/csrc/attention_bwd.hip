@@ -176,8 +176,8 @@ __device__ __forceinline__ void ranked_blocks(const BwdParams& p, int r, int& kb
 // side on the chip.  Per 64-query tile and wave (32 keys, 32 query rows of
 // the tile): S = Q K^T [, dP = dO V^T] with one key per lane, P / dS on the
 // vector units, then the transposed-operand MFMAs.
-template <int D>
-__device__ __forceinline__ void dkv_block(const BwdParams& p, bool want_dk, int kblk, int head,
+template <int D, bool want_dk>
+__device__ __forceinline__ void dkv_block(const BwdParams& p, int kblk, int head,
                                           char* sq0, char* sq1, char* so0, char* so1, char* st0,
                                           char* st1) {
   constexpr int KS = D / 16, DB = D / 32;
@@ -542,8 +542,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_mfma(BwdParams p) {
   ranked_blocks(p, r, kblk, qblk);
   if (role == 1)
     dq_block<D>(p, qblk, head, t0, t1, t2, t3);
+  else if (role == 0)
+    dkv_block<D, true>(p, kblk, head, t0, t1, t2, t3, st0, st1);
   else
-    dkv_block<D>(p, role == 0, kblk, head, t0, t1, t2, t3, st0, st1);
+    dkv_block<D, false>(p, kblk, head, t0, t1, t2, t3, st0, st1);
 }
 
 }  // namespace

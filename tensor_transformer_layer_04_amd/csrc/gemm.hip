@@ -293,14 +293,16 @@ __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, con
   }
 }
 
-// F8: operands are E4M3 bytes staged exactly like bf16 pairs (the host
+// F8: operands are FP8 bytes staged exactly like bf16 pairs (the host
 // passes K and the leading dimensions in 2-byte units), multiplied by
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) in two 64-k steps per
-// 128-byte k-tile; the epilogue applies the two per-tensor scales.
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false>
+// 128-byte k-tile; the epilogue applies the two per-tensor scales.  B is
+// E4M3; A is E4M3, or E5M2 with A5 (the gradients of the backward).
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false,
+          bool A5 = false>
 __global__ void __launch_bounds__(WGM * WGN * 64, (WGM * WGN + 3) / 4)
 gemm_bf16_kernel(GemmParams p) {
-  static_assert(!F8 || (AK && BKM), "FP8 operands: forward layout only");
+  static_assert(!F8 || (AK && BKM), "FP8 operands: k-major only");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -351,8 +353,11 @@ gemm_bf16_kernel(GemmParams p) {
   using FragT = std::conditional_t<F8, i32x8, bf16x8>;
   struct Frags { FragT a[FM], b[FN]; };
   auto mma = [&](const FragT& b, const FragT& a, const f32x16& c) {
+    // the format fields: 0 = E4M3, 1 = E5M2, for the first (B) and second (A)
+    // operand as passed
     if constexpr (F8)
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, A5 ? 1 : 0, 0, 127, 0,
+                                                              127);
     else
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
   };
@@ -539,13 +544,14 @@ gemm_bf16_kernel(GemmParams p) {
       }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false,
+          bool A5 = false>
 hipError_t launch_bf16(const GemmParams& p0, hipStream_t s) {
   GemmParams p = p0;
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   const int blocks = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, F8>), dim3(blocks),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, F8, A5>), dim3(blocks),
                      dim3(WGM * WGN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -634,13 +640,13 @@ int pick_tile_fp8(int M, int N) {
   return best;
 }
 
-template <int EPI>
+template <int EPI, bool A5>
 hipError_t dispatch_fp8(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
-    case kTile256x128: return launch_bf16<256, 128, 4, 2, true, true, EPI, true>(p, s);
-    case kTile128x128: return launch_bf16<128, 128, 2, 2, true, true, EPI, true>(p, s);
-    case kTileF8_256x192: return launch_bf16<256, 192, 4, 2, true, true, EPI, true>(p, s);
-    default: return launch_bf16<128, 256, 2, 4, true, true, EPI, true>(p, s);
+    case kTile256x128: return launch_bf16<256, 128, 4, 2, true, true, EPI, true, A5>(p, s);
+    case kTile128x128: return launch_bf16<128, 128, 2, 2, true, true, EPI, true, A5>(p, s);
+    case kTileF8_256x192: return launch_bf16<256, 192, 4, 2, true, true, EPI, true, A5>(p, s);
+    default: return launch_bf16<128, 256, 2, 4, true, true, EPI, true, A5>(p, s);
   }
 }
 
@@ -743,8 +749,13 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.fp8) {
     // bytes staged as bf16 pairs: K and the leading dimensions in 2-byte units
+    // forward (E4M3 A): Store, Gelu; data gradient (E5M2 A): Store, DGelu;
+    // weight gradient (E5M2 A): F32, F32Acc
+    const bool ok_epi = g.a_e5m2 ? (g.epi == kEpiStore || g.epi == kEpiDGelu ||
+                                    g.epi == kEpiF32 || g.epi == kEpiF32Acc)
+                                 : (g.epi == kEpiStore || g.epi == kEpiGelu);
     if (!g.a_kmajor || !g.b_kmajor || (g.K & 15) || (g.lda & 15) || (g.ldb & 15) || (g.N & 3) ||
-        !g.scale_a || !g.scale_b || (g.epi != kEpiStore && g.epi != kEpiGelu))
+        !g.scale_a || !g.scale_b || !ok_epi)
       return hipErrorInvalidValue;
     GemmDesc h = g;
     h.K = g.K / 2; h.lda = g.lda / 2; h.ldb = g.ldb / 2;
@@ -755,7 +766,15 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     p.a_bytes = static_cast<uint32_t>(ab);
     p.b_bytes = static_cast<uint32_t>(bb);
     const int tile = pick_tile_fp8(g.M, g.N);
-    return g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu>(p, tile, s) : dispatch_fp8<kEpiStore>(p, tile, s);
+    if (!g.a_e5m2)
+      return g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu, false>(p, tile, s)
+                               : dispatch_fp8<kEpiStore, false>(p, tile, s);
+    switch (g.epi) {
+      case kEpiStore: return dispatch_fp8<kEpiStore, true>(p, tile, s);
+      case kEpiDGelu: return dispatch_fp8<kEpiDGelu, true>(p, tile, s);
+      case kEpiF32: return dispatch_fp8<kEpiF32, true>(p, tile, s);
+      default: return dispatch_fp8<kEpiF32Acc, true>(p, tile, s);
+    }
   }
   GemmParams p = to_params(g);
   // Buffer offsets are 32-bit and the edge handling needs every valid byte

@@ -32,9 +32,11 @@ struct GemmDesc {
   const void* bias;    // [N] elem type, nullable
   void* aux; int64_t ld_aux;
   int epi;
-  // FP8 (E4M3) operands, forward layout only: A and B hold one byte per
-  // element and C = (A B^T) * scale_a[0] * scale_b[0] before the epilogue.
+  // FP8 operands, both k-major: A and B hold one byte per element and
+  // C = (A B^T) * scale_a[0] * scale_b[0] before the epilogue; B is E4M3,
+  // A is E4M3 or (a_e5m2) E5M2.
   bool fp8 = false;
+  bool a_e5m2 = false;
   const float* scale_a = nullptr;
   const float* scale_b = nullptr;
 };
@@ -46,6 +48,15 @@ hipError_t gemm_f32(const GemmDesc& g, hipStream_t stream);
 // receives amax, scale[0] s = amax / 448 (1 for a zero tensor), q the codes
 // of round-to-nearest-even(clamp(x / s, -448, 448)).
 hipError_t quantize_fp8(const void* x, int64_t n, uint8_t* q, float* scale, hipStream_t stream);
+// Per-tensor FP8 quantization in two steps, so that the shards of one tensor
+// share one scale: partial maxima of |x| (kAmaxParts fp32 per shard), then
+// the codes of a [rows, cols] shard, row-major and/or transposed, with the
+// scale of the maximum over n_parts shards' partial maxima.
+constexpr int kAmaxParts = 1024;
+enum Fp8Format : int { kFp8E4M3 = 0, kFp8E5M2 = 1 };
+hipError_t fp8_amax(const void* x, int64_t n, float* parts, hipStream_t stream);
+hipError_t fp8_quantize(int fmt, const void* x, int64_t rows, int cols, const float* const* parts,
+                        int n_parts, uint8_t* q, uint8_t* qt, float* scale, hipStream_t stream);
 
 // Column sums of a [rows, cols] matrix into fp32 out[cols] (= or +=).
 // ws must hold column_sum_ws_bytes(rows, cols) bytes.

@@ -451,6 +451,148 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(const bf16_t* __restrict
   }
 }
 
+// Code of |v| <= the format's largest value, in an 8-bit format with MANT
+// mantissa bits and exponent bias BIAS (E4M3: 3, 7; E5M2: 2, 15), rounded to
+// the nearest value, ties to the even mantissa, from the format's definition.
+template <int MANT, int BIAS>
+__device__ __forceinline__ uint32_t fp8_code(float v, float fmax) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), fmax);
+  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xff) - 127;  // a > 0: floor(log2 a)
+  if (e < 1 - BIAS) {
+    // subnormal grid 2^(1-BIAS-MANT), and zero; 2^MANT steps reach the
+    // smallest normal value, whose code follows on
+    return sign | static_cast<uint32_t>(
+                      rintf(a * __uint_as_float(static_cast<uint32_t>(127 + BIAS - 1 + MANT) << 23)));
+  }
+  // normal: a = m * 2^(e-MANT), m in [2^MANT, 2^(MANT+1)); rintf rounds half
+  // to even; m == 2^(MANT+1) carries into the exponent field
+  const uint32_t m = static_cast<uint32_t>(
+      rintf(a * __uint_as_float(static_cast<uint32_t>(127 + MANT - e) << 23)));
+  return sign | ((static_cast<uint32_t>(e + BIAS) << MANT) + (m - (1u << MANT)));
+}
+
+// Partial maxima of |x| over n = 8 * nvec values: workgroup b of the fixed
+// grid of kAmaxParts writes parts[b] (0 when it saw no element), so the
+// maximum of the parts is max |x| without atomics or a reset.
+__global__ void __launch_bounds__(256) fp8_amax_parts_kernel(const bf16_t* __restrict__ x,
+                                                             int64_t nvec, float* parts) {
+  float m = 0.0f;
+  // four 16-byte loads in flight per lane
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  for (; v + 3 * stride < nvec; v += 4 * stride) {
+    uint4 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const uint4*>(x + (v + i * stride) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[k] << 16)),
+                           fabsf(__uint_as_float(w[k] & 0xffff0000u))));
+    }
+  }
+  for (; v < nvec; v += stride) {
+    float t[8];
+    load8(x + v * 8, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(t[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) parts[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+struct AmaxParts { const float* p[kMaxPartials]; int n; };
+
+// Codes of x [rows, cols] (row-major bf16, cols % 8 == 0) with the scale
+// s = amax / fmax, amax the maximum over the n arrays of kAmaxParts partial
+// maxima (one array per shard of the tensor).  Each workgroup converts a
+// tile of kQRows rows x kQCols columns and writes it row-major to q
+// ([rows, cols]) and/or transposed to qt ([cols, rows]) through LDS.
+constexpr int kQRows = 128, kQCols = 64;
+template <int MANT, int BIAS>
+__global__ void __launch_bounds__(256)
+fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxParts parts,
+                   float fmax, uint8_t* __restrict__ q, uint8_t* __restrict__ qt, float* scale) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQCols][kQRows];
+  const int tid = threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kQRows;
+  const int c0 = blockIdx.x * kQCols;
+  // 8 threads per 64-column row segment, 32 rows per pass; every pass's
+  // load is issued before the scale is known
+  constexpr int kPasses = kQRows / 32;
+  const int lc = (tid & 7) * 8, lr = tid >> 3;
+  uint4 raw[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int64_t r = r0 + pass * 32 + lr;
+    const int c = c0 + lc;
+    raw[pass] = (r < rows && c < cols) ? *reinterpret_cast<const uint4*>(x + r * cols + c)
+                                       : make_uint4(0, 0, 0, 0);
+  }
+  float m = 0.0f;
+  for (int i = tid; i < parts.n * kAmaxParts; i += 256)
+    m = fmaxf(m, parts.p[i / kAmaxParts][i % kAmaxParts]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.0f ? amax / fmax : 1.0f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) scale[0] = s;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int rr = pass * 32 + lr;
+    const int64_t r = r0 + rr;
+    const int c = c0 + lc;
+    uint32_t code[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (r < rows && c < cols) {
+      const uint32_t w[4] = {raw[pass].x, raw[pass].y, raw[pass].z, raw[pass].w};
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        t[2 * k] = __uint_as_float(w[k] << 16);
+        t[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) code[e] = fp8_code<MANT, BIAS>(t[e] / s, fmax);
+      if (q)
+        *reinterpret_cast<uint2*>(q + r * cols + c) =
+            make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                       code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[lc + e][rr] = static_cast<uint8_t>(code[e]);
+  }
+  if (!qt) return;
+  __syncthreads();
+  // transposed: 64 output rows (columns c0..c0+63) of 128 bytes (rows
+  // r0..r0+127); 8 threads per output row, 16 bytes each, two passes
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int oc = pass * 32 + (tid >> 3);
+    const int orr = (tid & 7) * 16;
+    const int c = c0 + oc;
+    const int64_t r = r0 + orr;
+    if (c >= cols || r >= rows) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(&tile[oc][orr]);
+    uint8_t* dst = qt + static_cast<int64_t>(c) * rows + r;
+    if (r + 16 <= rows && (rows & 15) == 0) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint8_t* b = reinterpret_cast<const uint8_t*>(&v);
+      for (int e = 0; e < 16 && r + e < rows; ++e) dst[e] = b[e];
+    }
+  }
+}
+
 // ------------------------------------------------------------ partial sum
 struct PartialPtrs { const void* p[kMaxPartials]; };
 
@@ -1218,6 +1360,31 @@ hipError_t ce_bwd(bool bf16, const float* logits, const int32_t* targets, const 
   else
     hipLaunchKernelGGL(ce_bwd_kernel<float>, g, dim3(256), 0, s, logits, targets, M, S, scale,
                        static_cast<float*>(dlogits), V_l, v0, V, bpr);
+  return hipGetLastError();
+}
+
+hipError_t fp8_amax(const void* x, int64_t n, float* parts, hipStream_t s) {
+  hipLaunchKernelGGL(fp8_amax_parts_kernel, dim3(kAmaxParts), dim3(256), 0, s, cptr<bf16_t>(x),
+                     n / 8, parts);
+  return hipGetLastError();
+}
+
+hipError_t fp8_quantize(int fmt, const void* x, int64_t rows, int cols, const float* const* parts,
+                        int n_parts, uint8_t* q, uint8_t* qt, float* scale, hipStream_t s) {
+  if (n_parts < 1 || n_parts > kMaxPartials || (cols & 7) || cols <= 0 || rows < 0)
+    return hipErrorInvalidValue;
+  AmaxParts ap{};
+  for (int i = 0; i < n_parts; ++i) ap.p[i] = parts[i];
+  ap.n = n_parts;
+  const int64_t rt = rows > 0 ? (rows + kQRows - 1) / kQRows : 1;
+  if (rt > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((cols + kQCols - 1) / kQCols), static_cast<unsigned>(rt));
+  if (fmt == kFp8E5M2)
+    hipLaunchKernelGGL((fp8_convert_kernel<2, 15>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
+                       cols, ap, 57344.0f, q, qt, scale);
+  else
+    hipLaunchKernelGGL((fp8_convert_kernel<3, 7>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
+                       cols, ap, kE4M3Max, q, qt, scale);
   return hipGetLastError();
 }
 

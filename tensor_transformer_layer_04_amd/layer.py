@@ -36,6 +36,17 @@ result all-gathered.  On one device the ranks' row blocks live in one
 the GEMMs read the whole buffer.  LayerNorm weight gradients and the
 row-parallel bias gradients are each rank's column sums over its rows,
 added over the computed ranks in rank order.
+
+FP8 (``cfg.fp8``; the FP8 precision of page "Megatron-LM / Megatron Core
+README digest", §0): the twelve GEMMs of the step run on FP8 codes with one
+scale per tensor, E4M3 for the activations and weights the forward reads and
+E5M2 for the gradients the backward reads, each GEMM's operands k-major (the
+backward reads the transposed codes the quantization writes beside the
+row-major ones).  A tensor split over the ranks (a weight shard, ctx_r, g_r,
+du_r, dqkv_r) is scaled by the maximum over every rank's amax, as the ranks
+of a tensor-parallel group would agree on it; the step therefore runs phase
+by phase over the ranks (all ranks' amax, then their codes), and ranks not
+computed here contribute their amax parts through ``external``.
 """
 from __future__ import annotations
 
@@ -206,7 +217,16 @@ class TPLayer(_Probed):
                                            mtp.MTP_F32 if cfg.dtype == "f32" else mtp.MTP_BF16,
                                            vocab=cfg.vocab, ln_eps=cfg.eps)
                           for r in range(cfg.tp)}
+        self.fp8 = bool(getattr(cfg, "fp8", False))
+        if self.fp8:
+            if cfg.dtype != "bf16" or self.swiglu or self.sp or self.cp > 1:
+                raise ValueError("the FP8 step needs a bf16 GeLU layer without sequence or "
+                                 "context parallelism")
+            if self.T % 16:
+                raise ValueError(f"the FP8 step needs T ({self.T}) divisible by 16")
         self._alloc()
+        if self.fp8:
+            self._alloc_fp8()
 
     # ------------------------------------------------------------ buffers
     def _alloc(self):
@@ -256,6 +276,43 @@ class TPLayer(_Probed):
         self.owns_bias = self.ranks[0]  # rank whose call produces row-parallel bias grads
         self.probe = None
 
+    def _alloc_fp8(self):
+        """Codes (row-major q and transposed qt, uint8), scale and amax parts
+        of every tensor the FP8 GEMMs read."""
+        cfg, T, dev = self.cfg, self.T, self.device
+        h, t = cfg.hidden, cfg.tp
+        hl, fl = h // t, cfg.ffn // t
+
+        def slot(rows, cols):
+            return {"q": torch.empty(rows, cols, dtype=torch.uint8, device=dev),
+                    "qt": torch.empty(cols, rows, dtype=torch.uint8, device=dev),
+                    "s": torch.empty(4, dtype=torch.float32, device=dev),
+                    "amax": torch.zeros(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device=dev),
+                    "rows": rows, "cols": cols}
+        # replicated inputs (one quantization serves every rank)
+        self.q8 = {k: slot(T, h) for k in ("ln1", "ln2", "dy", "dy1")}
+        shapes = {"ctx": (T, hl), "g": (T, fl), "du": (T, fl), "dqkv": (T, 3 * hl),
+                  "wqkv": (3 * hl, h), "wo": (h, hl), "w1": (fl, h), "w2": (h, fl)}
+        self.r8 = {r: {k: slot(*sh) for k, sh in shapes.items()} for r in self.ranks}
+
+    def _quant_shared(self, name, x, fmt):
+        """amax and codes of a tensor every rank holds whole."""
+        sl = self.q8[name]
+        mtp.mtp_fp8_amax(self.d0, x, x.numel(), sl["amax"])
+        mtp.mtp_fp8_quantize(self.d0, fmt, x, sl["rows"], sl["cols"], [sl["amax"]], sl["q"],
+                             sl["qt"], sl["s"])
+
+    def _quant_split(self, name, xs, fmt, ext):
+        """amax of every computed rank's shard xs[r], then its codes with the
+        scale of the whole tensor (this layer's ranks and ``ext``'s)."""
+        for r in self.ranks:
+            mtp.mtp_fp8_amax(self.descs[r], xs[r], xs[r].numel(), self.r8[r][name]["amax"])
+        parts = [self.r8[r][name]["amax"] for r in self.ranks] + list(ext.get("fp8_" + name, []))
+        for r in self.ranks:
+            sl = self.r8[r][name]
+            mtp.mtp_fp8_quantize(self.descs[r], fmt, xs[r], sl["rows"], sl["cols"], parts, sl["q"],
+                                 sl["qt"], sl["s"])
+
     def adopt_rows(self, other: "TPLayer"):
         """Sequence parallelism: share ``other``'s token-sharded buffers, whose
         row blocks of the ranks not computed here stay resident (the
@@ -268,6 +325,8 @@ class TPLayer(_Probed):
         """Forward of the computed ranks; returns y (valid when every rank's
         partials are available, computed or external)."""
         ext = external or {}
+        if self.fp8:
+            return self._forward_fp8(x, ext)
         d0, rep = self.d0, self.rep
         self.x = x
         T = self._timed
@@ -326,6 +385,8 @@ class TPLayer(_Probed):
     # ----------------------------------------------------------- backward
     def backward(self, dy: torch.Tensor, external: Optional[Dict[str, List[torch.Tensor]]] = None):
         ext = external or {}
+        if self.fp8:
+            return self._backward_fp8(dy, ext)
         d0, rep, ws, wsb = self.d0, self.rep, self.ws, self.ws_bytes
         T = self._timed
         main = torch.cuda.current_stream(self.device)
@@ -435,6 +496,157 @@ class TPLayer(_Probed):
             main.wait_stream(side)
         return self.dx
 
+    # ------------------------------------------------------------- FP8 step
+    def _forward_fp8(self, x, ext):
+        d0, rep, T = self.d0, self.rep, self._timed
+        E4, q8, r8 = mtp.MTP_FP8_E4M3, self.q8, self.r8
+        self.x = x
+        with T("ln1"):
+            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+        with T("quant_w"):
+            # the weights' codes (made once per optimizer update; with gradient
+            # accumulation they serve every micro-batch until the next one)
+            for name, key in (("wqkv", "wqkv"), ("wo", "wo"), ("w1", "w1"), ("w2", "w2")):
+                self._quant_split(name, {r: self.w[r][key] for r in self.ranks}, E4, ext)
+        with T("quant"):
+            self._quant_shared("ln1", self.ln1, E4)
+        for r in self.ranks:
+            d, w, a, c = self.descs[r], self.w[r], self.a[r], r8[r]
+            with T("qkv_fwd"):
+                mtp.mtp_linear_fwd_fp8(d, mtp.MTP_QKV, q8["ln1"]["q"], q8["ln1"]["s"],
+                                       c["wqkv"]["q"], c["wqkv"]["s"], w["bqkv"], a["qkv"], None)
+        for r in self.ranks:
+            a = self.a[r]
+            with T("attn_fwd"):
+                mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
+        with T("quant"):
+            self._quant_split("ctx", {r: self.a[r]["ctx"] for r in self.ranks}, E4, ext)
+        for r in self.ranks:
+            c = r8[r]
+            with T("proj_fwd"):
+                mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_PROJ, c["ctx"]["q"], c["ctx"]["s"],
+                                       c["wo"]["q"], c["wo"]["s"], None, self.a[r]["p"], None)
+        parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
+        with T("sum_proj_ln2"):
+            mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
+                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+        with T("quant"):
+            self._quant_shared("ln2", self.ln2, E4)
+        for r in self.ranks:
+            w, a, c = self.w[r], self.a[r], r8[r]
+            with T("fc1_fwd"):
+                mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_FC1, q8["ln2"]["q"], q8["ln2"]["s"],
+                                       c["w1"]["q"], c["w1"]["s"], w["b1"], a["g"], a["u"])
+        with T("quant"):
+            self._quant_split("g", {r: self.a[r]["g"] for r in self.ranks}, E4, ext)
+        for r in self.ranks:
+            c = r8[r]
+            with T("fc2_fwd"):
+                mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_FC2, c["g"]["q"], c["g"]["s"],
+                                       c["w2"]["q"], c["w2"]["s"], None, self.a[r]["q"], None)
+        parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
+        with T("sum_fc2"):
+            mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
+        return self.y
+
+    def _backward_fp8(self, dy, ext):
+        d0, rep, ws, wsb = self.d0, self.rep, self.ws, self.ws_bytes
+        T = self._timed
+        E5, q8, r8 = mtp.MTP_FP8_E5M2, self.q8, self.r8
+        main = torch.cuda.current_stream(self.device)
+        side = self.side
+        wss = self.ws_side if side is not None else ws
+
+        def fork():
+            if side is not None:
+                side.wait_stream(main)
+
+        def on_side():
+            return torch.cuda.stream(side) if side is not None else contextlib.nullcontext()
+
+        self.dy_seen = dy
+        # FC2: du = (dy W2) * GeLU'(u); dW2 = dy^T g
+        with T("quant"):
+            self._quant_shared("dy", dy, E5)
+        fork()
+        for r in self.ranks:
+            d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
+            with T("fc2_dgrad"):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, q8["dy"]["q"], None, q8["dy"]["s"],
+                                       c["w2"]["qt"], c["w2"]["s"], None, None, a["u"], a["du"],
+                                       None)
+            with on_side(), T("fc2_wgrad", side):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, None, q8["dy"]["qt"], q8["dy"]["s"], None,
+                                       None, c["g"]["qt"], c["g"]["s"], None, None, g["dw2"])
+            if r == self.owns_bias:
+                with on_side(), T("fc2_bias", side):
+                    mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
+                                           self.rgrads["db2"], 0, wss, wsb)
+        # FC1: dln2_r = du_r W1_r; dW1 = du^T ln2
+        with T("quant"):
+            self._quant_split("du", {r: self.a[r]["du"] for r in self.ranks}, E5, ext)
+        fork()
+        for r in self.ranks:
+            d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
+            with on_side(), T("fc1_wgrad", side):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC1, None, c["du"]["qt"], c["du"]["s"], None,
+                                       None, q8["ln2"]["qt"], q8["ln2"]["s"], None, None, g["dw1"])
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, None,
+                                       g["db1"], 0, wss, wsb)
+            with T("fc1_dgrad"):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC1, c["du"]["q"], None, c["du"]["s"],
+                                       c["w1"]["qt"], c["w1"]["s"], None, None, None, a["dln2"],
+                                       None)
+        parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
+        with T("ln2_bwd"):
+            mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
+                                      self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0,
+                                      ws, wsb)
+        # PROJ: dctx_r = dy1 Wo_r; dWo_r = dy1^T ctx_r; then attention
+        with T("quant"):
+            self._quant_shared("dy1", self.dy1, E5)
+        fork()
+        for r in self.ranks:
+            d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
+            with T("proj_dgrad"):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_PROJ, q8["dy1"]["q"], None, q8["dy1"]["s"],
+                                       c["wo"]["qt"], c["wo"]["s"], None, None, None, a["dctx"],
+                                       None)
+            with on_side(), T("proj_wgrad", side):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_PROJ, None, q8["dy1"]["qt"], q8["dy1"]["s"],
+                                       None, None, c["ctx"]["qt"], c["ctx"]["s"], None, None,
+                                       g["dwo"])
+                if r == self.owns_bias:
+                    mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
+                                           None, None, self.rgrads["dbo"], 0, wss, wsb)
+            with T("attn_bwd"):
+                mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
+                                 self.n_seqs, ws, wsb)
+        # QKV: dln1_r = dqkv_r Wqkv_r; dWqkv_r = dqkv_r^T ln1
+        with T("quant"):
+            self._quant_split("dqkv", {r: self.a[r]["dqkv"] for r in self.ranks}, E5, ext)
+        fork()
+        for r in self.ranks:
+            d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
+            with T("qkv_dgrad"):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_QKV, c["dqkv"]["q"], None, c["dqkv"]["s"],
+                                       c["wqkv"]["qt"], c["wqkv"]["s"], None, None, None,
+                                       a["dln1"], None)
+            with on_side(), T("qkv_wgrad", side):
+                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_QKV, None, c["dqkv"]["qt"], c["dqkv"]["s"],
+                                       None, None, q8["ln1"]["qt"], q8["ln1"]["s"], None, None,
+                                       g["dwqkv"])
+                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None, None,
+                                       g["dbqkv"], 0, wss, wsb)
+        parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
+        with T("ln1_bwd"):
+            mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                                      self.dy1, self.dx, self.rgrads["dln1_g"],
+                                      self.rgrads["dln1_b"], 0, ws, wsb)
+        if side is not None:
+            main.wait_stream(side)
+        return self.dx
+
     # ------------------------------------------------ context parallelism
     def _chunks(self):
         L = self.T // self.cp
@@ -474,12 +686,16 @@ class TPLayer(_Probed):
     def partials(self) -> Dict[str, List[torch.Tensor]]:
         """This object's partial outputs, to be passed as ``external`` to a
         layer that computes the remaining ranks."""
-        return {
+        out = {
             "proj": [self.a[r]["p"].clone() for r in self.ranks],
             "fc2": [self.a[r]["q"].clone() for r in self.ranks],
             "fc1_dx": [self.a[r]["dln2"].clone() for r in self.ranks],
             "qkv_dx": [self.a[r]["dln1"].clone() for r in self.ranks],
         }
+        if self.fp8:  # the amax parts of the tensors split over the ranks
+            for k in ("ctx", "g", "du", "dqkv", "wqkv", "wo", "w1", "w2"):
+                out["fp8_" + k] = [self.r8[r][k]["amax"].clone() for r in self.ranks]
+        return out
 
 
 class VocabHead(_Probed):

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libmtp.so")
 MTP_OK, MTP_ERR_INVALID_ARG, MTP_ERR_UNSUPPORTED, MTP_ERR_WORKSPACE, MTP_ERR_HIP = range(5)
 MTP_F32, MTP_BF16 = 0, 1
 MTP_QKV, MTP_PROJ, MTP_FC1, MTP_FC2, MTP_VOCAB, MTP_FC1_SWIGLU, MTP_FC2_SWIGLU = range(7)
+MTP_FP8_E4M3, MTP_FP8_E5M2 = 0, 1
+FP8_AMAX_PARTS = 1024  # fp32 partial maxima written by mtp_fp8_amax
 (MTP_OP_LAYERNORM_BWD, MTP_OP_COL_LINEAR_BWD, MTP_OP_ROW_LINEAR_BWD, MTP_OP_ATTN_BWD,
  MTP_OP_VOCAB_CE) = range(5)
 
@@ -58,6 +60,10 @@ _SIGS = {
     "mtp_attn_bwd_noalloc": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP]),
     "mtp_quantize_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 7 + [_VP]),
+    "mtp_fp8_amax": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP]),
+    "mtp_fp8_quantize": (ctypes.c_int, [_VP, ctypes.c_int, _VP, ctypes.c_int64, ctypes.c_int64,
+                                        _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
+    "mtp_linear_bwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 10 + [ctypes.c_int, _VP]),
     "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4
                            + [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "mtp_attn_merge": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int64] * 2 + [_VP]),
@@ -201,6 +207,25 @@ def mtp_quantize_fp8(desc, x, n, q, scale, stream=None):
 def mtp_linear_fwd_fp8(desc, kind, x8, x_scale, w8, w_scale, b, y, preact, stream=None):
     return _call("mtp_linear_fwd_fp8", ctypes.byref(desc), kind, _addr(x8), _addr(x_scale),
                  _addr(w8), _addr(w_scale), _addr(b), _addr(y), _addr(preact), _stream(stream))
+
+
+def mtp_fp8_amax(desc, x, n, amax_parts, stream=None):
+    return _call("mtp_fp8_amax", ctypes.byref(desc), _addr(x), int(n), _addr(amax_parts),
+                 _stream(stream))
+
+
+def mtp_fp8_quantize(desc, fmt, x, rows, cols, amax_parts, q, q_t, scale, stream=None):
+    """``amax_parts``: a sequence of device tensors (one per shard)."""
+    arr = (ctypes.c_void_p * len(amax_parts))(*[_addr(a) for a in amax_parts])
+    return _call("mtp_fp8_quantize", ctypes.byref(desc), int(fmt), _addr(x), int(rows), int(cols),
+                 arr, len(amax_parts), _addr(q), _addr(q_t), _addr(scale), _stream(stream))
+
+
+def mtp_linear_bwd_fp8(desc, kind, dy8, dy8_t, dy_scale, w8_t, w_scale, x8_t, x_scale, preact,
+                       dx, dw, accumulate=0, stream=None):
+    return _call("mtp_linear_bwd_fp8", ctypes.byref(desc), kind, _addr(dy8), _addr(dy8_t),
+                 _addr(dy_scale), _addr(w8_t), _addr(w_scale), _addr(x8_t), _addr(x_scale),
+                 _addr(preact), _addr(dx), _addr(dw), int(accumulate), _stream(stream))
 
 
 def mtp_attn_fwd_block(desc, qkv, q_lo, q_hi, k_lo, k_hi, ctx, lse, cu_seqlens=None, n_seqs=0,

@@ -13,6 +13,16 @@ import oracle
 import synth
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# End to end, an FP8 layer is not determined by its inputs to better than
+# its formats' steps: a code is a discontinuous function of its input, so an
+# input that differs by a relative d (the bf16 path against the fp64 oracle,
+# d ~ 2^-8) lands on the neighbouring code with probability ~2d/e, moving the
+# value by e (the relative step: e ~ 2^-3.5 for E4M3, 2^-2.5 for E5M2): a
+# quantized product then deviates by ~sqrt(2 d e), about 3e-2 after one E4M3
+# product and about 1e-1 after the E5M2 gradient products that follow it.
+# The FP8 step is held to the bf16 tolerance product by product, on the
+# GPU's own codes (which are bit-exact), and end to end to this bound.
+FP8_E2E_TOL = 0.15
 
 
 def log(msg: str) -> None:
@@ -89,9 +99,10 @@ def oracle_layer(cfg, data, dy=None):
     return c, g
 
 
-def compare_layer(cfg, L, c, g, data, report, rows=None, ranks=None):
-    """Element-wise comparison of every per-rank and summed tensor."""
-    tol = TOL[cfg.dtype]
+def compare_layer(cfg, L, c, g, data, report, rows=None, ranks=None, tol=None):
+    """Element-wise comparison of every per-rank and summed tensor (at the
+    dtype's tolerance unless ``tol`` is given)."""
+    tol = TOL[cfg.dtype] if tol is None else tol
     sl = slice(None) if rows is None else slice(0, rows)
     ranks = L.ranks if ranks is None else ranks
     cpu = lambda t: t.detach().float().cpu()
@@ -198,3 +209,65 @@ def run_gpu_layer_with_head(cfg, data):
     L.backward(H.backward())
     torch.cuda.synchronize()
     return L, H
+
+
+def compare_fp8_components(cfg, L, report):
+    """The FP8 step of a layer that ran every rank, component by component:
+    (a) every code and scale it used, bit for bit against the oracle's
+    quantization of the GPU's own tensor (the whole tensor: its ranks'
+    shards together), in both layouts; (b) every FP8 product against the
+    oracle's product of those codes, at the bf16 tolerance."""
+    from oracle import fp8 as f8
+    tol = TOL["bf16"]
+    cpu = lambda t: t.detach().float().cpu()
+    R = L.ranks
+    assert R == list(range(cfg.tp)), "components need every rank"
+
+    def codes(name, shards, slots, fmt):
+        whole = np.concatenate([cpu(x).numpy().reshape(-1) for x in shards])
+        qw, s = f8.quantize_per_tensor(whole, fmt)
+        enc = f8.fp8_encode(qw, fmt)
+        out, off = [], 0
+        for x, sl in zip(shards, slots):
+            n = x.numel()
+            rows, cols = x.shape
+            q = qw[off:off + n].reshape(rows, cols)
+            e = enc[off:off + n].reshape(rows, cols)
+            off += n
+            assert float(sl["s"][0]) == float(s), f"{name}: scale {float(sl['s'][0])} != {float(s)}"
+            assert np.array_equal(sl["q"].cpu().numpy(), e), f"{name}: codes differ"
+            assert np.array_equal(sl["qt"].cpu().numpy(), e.T), f"{name}: transposed codes differ"
+            out.append((q, s))
+        report[f"codes.{name}"] = 0.0
+        return out
+    E4, E5 = "e4m3", "e5m2"
+    (ln1,), (ln2,) = codes("ln1", [L.ln1], [L.q8["ln1"]], E4), codes("ln2", [L.ln2], [L.q8["ln2"]], E4)
+    (dy,), (dy1,) = (codes("dy", [L.dy_seen], [L.q8["dy"]], E5),
+                     codes("dy1", [L.dy1], [L.q8["dy1"]], E5))
+    split = {}
+    for name, src, fmt in (("wqkv", lambda r: L.w[r]["wqkv"], E4), ("wo", lambda r: L.w[r]["wo"], E4),
+                           ("w1", lambda r: L.w[r]["w1"], E4), ("w2", lambda r: L.w[r]["w2"], E4),
+                           ("ctx", lambda r: L.a[r]["ctx"], E4), ("g", lambda r: L.a[r]["g"], E4),
+                           ("du", lambda r: L.a[r]["du"], E5), ("dqkv", lambda r: L.a[r]["dqkv"], E5)):
+        split[name] = codes(name, [src(r) for r in R], [L.r8[r][name] for r in R], fmt)
+    for r in R:
+        a, gr, w = L.a[r], L.grads[r], L.w[r]
+        (qwqkv, swqkv), (qwo, swo) = split["wqkv"][r], split["wo"][r]
+        (qw1, sw1), (qw2, sw2) = split["w1"][r], split["w2"][r]
+        (qctx, sctx), (qg, sg) = split["ctx"][r], split["g"][r]
+        (qdu, sdu), (qdq, sdq) = split["du"][r], split["dqkv"][r]
+        u = oracle.to64(cpu(a["u"]))
+        check(f"r{r}.fp8_qkv", cpu(a["qkv"]), f8.fp8_linear(*ln1, qwqkv, swqkv, oracle.to64(w["bqkv"].cpu())), tol, report)
+        check(f"r{r}.fp8_proj", cpu(a["p"]), f8.fp8_linear(qctx, sctx, qwo, swo), tol, report)
+        uref = f8.fp8_linear(*ln2, qw1, sw1, oracle.to64(w["b1"].cpu()))
+        check(f"r{r}.fp8_u", cpu(a["u"]), uref, tol, report)
+        check(f"r{r}.fp8_g", cpu(a["g"]), oracle.gelu_tanh(uref), tol, report)
+        check(f"r{r}.fp8_fc2", cpu(a["q"]), f8.fp8_linear(qg, sg, qw2, sw2), tol, report)
+        check(f"r{r}.fp8_du", cpu(a["du"]), f8.fp8_dgrad(*dy, qw2, sw2) * oracle.gelu_tanh_grad(u), tol, report)
+        check(f"r{r}.fp8_dw2", cpu(gr["dw2"]), f8.fp8_wgrad(*dy, qg, sg), tol, report)
+        check(f"r{r}.fp8_dln2", cpu(a["dln2"]), f8.fp8_dgrad(qdu, sdu, qw1, sw1), tol, report)
+        check(f"r{r}.fp8_dw1", cpu(gr["dw1"]), f8.fp8_wgrad(qdu, sdu, *ln2), tol, report)
+        check(f"r{r}.fp8_dctx", cpu(a["dctx"]), f8.fp8_dgrad(*dy1, qwo, swo), tol, report)
+        check(f"r{r}.fp8_dwo", cpu(gr["dwo"]), f8.fp8_wgrad(*dy1, qctx, sctx), tol, report)
+        check(f"r{r}.fp8_dln1", cpu(a["dln1"]), f8.fp8_dgrad(qdq, sdq, qwqkv, swqkv), tol, report)
+        check(f"r{r}.fp8_dwqkv", cpu(gr["dwqkv"]), f8.fp8_wgrad(qdq, sdq, *ln1), tol, report)

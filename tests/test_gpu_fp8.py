@@ -86,3 +86,94 @@ def test_fp8_linear_maps_7b_shard(T):
             ref = oracle.gelu_tanh(ref)
         check(f"{name}.y", y[rows].float().cpu(), ref, tol, report)
     log(f"fp8 linear T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
+
+
+# ------------------------------------------------------------ FP8 step
+def _amax_and_quant(d, fmt, shards):
+    """GPU codes of a tensor given as its column shards (each [rows, c_i]):
+    each shard's amax parts, then every shard's codes with all parts."""
+    from tensor_transformer_layer_04_amd import mtp
+    parts, out = [], []
+    for x in shards:
+        p = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_amax(d, x, x.numel(), p)
+        parts.append(p)
+    for x in shards:
+        rows, cols = x.shape
+        q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+        qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+        s = torch.empty(1, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_quantize(d, fmt, x, rows, cols, parts, q, qt, s)
+        out.append((q, qt, s))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols,n_shards,std", [(300, 200, 2, 1.0), (2048, 5504, 1, 1e-4),
+                                                    (77, 64, 3, 5.0), (0, 16, 1, 1.0)])
+def test_fp8_quantize_shards_both_layouts(fmt, rows, cols, n_shards, std):
+    """Codes of a tensor split into column shards, each scaled by the whole
+    tensor's amax: row-major and transposed codes bit for bit against the
+    oracle's quantization of the whole tensor, and the scale exactly."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    d = mtp.make_desc(4096, 32, 11008, 2, 0, 2048, 1, mtp.MTP_BF16)
+    x = _bf16((rows, cols * n_shards), 90 + rows + cols, std)
+    if rows:
+        x[rows // 2, 3] = 7.0 * std   # one clear maximum, away from the first shard's edge
+    shards = [x[:, i * cols:(i + 1) * cols].contiguous().cuda() for i in range(n_shards)]
+    got = _amax_and_quant(d, mtp.MTP_FP8_E4M3 if fmt == "e4m3" else mtp.MTP_FP8_E5M2, shards)
+    qo, so = ofp8.quantize_per_tensor(x.float().numpy(), fmt)
+    codes = ofp8.fp8_encode(qo, fmt).reshape(rows, cols * n_shards)
+    for i, (q, qt, s) in enumerate(got):
+        ref = codes[:, i * cols:(i + 1) * cols]
+        assert float(s[0]) == float(so), (float(s[0]), float(so))
+        assert np.array_equal(q.cpu().numpy(), ref), f"shard {i}: row-major codes differ"
+        assert np.array_equal(qt.cpu().numpy(), ref.T), f"shard {i}: transposed codes differ"
+
+
+@pytest.mark.parametrize("T", [2048, 304])
+def test_fp8_backward_gemms_7b_shard(T):
+    """Data and weight gradients of the four linear maps from FP8 codes (E5M2
+    gradient, the forward's E4M3 codes of W and x) at the 7B TP=2 shard
+    shapes, against the oracle's FP8 products of the same codes: every
+    element of the weight gradients, sampled rows of the data gradients."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    h, a, f, tp = 4096, 32, 11008, 2
+    hl, fl = h // tp, f // tp
+    d = mtp.make_desc(h, a, f, tp, 0, T, 1, mtp.MTP_BF16)
+    tol = TOL["bf16"]
+    rows = np.unique(np.concatenate([np.random.default_rng(T).choice(T, 24, replace=False),
+                                     [0, T - 1]]))
+    cases = {  # name: (kind, out, in)
+        "qkv": (mtp.MTP_QKV, 3 * hl, h), "fc1": (mtp.MTP_FC1, fl, h),
+        "proj": (mtp.MTP_PROJ, h, hl), "fc2": (mtp.MTP_FC2, h, fl)}
+    report = {}
+    for i, (name, (kind, out, inn)) in enumerate(cases.items()):
+        dy = _bf16((T, out), 110 + i, 1e-3)
+        w = _bf16((out, inn), 120 + i, 0.02)
+        x = _bf16((T, inn), 130 + i)
+        (dq, dqt, ds), = _amax_and_quant(d, mtp.MTP_FP8_E5M2, [dy.cuda()])
+        (wq, wqt, wsc), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w.cuda()])
+        (xq, xqt, xs), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [x.cuda()])
+        u = _bf16((T, inn), 140 + i) if kind == mtp.MTP_FC2 else None
+        dx = torch.empty(T, inn, dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty(out, inn, dtype=torch.float32, device="cuda")
+        mtp.mtp_linear_bwd_fp8(d, kind, dq, dqt, ds, wqt, wsc, xqt, xs,
+                               None if u is None else u.cuda(), dx, dw)
+        dw2 = torch.zeros(out, inn, dtype=torch.float32, device="cuda") + 1.0
+        mtp.mtp_linear_bwd_fp8(d, kind, None, dqt, ds, None, None, xqt, xs, None, None, dw2, 1)
+        torch.cuda.synchronize()
+        q_dy, s_dy = ofp8.quantize_per_tensor(dy.float().numpy(), "e5m2")
+        q_w, s_w = ofp8.quantize_per_tensor(w.float().numpy(), "e4m3")
+        q_x, s_x = ofp8.quantize_per_tensor(x.float().numpy(), "e4m3")
+        ref_dx = ofp8.fp8_dgrad(q_dy[rows], s_dy, q_w, s_w)
+        if u is not None:
+            ref_dx = ref_dx * oracle.gelu_tanh_grad(oracle.to64(u)[rows])
+        ref_dw = ofp8.fp8_wgrad(q_dy, s_dy, q_x, s_x)
+        check(f"{name}.dx", dx[rows].float().cpu(), ref_dx, tol, report)
+        check(f"{name}.dw", dw.cpu(), ref_dw, 1e-4, report)
+        check(f"{name}.dw_acc", dw2.cpu(), ref_dw + 1.0, 1e-4, report)
+    log(f"fp8 backward GEMMs T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))

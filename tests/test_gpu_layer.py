@@ -21,8 +21,9 @@ import torch
 
 import oracle
 import synth
-from gpu_common import (TOL, check, compare_head, compare_layer, fmt_report, log, oracle_head,
-                        oracle_layer, require_gpu, run_gpu_layer, run_gpu_layer_with_head)
+from gpu_common import (FP8_E2E_TOL, TOL, check, compare_fp8_components, compare_head,
+                        compare_layer, fmt_report, log, oracle_head, oracle_layer, require_gpu,
+                        run_gpu_layer, run_gpu_layer_with_head)
 
 pytestmark = pytest.mark.gpu
 
@@ -301,3 +302,28 @@ def test_sequence_parallel_one_rank_with_resident_rows():
     torch.cuda.synchronize()
     for k, v in ref.items():
         assert torch.equal(getattr(L, k)[rows], v[rows]), f"rank-0 rows of {k} differ"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["small_fp8_tp2", "small_fp8_d64_tp4", "7b_tp2_fp8"])
+def test_layer_fp8_parity(name):
+    """The FP8 layer step (twelve GEMMs on FP8 codes, whole-tensor scales
+    shared by the ranks), all ranks, forward and backward: (a) every code and
+    scale bit for bit and (b) every FP8 product at the bf16 tolerance, both
+    against the oracle applied to the GPU's own tensors; (c) every per-rank
+    and summed tensor against the oracle's FP8 layer end to end."""
+    require_gpu()
+    cfg = synth.get_config(name)
+    log(f"FP8 layer parity {name}: T={cfg.tokens} h={cfg.hidden} tp={cfg.tp}")
+    data = synth.generate(cfg)
+    L = run_gpu_layer(cfg, data)
+    log("  GPU done; components")
+    report = {}
+    compare_fp8_components(cfg, L, report)
+    log(f"  components worst: {fmt_report(report)}")
+    starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    c = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts, fp8=True)
+    g = oracle.layer_backward(data, c, data["dy"], cfg.heads, starts)
+    e2e = {}
+    compare_layer(cfg, L, c, g, data, e2e, tol=FP8_E2E_TOL)
+    log(f"  end to end worst: {fmt_report(e2e)}")
