@@ -137,6 +137,34 @@ __device__ __forceinline__ void issue_tile(const u32x4& rs, char* stage, int wav
   }
 }
 
+// Byte offsets of the copies of issue_tile at k0 = 0, with the row bound
+// applied (a row outside the matrix gets kOOB, which stays past num_records
+// when the k offset is added).  For a tile that lies wholly inside K the
+// copy offsets are these plus k0 * 2 (k-major) or k0 * ld (m/n-major), so the
+// main loop adds one scalar per copy instead of recomputing each offset and
+// its bounds.
+template <int R, int NW, bool KMAJ>
+__device__ __forceinline__ void tile_bases(uint32_t (&base)[R / 8 / NW], int wave, int lane,
+                                           int row0, int rmax, uint32_t ld_bytes) {
+  constexpr int kPer = R / 8 / NW;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = (wave * kPer + i) * 64 + lane;
+    if (KMAJ) {
+      const int row = q >> 3;
+      const int lc = (q & 7) ^ swz_k(row);
+      const int gr = row0 + row;
+      base[i] = gr < rmax ? static_cast<uint32_t>(gr) * ld_bytes + lc * 16 : kOOB;
+    } else {
+      constexpr int kCpr = R / 8;
+      const int kr = q / kCpr;
+      const int lc = swz_m<R>(q % kCpr, kr);
+      const int gm = row0 + lc * 8;
+      base[i] = gm < rmax ? static_cast<uint32_t>(kr) * ld_bytes + gm * 2 : kOOB;
+    }
+  }
+}
+
 // Workgroup barrier without the fence of __syncthreads(), whose release
 // semantics make the compiler wait for every outstanding LDS copy
 // (vmcnt(0)) first.  The caller's s_waitcnt has already waited for the
@@ -344,10 +372,6 @@ gemm_bf16_kernel(GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int lrow = lane & 31, lk = lane >> 5;
-  auto issue = [&](char* sa, char* sb, int k0) {
-    issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
-    issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
-  };
   // Operand fragments of one k-step (16 k, or 64 with F8): FM A blocks and
   // FN B blocks.
   using FragT = std::conditional_t<F8, i32x8, bf16x8>;
@@ -457,11 +481,30 @@ gemm_bf16_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
+  uint32_t abase[kCopiesA], bbase[kCopiesB];
+  tile_bases<BM, NW, AK>(abase, wave, lane, m0, p.M, lda_b);
+  tile_bases<BN, NW, BKM>(bbase, wave, lane, n0, p.N, ldb_b);
+  // A tile wholly inside K: the precomputed offsets plus the tile's k offset;
+  // else (the ragged last tile, or tiles past K) every chunk's bounds.
   auto copy_a = [&](char* sa, int k0) {
-    issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
+    if (k0 + kBK <= p.K) {
+      const uint32_t dk = AK ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(k0) * lda_b;
+#pragma unroll
+      for (int i = 0; i < kCopiesA; ++i)
+        copy16_raw(ra, lds_addr(sa) + (wave * kCopiesA + i) * 1024, abase[i] + dk);
+    } else {
+      issue_tile<BM, NW, AK>(ra, sa, wave, lane, m0, p.M, k0, p.K, lda_b);
+    }
   };
   auto copy_b = [&](char* sb, int k0) {
-    issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
+    if (k0 + kBK <= p.K) {
+      const uint32_t dk = BKM ? static_cast<uint32_t>(k0) * 2 : static_cast<uint32_t>(k0) * ldb_b;
+#pragma unroll
+      for (int i = 0; i < kCopiesB; ++i)
+        copy16_raw(rb, lds_addr(sb) + (wave * kCopiesB + i) * 1024, bbase[i] + dk);
+    } else {
+      issue_tile<BN, NW, BKM>(rb, sb, wave, lane, n0, p.N, k0, p.K, ldb_b);
+    }
   };
   // Stage objects by compile-time index.
   auto sa = [&](auto i) -> char* {

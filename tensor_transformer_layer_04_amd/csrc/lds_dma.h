@@ -58,9 +58,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // which clobber memory), while LDS reads of other stages may be scheduled
 // around it.  The caller must not read a stage between issuing a copy into
 // it and the wait + barrier that make the copy visible.
+// The destination is wave-uniform; readfirstlane states so (it costs
+// nothing where the compiler already knows it), so that the "s" operand is
+// never a VGPR.
 __device__ __forceinline__ void copy16_raw(const u32x4& rs, uint32_t dst, uint32_t off) {
+  const uint32_t d = __builtin_amdgcn_readfirstlane(dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(dst), "v"(off), "s"(rs) : "m0");
+               :: "s"(d), "v"(off), "s"(rs) : "m0");
 }
 
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element j

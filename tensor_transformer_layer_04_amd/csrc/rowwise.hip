@@ -514,32 +514,33 @@ struct AmaxParts { const float* p[kMaxPartials]; int n; };
 // s = amax / fmax, amax the maximum over the n arrays of kAmaxParts partial
 // maxima (one array per shard of the tensor).  Each workgroup converts a
 // tile of kQRows rows x kQCols columns and writes it row-major to q
-// ([rows, cols]) and/or transposed to qt ([cols, rows]) through LDS.
-constexpr int kQRows = 128, kQCols = 64;
+// ([rows, cols]) and/or transposed to qt ([cols, rows]) through LDS.  A lane
+// takes 4 consecutive rows x 8 columns, so it packs the 4 codes of each of
+// its columns into one 4-byte LDS word; the transposed tile's rows are
+// padded to 33 words, which puts the 64 lanes' words in 64 distinct banks.
+constexpr int kQRows = 128, kQCols = 64, kQPitch = kQRows + 4;
 template <int MANT, int BIAS>
 __global__ void __launch_bounds__(256)
 fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxParts parts,
                    float fmax, uint8_t* __restrict__ q, uint8_t* __restrict__ qt, float* scale) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kQCols][kQRows];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQCols * kQPitch];
   const int tid = threadIdx.x;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kQRows;
   const int c0 = blockIdx.x * kQCols;
-  // 8 threads per 64-column row segment, 32 rows per pass; every pass's
-  // load is issued before the scale is known
-  constexpr int kPasses = kQRows / 32;
-  const int lc = (tid & 7) * 8, lr = tid >> 3;
-  uint4 raw[kPasses];
+  const int lc = (tid & 7) * 8, lg = tid >> 3;  // columns lc..lc+7, rows 4lg..4lg+3
+  const int c = c0 + lc;
+  // every load is issued before the scale is known
+  uint4 raw[4];
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {
-    const int64_t r = r0 + pass * 32 + lr;
-    const int c = c0 + lc;
-    raw[pass] = (r < rows && c < cols) ? *reinterpret_cast<const uint4*>(x + r * cols + c)
-                                       : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 4 * lg + i;
+    raw[i] = (r < rows && c < cols) ? *reinterpret_cast<const uint4*>(x + r * cols + c)
+                                    : make_uint4(0, 0, 0, 0);
   }
   float m = 0.0f;
-  for (int i = tid; i < parts.n * kAmaxParts; i += 256)
-    m = fmaxf(m, parts.p[i / kAmaxParts][i % kAmaxParts]);
+  for (int k = tid; k < parts.n * kAmaxParts; k += 256)
+    m = fmaxf(m, parts.p[k / kAmaxParts][k % kAmaxParts]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -547,49 +548,46 @@ fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxPar
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / fmax : 1.0f;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) scale[0] = s;
+  uint32_t col4[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // column e: the 4 rows' codes
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {
-    const int rr = pass * 32 + lr;
-    const int64_t r = r0 + rr;
-    const int c = c0 + lc;
-    uint32_t code[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (r < rows && c < cols) {
-      const uint32_t w[4] = {raw[pass].x, raw[pass].y, raw[pass].z, raw[pass].w};
-      float t[8];
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 4 * lg + i;
+    if (r >= rows || c >= cols) continue;
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    uint32_t code[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        t[2 * k] = __uint_as_float(w[k] << 16);
-        t[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) code[e] = fp8_code<MANT, BIAS>(t[e] / s, fmax);
-      if (q)
-        *reinterpret_cast<uint2*>(q + r * cols + c) =
-            make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                       code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+    for (int k = 0; k < 4; ++k) {
+      code[2 * k] = fp8_code<MANT, BIAS>(__uint_as_float(w[k] << 16) / s, fmax);
+      code[2 * k + 1] = fp8_code<MANT, BIAS>(__uint_as_float(w[k] & 0xffff0000u) / s, fmax);
     }
+    if (q)
+      *reinterpret_cast<uint2*>(q + r * cols + c) =
+          make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                     code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile[lc + e][rr] = static_cast<uint8_t>(code[e]);
+    for (int e = 0; e < 8; ++e) col4[e] |= code[e] << (8 * i);
   }
   if (!qt) return;
-  __syncthreads();
-  // transposed: 64 output rows (columns c0..c0+63) of 128 bytes (rows
-  // r0..r0+127); 8 threads per output row, 16 bytes each, two passes
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int oc = pass * 32 + (tid >> 3);
-    const int orr = (tid & 7) * 16;
-    const int c = c0 + oc;
-    const int64_t r = r0 + orr;
-    if (c >= cols || r >= rows) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(&tile[oc][orr]);
-    uint8_t* dst = qt + static_cast<int64_t>(c) * rows + r;
-    if (r + 16 <= rows && (rows & 15) == 0) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint8_t* b = reinterpret_cast<const uint8_t*>(&v);
-      for (int e = 0; e < 16 && r + e < rows; ++e) dst[e] = b[e];
-    }
+  for (int e = 0; e < 8; ++e)
+    *reinterpret_cast<uint32_t*>(tile + (lc + e) * kQPitch + 4 * lg) = col4[e];
+  __syncthreads();
+  // transposed: output row oc (column c0 + oc) holds rows r0..r0+127; four
+  // lanes per output row, 32 bytes each
+  const int oc = tid >> 2, part = tid & 3;
+  const int cc = c0 + oc;
+  const int64_t rb = r0 + 32 * part;
+  if (cc >= cols || rb >= rows) return;
+  uint32_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = *reinterpret_cast<const uint32_t*>(tile + oc * kQPitch + 32 * part + 4 * j);
+  uint8_t* dst = qt + static_cast<int64_t>(cc) * rows + rb;
+  if (rb + 32 <= rows && (rows & 15) == 0) {
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(v[4], v[5], v[6], v[7]);
+  } else {
+    for (int e = 0; e < 32 && rb + e < rows; ++e) dst[e] = static_cast<uint8_t>(v[e >> 2] >> (8 * (e & 3)));
   }
 }
 
