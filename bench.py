@@ -328,22 +328,33 @@ def main(argv=None) -> int:
         parts = full.partials()
         ext = {k: [v[i] for i, r in enumerate(full.ranks) if r != args.rank] for k, v in parts.items()}
         torch.cuda.synchronize()
-    L = TPLayer(cfg, data, ranks=[args.rank], device=dev, cu_seqlens=data["cu_seqlens"])
-    if cfg.tp > 1:
-        if L.sp:
+    def make_layer(overlap):
+        lay = TPLayer(cfg, data, ranks=[args.rank], device=dev, cu_seqlens=data["cu_seqlens"],
+                      overlap=overlap)
+        if cfg.tp > 1 and lay.sp:
             # The other ranks' row blocks of the token-sharded activations and
             # gradients (what the all-gathers would deliver) stay resident.
-            L.adopt_rows(full)
+            lay.adopt_rows(full)
+        return lay
+    # L: weight and bias gradients on a second stream beside the data
+    # gradients (the timed step); L1: the same step on one stream, for the
+    # HIP-graph replay (a graph captured from two streams replays slower).
+    L = make_layer(True)
+    L1 = make_layer(False)
+    if cfg.tp > 1:
         del full
     H = VocabHead(cfg, data, ranks=[args.rank], device=dev) if cfg.vocab else None
 
-    def step():
-        L.forward(x, ext)
-        if H is None:
-            L.backward(dy, ext)
-        else:
-            H.forward(L.y, head_ext[0])
-            L.backward(H.backward(head_ext[1]), ext)
+    def step_of(lay):
+        def step():
+            lay.forward(x, ext)
+            if H is None:
+                lay.backward(dy, ext)
+            else:
+                H.forward(lay.y, head_ext[0])
+                lay.backward(H.backward(head_ext[1]), ext)
+        return step
+    step = step_of(L)
 
     for _ in range(args.warmup):
         step()
@@ -396,31 +407,46 @@ def main(argv=None) -> int:
     call_us = {t: round(1e3 * sum(a.elapsed_time(b) for a, b in calls[t]) / n_call_steps, 1)
                for t in CALL_TAGS + HEAD_TAGS if calls[t]}
 
-    # The same step replayed from a HIP graph (captured once, inputs unchanged).
-    graph_ms = None
-    try:
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            step()
-        torch.cuda.current_stream().wait_stream(cs)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.steps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        graph_ms = round(a.elapsed_time(b) / args.steps, 4)
-        del g
-    except RuntimeError as exc:  # capture unsupported: report it, keep the eager figure
-        graph_ms = f"capture failed: {exc}"[:200]
+    # The same step replayed from a HIP graph (captured once, inputs
+    # unchanged): the one-stream step, and the two-stream one beside it.
+    def graph_replay_ms(fn):
+        try:
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                fn()
+            torch.cuda.current_stream().wait_stream(cs)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            del g
+            return round(a.elapsed_time(b) / args.steps, 4)
+        except RuntimeError as exc:  # capture unsupported: report it, keep the eager figure
+            return f"capture failed: {exc}"[:200]
+    step1 = step_of(L1)
+    graph_ms = graph_replay_ms(step1)
+    graph_ms_two_streams = graph_replay_ms(step)
+    # the one-stream step launched eagerly, for comparison with its graph
+    for _ in range(args.warmup):
+        step1()
+    torch.cuda.synchronize()
+    a1, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a1.record()
+    for _ in range(args.steps):
+        step1()
+    b1.record()
+    torch.cuda.synchronize()
+    eager_one_stream_ms = round(a1.elapsed_time(b1) / args.steps, 4)
 
     fl = shard_flops(cfg, cu)
     tflops = fl["total"] / (ms * 1e-3) / 1e12
@@ -459,6 +485,8 @@ def main(argv=None) -> int:
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "graph_replay_ms_per_step": graph_ms,
+        "graph_replay_two_streams_ms_per_step": graph_ms_two_streams,
+        "eager_one_stream_ms_per_step": eager_one_stream_ms,
         "call_us_per_step": call_us,
         # The step without the forward sums of the ranks' row-parallel partials
         # (charged in full above): the FFN output sum, and the projection sum
