@@ -412,11 +412,7 @@ class TPLayer(_Probed):
                                        None, 0, ws, wsb)
             with on_side(), T("fc2_wgrad", side):
                 mtp.mtp_row_linear_bwd(d, self.k_fc2, dy, a["g"], w["w2"], None, None, g["dw2"],
-                                       None, 0, wss, wsb)
-            if db2 is not None:
-                with on_side(), T("fc2_bias", side):
-                    mtp.mtp_row_linear_bwd(d, self.k_fc2, dy, a["g"], w["w2"], None, None, None,
-                                           db2, 0, wss, wsb)
+                                       db2, 0, wss, wsb)
             if self.sp:
                 # row-parallel bias: this rank's column sums of dy over its rows
                 s = self.rows[r]
