@@ -93,16 +93,40 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
 __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
 // 64-byte segment swizzle of an m/n-major k-row holding R elements (R/32
-// segments): the 8 k-rows {16t+0..3, 16t+8..11} (or +4) touched by one
-// transpose read map to 8 distinct segments when R >= 256.  The XOR stays
-// inside aligned groups of kP segments, kP the largest power of two that
-// divides the segment count, so every swizzled chunk stays in the row.
+// segments).  A transpose read (ds_read_b64_tr_b16) is served one group of
+// 16 lanes at a time, and a group reads 32 bytes at one logical segment from
+// each of 4 consecutive k-rows: those 4 pieces must land in distinct banks.
+//  * R = 128, 256 (rows a multiple of 256 bytes, so every row starts at the
+//    same bank): the segment is XORed with f(k), which gives the 4 rows 4
+//    distinct segments;
+//  * R = 192 (6 segments, rows of 384 bytes, so rows k and k + 2 start at
+//    the same bank and k + 1 half the bank width further): an XOR would have
+//    to stay inside aligned pairs of segments, and left two rows of every
+//    group on the same banks (a third of the LDS cycles of these tiles went
+//    to bank conflicts); instead the segment is rotated by bit 1 of k, which
+//    with the row parity puts the 4 rows 0, 2, 1, 3 segments apart.
+// swz_m maps a logical chunk to its LDS slot (the fragment reads), unswz_m
+// a slot back to its logical chunk (the copies); for the XOR they agree.
 template <int R>
 __device__ __forceinline__ int swz_m(int chunk, int k) {
   constexpr int kSegs = R / 32;
-  constexpr int kP = kSegs & -kSegs;
-  const int f = ((k & 3) | (((k >> 3) & 1) << 2)) & (kP - 1);
-  return chunk ^ (f << 2);
+  if constexpr ((kSegs & (kSegs - 1)) == 0) {
+    const int f = ((k & 3) | (((k >> 3) & 1) << 2)) & (kSegs - 1);
+    return chunk ^ (f << 2);
+  } else {
+    const int c = chunk + (((k >> 1) & 1) << 2);
+    return c >= R / 8 ? c - R / 8 : c;
+  }
+}
+template <int R>
+__device__ __forceinline__ int unswz_m(int slot, int k) {
+  constexpr int kSegs = R / 32;
+  if constexpr ((kSegs & (kSegs - 1)) == 0) {
+    return swz_m<R>(slot, k);
+  } else {
+    const int c = slot - (((k >> 1) & 1) << 2);
+    return c < 0 ? c + R / 8 : c;
+  }
 }
 
 // Issue the copy of one operand tile (R rows of the tile's m or n range x
@@ -129,7 +153,7 @@ __device__ __forceinline__ void issue_tile(const u32x4& rs, char* stage, int wav
     } else {
       constexpr int kCpr = R / 8;  // 16-byte chunks per k-row
       const int kr = q / kCpr;
-      const int lc = swz_m<R>(q % kCpr, kr);
+      const int lc = unswz_m<R>(q % kCpr, kr);
       const int gk = k0 + kr, gm = row0 + lc * 8;
       off = (gk < K && gm < rmax) ? static_cast<uint32_t>(gk) * ld_bytes + gm * 2 : kOOB;
     }
@@ -158,7 +182,7 @@ __device__ __forceinline__ void tile_bases(uint32_t (&base)[R / 8 / NW], int wav
     } else {
       constexpr int kCpr = R / 8;
       const int kr = q / kCpr;
-      const int lc = swz_m<R>(q % kCpr, kr);
+      const int lc = unswz_m<R>(q % kCpr, kr);
       const int gm = row0 + lc * 8;
       base[i] = gm < rmax ? static_cast<uint32_t>(kr) * ld_bytes + gm * 2 : kOOB;
     }
