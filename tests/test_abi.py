@@ -209,3 +209,64 @@ def test_attn_bwd_noalloc_rejects_oversize_before_launch():
                                     None) == mtp.MTP_ERR_WORKSPACE
     assert lib.mtp_attn_bwd_noalloc(ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, None, 0,
                                     None) == mtp.MTP_ERR_INVALID_ARG
+
+
+def test_fp8_entry_points_refuse_bad_arguments():
+    """The FP8 quantization and linear maps reject every argument their
+    contract excludes with the documented status, before any launch: fp32
+    shards, formats and kinds outside the enums, widths that are not whole
+    16-byte chunks, reduction lengths that are not multiples of 16, missing
+    operands of a requested product, a bias on a row-parallel map, and the
+    GeLU derivative on anything but FC2."""
+    lib = mtp.lib()
+    d = valid()
+    bd = ctypes.byref(d)
+    I, U = mtp.MTP_ERR_INVALID_ARG, mtp.MTP_ERR_UNSUPPORTED
+    f32 = valid(dtype=mtp.MTP_F32)
+    parts = (ctypes.c_void_p * 17)(*([FAKE] * 17))
+    # fp32 shards have no FP8 path
+    assert lib.mtp_fp8_amax(ctypes.byref(f32), FAKE, 64, FAKE, None) == U
+    assert lib.mtp_fp8_quantize(ctypes.byref(f32), mtp.MTP_FP8_E4M3, FAKE, 8, 64, parts, 1, FAKE,
+                                FAKE, FAKE, None) == U
+    assert lib.mtp_linear_fwd_fp8(ctypes.byref(f32), mtp.MTP_QKV, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, None, None) == U
+    assert lib.mtp_linear_bwd_fp8(ctypes.byref(f32), mtp.MTP_QKV, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, None, FAKE, FAKE, 0, None) == U
+    # amax: whole 16-byte vectors only
+    assert lib.mtp_fp8_amax(bd, FAKE, 12, FAKE, None) == I
+    assert lib.mtp_fp8_amax(bd, FAKE, -8, FAKE, None) == I
+    assert lib.mtp_fp8_amax(bd, FAKE, 64, None, None) == I
+    # quantize: format, width, part count, pointers
+    q = lambda fmt=mtp.MTP_FP8_E4M3, x=FAKE, rows=8, cols=64, n=1, qq=FAKE, qt=FAKE, s=FAKE: \
+        lib.mtp_fp8_quantize(bd, fmt, x, rows, cols, parts, n, qq, qt, s, None)
+    assert q(fmt=5) == I
+    assert q(cols=60) == I
+    assert q(cols=0) == I
+    assert q(n=0) == I and q(n=17) == I
+    assert q(x=None) == I
+    assert q(qq=None, qt=None) == I
+    assert q(s=None) == I
+    parts[0] = FAKE + 4
+    assert q() == I
+    parts[0] = FAKE
+    # forward linear maps
+    fwd = lambda kind, b=None, pre=None, dd=bd: lib.mtp_linear_fwd_fp8(
+        dd, kind, FAKE, FAKE, FAKE, FAKE, b, FAKE, pre, None)
+    assert fwd(7) == I
+    assert fwd(mtp.MTP_PROJ, b=FAKE) == I          # the row-parallel bias comes after the sum
+    assert fwd(mtp.MTP_FC1) == I                    # FC1 writes its pre-activation
+    assert fwd(mtp.MTP_QKV, pre=FAKE) == I
+    odd = valid(ffn=2000)                            # f_l = 1000: 8 but not 16 bytes of codes
+    assert fwd(mtp.MTP_FC2, dd=ctypes.byref(odd)) == U
+    # backward: data gradient (dy8, W^T codes) and/or weight gradient (dy^T, x^T codes)
+    bwd = lambda kind, dy8=FAKE, dyt=FAKE, w8t=FAKE, x8t=FAKE, pre=None, dx=FAKE, dw=FAKE, dd=bd: \
+        lib.mtp_linear_bwd_fp8(dd, kind, dy8, dyt, FAKE, w8t, FAKE, x8t, FAKE, pre, dx, dw, 0, None)
+    assert bwd(7) == I
+    assert bwd(mtp.MTP_PROJ, pre=FAKE) == I         # GeLU' belongs to FC2
+    assert bwd(mtp.MTP_FC2, dy8=None) == I
+    assert bwd(mtp.MTP_FC2, w8t=None) == I
+    assert bwd(mtp.MTP_FC2, dyt=None) == I
+    assert bwd(mtp.MTP_FC2, x8t=None) == I
+    assert bwd(mtp.MTP_FC1, dd=ctypes.byref(odd), dw=None) == U   # data gradient reduces over f_l
+    ragged = valid(seq_len=2004)                     # weight gradient reduces over T
+    assert bwd(mtp.MTP_QKV, dd=ctypes.byref(ragged), dx=None) == U
