@@ -499,11 +499,28 @@ class TPLayer(_Probed):
         self.x = x
         with T("ln1"):
             mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+        # The weights' codes (made once per optimizer update; with gradient
+        # accumulation they serve every micro-batch until the next one): the
+        # QKV weight's on the main stream, the other three on the second
+        # stream, which has no other work in the forward; each GEMM waits for
+        # its weight's codes only.
+        side = self.side
         with T("quant_w"):
-            # the weights' codes (made once per optimizer update; with gradient
-            # accumulation they serve every micro-batch until the next one)
-            for name, key in (("wqkv", "wqkv"), ("wo", "wo"), ("w1", "w1"), ("w2", "w2")):
-                self._quant_split(name, {r: self.w[r][key] for r in self.ranks}, E4, ext)
+            self._quant_split("wqkv", {r: self.w[r]["wqkv"] for r in self.ranks}, E4, ext)
+        ready = {}
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream(self.device))
+        for name in ("wo", "w1", "w2"):
+            with (torch.cuda.stream(side) if side is not None else contextlib.nullcontext()), \
+                    T("quant_w", side):
+                self._quant_split(name, {r: self.w[r][name] for r in self.ranks}, E4, ext)
+            if side is not None:
+                ready[name] = torch.cuda.Event()
+                ready[name].record(side)
+
+        def wait_w(name):
+            if name in ready:
+                torch.cuda.current_stream(self.device).wait_event(ready[name])
         with T("quant"):
             self._quant_shared("ln1", self.ln1, E4)
         for r in self.ranks:
@@ -517,6 +534,7 @@ class TPLayer(_Probed):
                 mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
         with T("quant"):
             self._quant_split("ctx", {r: self.a[r]["ctx"] for r in self.ranks}, E4, ext)
+        wait_w("wo")
         for r in self.ranks:
             c = r8[r]
             with T("proj_fwd"):
@@ -528,6 +546,7 @@ class TPLayer(_Probed):
                                           rep["ln2_b"], self.ln2, self.mu2, self.rs2)
         with T("quant"):
             self._quant_shared("ln2", self.ln2, E4)
+        wait_w("w1")
         for r in self.ranks:
             w, a, c = self.w[r], self.a[r], r8[r]
             with T("fc1_fwd"):
@@ -535,6 +554,7 @@ class TPLayer(_Probed):
                                        c["w1"]["q"], c["w1"]["s"], w["b1"], a["g"], a["u"])
         with T("quant"):
             self._quant_split("g", {r: self.a[r]["g"] for r in self.ranks}, E4, ext)
+        wait_w("w2")
         for r in self.ranks:
             c = r8[r]
             with T("fc2_fwd"):
