@@ -684,7 +684,7 @@ hipError_t dispatch_tile(const GemmParams& p, int tile, hipStream_t s) {
 
 // FP8 tiles: 128x256, 256x128, 128x128 and 256x192 (64x96 wave tiles, the
 // largest whose doubled FP8 fragments fit the 256 registers of two waves
-// per SIMD, with a few spills); 256x192 fills the chip in one round where
+// per SIMD: 239 of them); 256x192 fills the chip in one round where
 // 128x256 needs one and a half (M = 2048 with N = 6144 or 5504), and stages
 // fewer bytes per k-tile than a 128x384 tile of the same area (measured
 // 52-55 vs 57-60 us).  Chosen by the cost of pick_tile: rounds x tile area
