@@ -119,9 +119,15 @@ typedef struct {
  * the column/row split each rank holds the whole [T,h] input, so the
  * statistics are computed locally with no exchange.
  *   x, y: [T,h] dtype.  gamma, beta: [h] dtype.  mean, rstd: [T] fp32 (out).
+ *   amax_parts: nullable, 1024 fp32 (out); when given, receives partial
+ *   maxima of |y| as stored, in the form mtp_fp8_amax writes (each part the
+ *   maximum over some of y's elements, unused parts 0, so the largest part
+ *   is y's amax), for mtp_fp8_quantize of y without a separate amax pass;
+ *   bf16 only (MTP_ERR_UNSUPPORTED for an fp32 shard).
  */
 int mtp_layernorm(const mtp_shard_desc* desc, const void* x, const void* gamma,
-                  const void* beta, void* y, float* mean, float* rstd, void* stream);
+                  const void* beta, void* y, float* mean, float* rstd, float* amax_parts,
+                  void* stream);
 
 /* LayerNorm backward.  dy: [T,h] gradient w.r.t. y; x, gamma, mean, rstd as
  * saved by mtp_layernorm.  dres: nullable [T,h] residual-branch gradient that
@@ -142,12 +148,13 @@ int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x,
  *   it (a single partial is used as is); then everything as
  *   mtp_layernorm_bwd(dy, ...).  The sum itself is not stored.
  * dy_partials: HOST array of n_partials (1..16) device pointers, [T,h] dtype.
+ * amax_parts: nullable, as in mtp_layernorm, of dx.
  * Other arguments, workspace and errors as mtp_layernorm_bwd.                */
 int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_partials,
                           int32_t n_partials, const void* x, const void* gamma,
                           const float* mean, const float* rstd, const void* dres, void* dx,
                           float* dgamma, float* dbeta, int accumulate, void* ws,
-                          size_t ws_bytes, void* stream);
+                          size_t ws_bytes, float* amax_parts, void* stream);
 
 /* ----------------------------------------------- column-parallel linear
  * ColumnParallelLinear with the output left sharded (page "Megatron-LM:
@@ -399,12 +406,12 @@ int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials,
  * fuses LayerNorm with its neighbours), in one pass where the width allows:
  *   out = exactly what mtp_partial_sum(partials, n_partials, bias, residual)
  *   stores; then ln_out, mean, rstd = exactly what mtp_layernorm(out, gamma,
- *   beta) writes.  Arguments as those two calls; out may alias residual or a
- *   partial.                                                                 */
+ *   beta, amax_parts) writes.  Arguments as those two calls; out may alias
+ *   residual or a partial.                                                   */
 int mtp_partial_sum_layernorm(const mtp_shard_desc* desc, const void* const* partials,
                               int32_t n_partials, const void* bias, const void* residual,
                               void* out, const void* gamma, const void* beta, void* ln_out,
-                              float* mean, float* rstd, void* stream);
+                              float* mean, float* rstd, float* amax_parts, void* stream);
 
 /* ------------------------------------------------- vocab-parallel CE head
  * Cross-entropy over a vocabulary split across ranks (VocabParallelEmbedding,

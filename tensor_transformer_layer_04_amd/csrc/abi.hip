@@ -141,14 +141,16 @@ size_t mtp_workspace_size(const mtp_shard_desc* desc, int op, int kind) {
 }
 
 int mtp_layernorm(const mtp_shard_desc* desc, const void* x, const void* gamma, const void* beta,
-                  void* y, float* mean, float* rstd, void* stream) {
+                  void* y, float* mean, float* rstd, float* amax_parts, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
-  if (!ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(beta) || !ok_ptr(y) || !ok_ptr(mean) || !ok_ptr(rstd))
+  if (!ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(beta) || !ok_ptr(y) || !ok_ptr(mean) ||
+      !ok_ptr(rstd) || !ok_opt(amax_parts))
     return MTP_ERR_INVALID_ARG;
+  if (amax_parts && !s.bf16) return MTP_ERR_UNSUPPORTED;
   return hip_status(mtp::layernorm_fwd(s.bf16, x, gamma, beta, y, mean, rstd, s.T, s.h, s.eps,
-                                       static_cast<hipStream_t>(stream)));
+                                       amax_parts, static_cast<hipStream_t>(stream)));
 }
 
 int mtp_layernorm_bwd(const mtp_shard_desc* desc, const void* dy, const void* x, const void* gamma,
@@ -172,7 +174,7 @@ int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_part
                           int32_t n_partials, const void* x, const void* gamma,
                           const float* mean, const float* rstd, const void* dres, void* dx,
                           float* dgamma, float* dbeta, int accumulate, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, float* amax_parts, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
@@ -180,13 +182,14 @@ int mtp_layernorm_bwd_sum(const mtp_shard_desc* desc, const void* const* dy_part
   for (int i = 0; i < n_partials; ++i)
     if (!ok_ptr(dy_partials[i])) return MTP_ERR_INVALID_ARG;
   if (!ok_ptr(x) || !ok_ptr(gamma) || !ok_ptr(mean) || !ok_ptr(rstd) || !ok_opt(dres) ||
-      !ok_ptr(dx) || !ok_ptr(dgamma) || !ok_ptr(dbeta))
+      !ok_ptr(dx) || !ok_ptr(dgamma) || !ok_ptr(dbeta) || !ok_opt(amax_parts))
     return MTP_ERR_INVALID_ARG;
+  if (amax_parts && !s.bf16) return MTP_ERR_UNSUPPORTED;
   const size_t need = mtp::layernorm_bwd_ws_bytes(s.T, s.h, s.bf16);
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
   return hip_status(mtp::layernorm_bwd_sum(s.bf16, dy_partials, n_partials, x, gamma, mean, rstd,
                                            dres, dx, dgamma, dbeta, accumulate != 0, s.T, s.h,
-                                           ws, static_cast<hipStream_t>(stream)));
+                                           ws, amax_parts, static_cast<hipStream_t>(stream)));
 }
 
 int mtp_col_linear_fwd(const mtp_shard_desc* desc, int kind, const void* x, const void* w,
@@ -612,7 +615,7 @@ int mtp_partial_sum(const mtp_shard_desc* desc, const void* const* partials, int
 int mtp_partial_sum_layernorm(const mtp_shard_desc* desc, const void* const* partials,
                               int32_t n_partials, const void* bias, const void* residual,
                               void* out, const void* gamma, const void* beta, void* ln_out,
-                              float* mean, float* rstd, void* stream) {
+                              float* mean, float* rstd, float* amax_parts, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
@@ -620,11 +623,12 @@ int mtp_partial_sum_layernorm(const mtp_shard_desc* desc, const void* const* par
   for (int i = 0; i < n_partials; ++i)
     if (!ok_ptr(partials[i])) return MTP_ERR_INVALID_ARG;
   if (!ok_opt(bias) || !ok_opt(residual) || !ok_ptr(out) || !ok_ptr(gamma) || !ok_ptr(beta) ||
-      !ok_ptr(ln_out) || !ok_ptr(mean) || !ok_ptr(rstd))
+      !ok_ptr(ln_out) || !ok_ptr(mean) || !ok_ptr(rstd) || !ok_opt(amax_parts))
     return MTP_ERR_INVALID_ARG;
+  if (amax_parts && !s.bf16) return MTP_ERR_UNSUPPORTED;
   return hip_status(mtp::sum_layernorm_fwd(s.bf16, partials, n_partials, bias, residual, out,
                                            gamma, beta, ln_out, mean, rstd, s.T, s.h, s.eps,
-                                           static_cast<hipStream_t>(stream)));
+                                           amax_parts, static_cast<hipStream_t>(stream)));
 }
 
 int mtp_vocab_ce_stats(const mtp_shard_desc* desc, const float* logits, const int32_t* targets,

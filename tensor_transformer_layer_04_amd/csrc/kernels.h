@@ -65,8 +65,11 @@ hipError_t column_sum(bool bf16, const void* x, int64_t rows, int64_t cols, floa
                       bool accumulate, void* ws, hipStream_t stream);
 
 // ------------------------------------------------------------- row-wise
+// amax (nullable, bf16 output): kAmaxParts partial maxima of |y| in
+// fp8_amax's form (their maximum is y's amax), from the LayerNorm kernel
+// itself where its grid fits, else by fp8_amax on y.
 hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void* beta, void* y,
-                         float* mean, float* rstd, int64_t T, int h, float eps,
+                         float* mean, float* rstd, int64_t T, int h, float eps, float* amax,
                          hipStream_t stream);
 size_t layernorm_bwd_ws_bytes(int64_t T, int h, bool bf16);
 hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* gamma,
@@ -80,12 +83,14 @@ hipError_t partial_sum(bool bf16, const void* const* partials, int n, const void
 hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, const void* bias,
                              const void* residual, void* out, const void* gamma,
                              const void* beta, void* y, float* mean, float* rstd, int64_t T,
-                             int h, float eps, hipStream_t stream);
-// LayerNorm backward of dy = sum of n partials (rounded to the storage type).
+                             int h, float eps, float* amax, hipStream_t stream);
+// LayerNorm backward of dy = sum of n partials (rounded to the storage type);
+// amax as in layernorm_fwd, of dx.
 hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const void* x,
                              const void* gamma, const float* mean, const float* rstd,
                              const void* dres, void* dx, float* dgamma, float* dbeta,
-                             bool accumulate, int64_t T, int h, void* ws, hipStream_t stream);
+                             bool accumulate, int64_t T, int h, void* ws, float* amax,
+                             hipStream_t stream);
 hipError_t zero_f32(float* p, int64_t n, hipStream_t stream);
 
 // ------------------------------------------------------------- attention

@@ -186,44 +186,73 @@ __device__ __forceinline__ float bfw(const uint4& v, int e) {
   return (e & 1) ? hi_bf(w) : lo_bf(w);
 }
 
+// Partial maximum of |output| of one workgroup for the FP8 scale of the
+// tensor it writes (the convention of fp8_amax_parts_kernel: amax[b] for
+// workgroup b, 0 in the slots no workgroup owns, so that the maximum over
+// the kAmaxParts slots is the tensor's).  mx is the lane's maximum of the
+// fp32 values it stored as bf16; rounding is monotonic, so the rounded
+// maximum is the maximum of the stored values.  Every thread of the
+// workgroup must call it (it has a barrier).
+template <int NWAVES>
+__device__ __forceinline__ void store_amax_part(float mx, float* amax) {
+  __shared__ float wm[NWAVES];
+  mx = warp_max(mx);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = wm[0];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) m = fmaxf(m, wm[w]);
+    amax[blockIdx.x] = lo_bf(pack_bf2(m, 0.0f));
+  }
+  if (blockIdx.x == 0)
+    for (int i = gridDim.x + threadIdx.x; i < kAmaxParts; i += NWAVES * 64) amax[i] = 0.0f;
+}
+
 template <int NC>
 __global__ void __launch_bounds__(256)
 layernorm_fwd_bf16_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                           const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
                           float* __restrict__ mean, float* __restrict__ rstd, int64_t T_rows,
-                          int h, float eps) {
+                          int h, float eps, float* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= T_rows) return;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * h);
-  uint4 v[NC];
+  float mx = 0.0f;
+  if (row < T_rows) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * h);
+    uint4 v[NC];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) v[i] = xr[lane + 64 * i];
-  float s = 0.0f;
+    for (int i = 0; i < NC; ++i) v[i] = xr[lane + 64 * i];
+    float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NC; ++i)
+    for (int i = 0; i < NC; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += bfw(v[i], e);
-  const float mu = warp_sum(s) / h;
-  float q = 0.0f;
+      for (int e = 0; e < 8; ++e) s += bfw(v[i], e);
+    const float mu = warp_sum(s) / h;
+    float q = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NC; ++i)
+    for (int i = 0; i < NC; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { const float d = bfw(v[i], e) - mu; q += d * d; }
-  const float rs = rsqrtf(warp_sum(q) / h + eps);
-  const uint4* gr = reinterpret_cast<const uint4*>(gamma);
-  const uint4* br = reinterpret_cast<const uint4*>(beta);
-  uint4* yr = reinterpret_cast<uint4*>(y + row * h);
+      for (int e = 0; e < 8; ++e) { const float d = bfw(v[i], e) - mu; q += d * d; }
+    const float rs = rsqrtf(warp_sum(q) / h + eps);
+    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+    const uint4* br = reinterpret_cast<const uint4*>(beta);
+    uint4* yr = reinterpret_cast<uint4*>(y + row * h);
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const uint4 g = gr[lane + 64 * i], b = br[lane + 64 * i];
-    float o[8];
+    for (int i = 0; i < NC; ++i) {
+      const uint4 g = gr[lane + 64 * i], b = br[lane + 64 * i];
+      float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bfw(v[i], e) - mu) * rs * bfw(g, e) + bfw(b, e);
-    yr[lane + 64 * i] = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]),
-                                   pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
+      for (int e = 0; e < 8; ++e) {
+        o[e] = (bfw(v[i], e) - mu) * rs * bfw(g, e) + bfw(b, e);
+        mx = fmaxf(mx, fabsf(o[e]));
+      }
+      yr[lane + 64 * i] = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]),
+                                     pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
+    }
+    if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
   }
-  if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+  if (amax) store_amax_part<4>(mx, amax);
 }
 
 template <int NC>
@@ -687,97 +716,104 @@ __global__ void __launch_bounds__(256)
 sum_layernorm_fwd_kernel(PartialPtrs parts, int n, const T* __restrict__ bias,
                          const T* residual, T* out, const T* __restrict__ gamma,
                          const T* __restrict__ beta, T* __restrict__ y, float* __restrict__ mean,
-                         float* __restrict__ rstd, int64_t T_rows, int h, float eps) {
+                         float* __restrict__ rstd, int64_t T_rows, int h, float eps,
+                         float* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= T_rows) return;
-  const int64_t base = row * h;
-  float v[NC][8];
-  if constexpr (NP > 0) {
-    static_assert(sizeof(T) == 2, "compile-time partial count: bf16 rows");
-    uint4 raw[NP][NC], rb[NC], rr[NC];
+  float mx = 0.0f;
+  if (row < T_rows) {
+    const int64_t base = row * h;
+    float v[NC][8];
+    if constexpr (NP > 0) {
+      static_assert(sizeof(T) == 2, "compile-time partial count: bf16 rows");
+      uint4 raw[NP][NC], rb[NC], rr[NC];
 #pragma unroll
-    for (int i = 0; i < NP; ++i)
+      for (int i = 0; i < NP; ++i)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          raw[i][c] = *reinterpret_cast<const uint4*>(static_cast<const T*>(parts.p[i]) + base +
+                                                      (lane + 64 * c) * 8);
+      if (bias) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          rb[c] = *reinterpret_cast<const uint4*>(bias + (lane + 64 * c) * 8);
+      }
+      if (residual) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          rr[c] = *reinterpret_cast<const uint4*>(residual + base + (lane + 64 * c) * 8);
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        raw[i][c] = *reinterpret_cast<const uint4*>(static_cast<const T*>(parts.p[i]) + base +
-                                                    (lane + 64 * c) * 8);
-    if (bias) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        rb[c] = *reinterpret_cast<const uint4*>(bias + (lane + 64 * c) * 8);
+        for (int e = 0; e < 8; ++e) {
+          float a = bfw(raw[0][c], e);
+#pragma unroll
+          for (int i = 1; i < NP; ++i) a += bfw(raw[i][c], e);
+          if (bias) a += bfw(rb[c], e);
+          if (residual) a += bfw(rr[c], e);
+          v[c][e] = a;
+        }
+    } else {
+      load_row<T, NC>(static_cast<const T*>(parts.p[0]) + base, lane, v);
+      for (int i = 1; i < n; ++i) {
+        float t[NC][8];
+        load_row<T, NC>(static_cast<const T*>(parts.p[i]) + base, lane, t);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+      }
+      if (bias) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          float t[8];
+          load8(bias + (lane + 64 * c) * 8, t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[c][e] += t[e];
+        }
+      }
+      if (residual) {
+        float t[NC][8];
+        load_row<T, NC>(residual + base, lane, t);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+      }
     }
-    if (residual) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        rr[c] = *reinterpret_cast<const uint4*>(residual + base + (lane + 64 * c) * 8);
+    for (int c = 0; c < NC; ++c) {
+      round8<T>(v[c]);
+      store8(out + base + (lane + 64 * c) * 8, v[c]);
     }
+    float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[c][e];
+    const float mu = warp_sum(s) / h;
+    float q = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float d = v[c][e] - mu; q += d * d; }
+    const float rs = rsqrtf(warp_sum(q) / h + eps);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float g[8], b[8], o[8];
+      load8(gamma + (lane + 64 * c) * 8, g);
+      load8(beta + (lane + 64 * c) * 8, b);
+#pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float a = bfw(raw[0][c], e);
-#pragma unroll
-        for (int i = 1; i < NP; ++i) a += bfw(raw[i][c], e);
-        if (bias) a += bfw(rb[c], e);
-        if (residual) a += bfw(rr[c], e);
-        v[c][e] = a;
+        o[e] = (v[c][e] - mu) * rs * g[e] + b[e];
+        mx = fmaxf(mx, fabsf(o[e]));
       }
-  } else {
-    load_row<T, NC>(static_cast<const T*>(parts.p[0]) + base, lane, v);
-    for (int i = 1; i < n; ++i) {
-      float t[NC][8];
-      load_row<T, NC>(static_cast<const T*>(parts.p[i]) + base, lane, t);
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
+      store8(y + base + (lane + 64 * c) * 8, o);
     }
-    if (bias) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        float t[8];
-        load8(bias + (lane + 64 * c) * 8, t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += t[e];
-      }
-    }
-    if (residual) {
-      float t[NC][8];
-      load_row<T, NC>(residual + base, lane, t);
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += t[c][e];
-    }
+    if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    round8<T>(v[c]);
-    store8(out + base + (lane + 64 * c) * 8, v[c]);
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += v[c][e];
-  const float mu = warp_sum(s) / h;
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { const float d = v[c][e] - mu; q += d * d; }
-  const float rs = rsqrtf(warp_sum(q) / h + eps);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float g[8], b[8], o[8];
-    load8(gamma + (lane + 64 * c) * 8, g);
-    load8(beta + (lane + 64 * c) * 8, b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mu) * rs * g[e] + b[e];
-    store8(y + base + (lane + 64 * c) * 8, o);
-  }
-  if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+  if (amax) store_amax_part<4>(mx, amax);
 }
 
 // ------------------------------------- LayerNorm bwd with column partials
@@ -799,7 +835,8 @@ __global__ void __launch_bounds__(512)
 layernorm_bwd_fused_kernel(PartialPtrs dys, int n, const T* __restrict__ x,
                            const T* __restrict__ gamma, const float* __restrict__ mean,
                            const float* __restrict__ rstd, const T* dres, T* dx, int64_t T_rows,
-                           int h, float* __restrict__ part_g, float* __restrict__ part_b) {
+                           int h, float* __restrict__ part_g, float* __restrict__ part_b,
+                           float* __restrict__ amax) {
   constexpr int NCW = NC / SPLIT;     // chunks per lane
   constexpr int kSlots = 8 / SPLIT;   // rows per iteration
   __shared__ float red[2][512 * NC];
@@ -815,6 +852,7 @@ layernorm_bwd_fused_kernel(PartialPtrs dys, int n, const T* __restrict__ x,
 #pragma unroll
     for (int e = 0; e < 8; ++e) { ag[c][e] = 0.0f; ab[c][e] = 0.0f; }
   }
+  float mx = 0.0f;  // max |dx| stored by this lane
   const int64_t per_iter = static_cast<int64_t>(gridDim.x) * kSlots;
   const int64_t iters = (T_rows + per_iter - 1) / per_iter;  // the same for every wave
   for (int64_t k = 0; k < iters; ++k) {
@@ -882,7 +920,10 @@ layernorm_bwd_fused_kernel(PartialPtrs dys, int n, const T* __restrict__ x,
           for (int e = 0; e < 8; ++e) o[e] = 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += rs * (dv[c][e] * gm[c][e] - m1 - xv[c][e] * m2);
+        for (int e = 0; e < 8; ++e) {
+          o[e] += rs * (dv[c][e] * gm[c][e] - m1 - xv[c][e] * m2);
+          mx = fmaxf(mx, fabsf(o[e]));
+        }
         store8(dx + base + col(c), o);
       }
     }
@@ -914,6 +955,7 @@ layernorm_bwd_fused_kernel(PartialPtrs dys, int n, const T* __restrict__ x,
   const float4* rg = reinterpret_cast<const float4*>(red[0]);
   const float4* rb = reinterpret_cast<const float4*>(red[1]);
   for (int i = threadIdx.x; i < h / 4; i += 512) { og[i] = rg[i]; ob[i] = rb[i]; }
+  if (amax) store_amax_part<8>(mx, amax);
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
@@ -1044,22 +1086,25 @@ int64_t colsum_parts(int64_t rows) {
 
 // ---------------------------------------------------------------- launchers
 
+// Returns whether the kernel also wrote the partial maxima of |y| (amax given,
+// the bf16 row kernel, and at most kAmaxParts workgroups).
 template <typename T>
-void ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
-            float* rstd, int64_t T_rows, int h, float eps, hipStream_t s) {
+bool ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+            float* rstd, int64_t T_rows, int h, float eps, float* amax, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((T_rows + 3) / 4));
   const int per_lane = (h / 8 + 63) / 64;
   if (sizeof(T) == 2 && h % 512 == 0 && per_lane <= 16) {
+    float* am = (amax && grid.x <= static_cast<unsigned>(kAmaxParts)) ? amax : nullptr;
 #define MTP_LN_FWD16(NC)                                                                     \
   hipLaunchKernelGGL((layernorm_fwd_bf16_kernel<NC>), grid, dim3(256), 0, s, cptr<bf16_t>(x), \
                      cptr<bf16_t>(gamma), cptr<bf16_t>(beta), static_cast<bf16_t*>(y), mean, \
-                     rstd, T_rows, h, eps)
+                     rstd, T_rows, h, eps, am)
     switch (per_lane) {
-      case 1: MTP_LN_FWD16(1); return;
-      case 2: MTP_LN_FWD16(2); return;
-      case 4: MTP_LN_FWD16(4); return;
-      case 8: MTP_LN_FWD16(8); return;
-      case 16: MTP_LN_FWD16(16); return;
+      case 1: MTP_LN_FWD16(1); return am != nullptr;
+      case 2: MTP_LN_FWD16(2); return am != nullptr;
+      case 4: MTP_LN_FWD16(4); return am != nullptr;
+      case 8: MTP_LN_FWD16(8); return am != nullptr;
+      case 16: MTP_LN_FWD16(16); return am != nullptr;
       default: break;
     }
 #undef MTP_LN_FWD16
@@ -1074,6 +1119,7 @@ void ln_fwd(const void* x, const void* gamma, const void* beta, void* y, float* 
   else if (per_lane <= 8) MTP_LN_FWD(8);
   else MTP_LN_FWD(0);
 #undef MTP_LN_FWD
+  return false;
 }
 
 template <typename T>
@@ -1112,12 +1158,15 @@ void ln_bwd_rows(const void* dy, const void* x, const void* gamma, const float* 
 }  // namespace
 
 hipError_t layernorm_fwd(bool bf16, const void* x, const void* gamma, const void* beta, void* y,
-                         float* mean, float* rstd, int64_t T, int h, float eps,
+                         float* mean, float* rstd, int64_t T, int h, float eps, float* amax,
                          hipStream_t s) {
-  if (T == 0) return hipSuccess;
   if (h / 8 > kMaxRowChunks) return hipErrorInvalidValue;
-  if (bf16) ln_fwd<bf16_t>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
-  else ln_fwd<float>(x, gamma, beta, y, mean, rstd, T, h, eps, s);
+  bool fused = false;
+  if (T > 0) {
+    if (bf16) fused = ln_fwd<bf16_t>(x, gamma, beta, y, mean, rstd, T, h, eps, amax, s);
+    else fused = ln_fwd<float>(x, gamma, beta, y, mean, rstd, T, h, eps, amax, s);
+  }
+  if (amax && !fused) return fp8_amax(y, T * h, amax, s);
   return hipGetLastError();
 }
 
@@ -1156,22 +1205,23 @@ size_t layernorm_bwd_ws_bytes(int64_t T, int h, bool bf16) {
 hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, const void* bias,
                              const void* residual, void* out, const void* gamma,
                              const void* beta, void* y, float* mean, float* rstd, int64_t T,
-                             int h, float eps, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                             int h, float eps, float* amax, hipStream_t s) {
   if (h / 8 > kMaxRowChunks || n < 1 || n > kMaxPartials) return hipErrorInvalidValue;
+  if (T == 0) return amax ? fp8_amax(y, 0, amax, s) : hipSuccess;
   const int nc = fused_row_nc(h);
   if (nc == 0) {
     const hipError_t e = partial_sum(bf16, partials, n, bias, residual, out, T, h, s);
     if (e != hipSuccess) return e;
-    return layernorm_fwd(bf16, out, gamma, beta, y, mean, rstd, T, h, eps, s);
+    return layernorm_fwd(bf16, out, gamma, beta, y, mean, rstd, T, h, eps, amax, s);
   }
   PartialPtrs pp{};
   for (int i = 0; i < n; ++i) pp.p[i] = partials[i];
   const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+  float* am = (amax && bf16 && grid.x <= static_cast<unsigned>(kAmaxParts)) ? amax : nullptr;
 #define MTP_SUM_LN(TT, NC, NP)                                                                 \
   hipLaunchKernelGGL((sum_layernorm_fwd_kernel<TT, NC, NP>), grid, dim3(256), 0, s, pp, n,       \
                      cptr<TT>(bias), cptr<TT>(residual), static_cast<TT*>(out), cptr<TT>(gamma), \
-                     cptr<TT>(beta), static_cast<TT*>(y), mean, rstd, T, h, eps)
+                     cptr<TT>(beta), static_cast<TT*>(y), mean, rstd, T, h, eps, am)
 #define MTP_SUM_LN_T(TT, NP)                  \
   switch (nc) {                               \
     case 1: MTP_SUM_LN(TT, 1, NP); break;     \
@@ -1191,13 +1241,15 @@ hipError_t sum_layernorm_fwd(bool bf16, const void* const* partials, int n, cons
   }
 #undef MTP_SUM_LN_T
 #undef MTP_SUM_LN
+  if (amax && !am) return fp8_amax(y, T * h, amax, s);
   return hipGetLastError();
 }
 
 hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const void* x,
                              const void* gamma, const float* mean, const float* rstd,
                              const void* dres, void* dx, float* dgamma, float* dbeta,
-                             bool accumulate, int64_t T, int h, void* ws, hipStream_t s) {
+                             bool accumulate, int64_t T, int h, void* ws, float* amax,
+                             hipStream_t s) {
   if (h / 8 > kMaxRowChunks || n < 1 || n > kMaxPartials) return hipErrorInvalidValue;
   const int nc = fused_bwd_nc(h);
   float* pg = static_cast<float*>(ws);
@@ -1230,10 +1282,13 @@ hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const voi
     hipLaunchKernelGGL(reduce_parts_kernel, rg, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
                        dbeta, static_cast<int>(T > 0 ? parts : 0), static_cast<int64_t>(h),
                        accumulate ? 1 : 0);
+    if (amax) return fp8_amax(dx, T * h, amax, s);
     return hipGetLastError();
   }
   const int64_t blocks = ln_bwd_blocks(T);
   float* pb = pg + blocks * h;
+  // at most 256 workgroups: the partial maxima of |dx| fit kAmaxParts
+  float* am = (amax && bf16 && T > 0) ? amax : nullptr;
   if (T > 0) {
     PartialPtrs pp{};
     for (int i = 0; i < n; ++i) pp.p[i] = dys[i];
@@ -1241,7 +1296,7 @@ hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const voi
 #define MTP_LN_BWD_F(TT, NC, SPLIT)                                                             \
   hipLaunchKernelGGL((layernorm_bwd_fused_kernel<TT, NC, SPLIT>), grid, dim3(512), 0, s, pp, n,   \
                      cptr<TT>(x), cptr<TT>(gamma), mean, rstd, cptr<TT>(dres),                   \
-                     static_cast<TT*>(dx), T, h, pg, pb)
+                     static_cast<TT*>(dx), T, h, pg, pb, am)
 #define MTP_LN_BWD_F_T(TT)                      \
   switch (nc) {                                 \
     case 1: MTP_LN_BWD_F(TT, 1, 1); break;      \
@@ -1259,6 +1314,7 @@ hipError_t layernorm_bwd_sum(bool bf16, const void* const* dys, int n, const voi
   hipLaunchKernelGGL(reduce_parts_kernel, rg, dim3(kRedCols * kRedLanes), 0, s, pg, dgamma, pb,
                      dbeta, static_cast<int>(T > 0 ? blocks : 0), static_cast<int64_t>(h),
                      accumulate ? 1 : 0);
+  if (amax && !am) return fp8_amax(dx, T * h, amax, s);
   return hipGetLastError();
 }
 
@@ -1268,7 +1324,7 @@ hipError_t layernorm_bwd(bool bf16, const void* dy, const void* x, const void* g
                          void* ws, hipStream_t s) {
   const void* dys[1] = {dy};
   return layernorm_bwd_sum(bf16, dys, 1, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
-                           accumulate, T, h, ws, s);
+                           accumulate, T, h, ws, nullptr, s);
 }
 
 size_t column_sum_ws_bytes(int64_t rows, int64_t cols) {

@@ -295,10 +295,12 @@ class TPLayer(_Probed):
                   "wqkv": (3 * hl, h), "wo": (h, hl), "w1": (fl, h), "w2": (h, fl)}
         self.r8 = {r: {k: slot(*sh) for k, sh in shapes.items()} for r in self.ranks}
 
-    def _quant_shared(self, name, x, fmt):
-        """amax and codes of a tensor every rank holds whole."""
+    def _quant_shared(self, name, x, fmt, amax_written=False):
+        """amax and codes of a tensor every rank holds whole (amax_written:
+        the kernel that produced x already wrote its amax parts)."""
         sl = self.q8[name]
-        mtp.mtp_fp8_amax(self.d0, x, x.numel(), sl["amax"])
+        if not amax_written:
+            mtp.mtp_fp8_amax(self.d0, x, x.numel(), sl["amax"])
         mtp.mtp_fp8_quantize(self.d0, fmt, x, sl["rows"], sl["cols"], [sl["amax"]], sl["q"],
                              sl["qt"], sl["s"])
 
@@ -498,7 +500,8 @@ class TPLayer(_Probed):
         E4, q8, r8 = mtp.MTP_FP8_E4M3, self.q8, self.r8
         self.x = x
         with T("ln1"):
-            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1)
+            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1,
+                              amax_parts=q8["ln1"]["amax"])
         # The weights' codes (made once per optimizer update; with gradient
         # accumulation they serve every micro-batch until the next one): the
         # QKV weight's on the main stream, the other three on the second
@@ -522,7 +525,7 @@ class TPLayer(_Probed):
             if name in ready:
                 torch.cuda.current_stream(self.device).wait_event(ready[name])
         with T("quant"):
-            self._quant_shared("ln1", self.ln1, E4)
+            self._quant_shared("ln1", self.ln1, E4, amax_written=True)
         for r in self.ranks:
             d, w, a, c = self.descs[r], self.w[r], self.a[r], r8[r]
             with T("qkv_fwd"):
@@ -543,9 +546,10 @@ class TPLayer(_Probed):
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
         with T("sum_proj_ln2"):
             mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
-                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2)
+                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2,
+                                          amax_parts=q8["ln2"]["amax"])
         with T("quant"):
-            self._quant_shared("ln2", self.ln2, E4)
+            self._quant_shared("ln2", self.ln2, E4, amax_written=True)
         wait_w("w1")
         for r in self.ranks:
             w, a, c = self.w[r], self.a[r], r8[r]
@@ -617,10 +621,10 @@ class TPLayer(_Probed):
         with T("ln2_bwd"):
             mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
                                       self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0,
-                                      ws, wsb)
+                                      ws, wsb, amax_parts=q8["dy1"]["amax"])
         # PROJ: dctx_r = dy1 Wo_r; dWo_r = dy1^T ctx_r; then attention
         with T("quant"):
-            self._quant_shared("dy1", self.dy1, E5)
+            self._quant_shared("dy1", self.dy1, E5, amax_written=True)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]

@@ -47,7 +47,7 @@ _SIGS = {
     "mtp_version": (ctypes.c_int, []),
     "mtp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mtp_workspace_size": (ctypes.c_size_t, [_VP, ctypes.c_int, ctypes.c_int]),
-    "mtp_layernorm": (ctypes.c_int, [_VP] + [_VP] * 6 + [_VP]),
+    "mtp_layernorm": (ctypes.c_int, [_VP] + [_VP] * 7 + [_VP]),
     "mtp_layernorm_bwd": (ctypes.c_int, [_VP] + [_VP] * 9 + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
     "mtp_col_linear_fwd": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 5 + [_VP]),
     "mtp_col_linear_bwd": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 6
@@ -70,9 +70,9 @@ _SIGS = {
     "mtp_attn_bwd_block": (ctypes.c_int, [_VP] + [_VP] * 5 + [ctypes.c_int64] * 4
                            + [ctypes.c_int, _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "mtp_partial_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
-    "mtp_partial_sum_layernorm": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8 + [_VP]),
+    "mtp_partial_sum_layernorm": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 9 + [_VP]),
     "mtp_layernorm_bwd_sum": (ctypes.c_int, [_VP, _VP, ctypes.c_int32] + [_VP] * 8
-                              + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
+                              + [ctypes.c_int, _VP, ctypes.c_size_t, _VP, _VP]),
     "mtp_vocab_ce_stats": (ctypes.c_int, [_VP] + [_VP] * 5 + [_VP]),
     "mtp_vocab_ce_combine": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32] + [_VP] * 4 + [_VP]),
     "mtp_vocab_ce_bwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_float, _VP, _VP]),
@@ -147,9 +147,9 @@ def mtp_workspace_size(desc, op, kind=0) -> int:
     return lib().mtp_workspace_size(ctypes.byref(desc), op, kind)
 
 
-def mtp_layernorm(desc, x, gamma, beta, y, mean, rstd, stream=None):
+def mtp_layernorm(desc, x, gamma, beta, y, mean, rstd, amax_parts=None, stream=None):
     return _call("mtp_layernorm", ctypes.byref(desc), _addr(x), _addr(gamma), _addr(beta),
-                 _addr(y), _addr(mean), _addr(rstd), _stream(stream))
+                 _addr(y), _addr(mean), _addr(rstd), _addr(amax_parts), _stream(stream))
 
 
 def mtp_layernorm_bwd(desc, dy, x, gamma, mean, rstd, dres, dx, dgamma, dbeta, accumulate, ws,
@@ -253,19 +253,20 @@ def mtp_partial_sum(desc, partials, bias, residual, out, stream=None):
 
 
 def mtp_partial_sum_layernorm(desc, partials, bias, residual, out, gamma, beta, ln_out, mean,
-                              rstd, stream=None):
+                              rstd, amax_parts=None, stream=None):
     arr = _ptr_array(partials)
     return _call("mtp_partial_sum_layernorm", ctypes.byref(desc), arr, len(partials), _addr(bias),
                  _addr(residual), _addr(out), _addr(gamma), _addr(beta), _addr(ln_out),
-                 _addr(mean), _addr(rstd), _stream(stream))
+                 _addr(mean), _addr(rstd), _addr(amax_parts), _stream(stream))
 
 
 def mtp_layernorm_bwd_sum(desc, dy_partials, x, gamma, mean, rstd, dres, dx, dgamma, dbeta,
-                          accumulate, ws, ws_bytes, stream=None):
+                          accumulate, ws, ws_bytes, amax_parts=None, stream=None):
     arr = _ptr_array(dy_partials)
     return _call("mtp_layernorm_bwd_sum", ctypes.byref(desc), arr, len(dy_partials), _addr(x),
                  _addr(gamma), _addr(mean), _addr(rstd), _addr(dres), _addr(dx), _addr(dgamma),
-                 _addr(dbeta), int(accumulate), _addr(ws), ws_bytes, _stream(stream))
+                 _addr(dbeta), int(accumulate), _addr(ws), ws_bytes, _addr(amax_parts),
+                 _stream(stream))
 
 
 def mtp_vocab_ce_stats(desc, logits, targets, m, s, z_tgt, stream=None):

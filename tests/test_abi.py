@@ -48,7 +48,7 @@ FAKE = 1 << 20  # aligned non-null address; never dereferenced on these paths
 
 def ln(desc, x=FAKE):
     return mtp.lib().mtp_layernorm(ctypes.byref(desc) if desc is not None else None,
-                                   x, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+                                   x, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -270,3 +270,20 @@ def test_fp8_entry_points_refuse_bad_arguments():
     assert bwd(mtp.MTP_FC1, dd=ctypes.byref(odd), dw=None) == U   # data gradient reduces over f_l
     ragged = valid(seq_len=2004)                     # weight gradient reduces over T
     assert bwd(mtp.MTP_QKV, dd=ctypes.byref(ragged), dx=None) == U
+
+
+def test_layernorm_amax_parts_arguments():
+    """The FP8 amax parts of the LayerNorm entry points: refused for an fp32
+    shard (there is no FP8 path for it) and when misaligned, before any
+    launch."""
+    lib = mtp.lib()
+    f32 = ctypes.byref(valid(dtype=mtp.MTP_F32))
+    bd = ctypes.byref(valid())
+    U, I = mtp.MTP_ERR_UNSUPPORTED, mtp.MTP_ERR_INVALID_ARG
+    parts = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    for d, am, want in ((f32, FAKE, U), (bd, FAKE + 4, I)):
+        assert lib.mtp_layernorm(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, am, None) == want
+        assert lib.mtp_partial_sum_layernorm(d, parts, 2, None, None, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, FAKE, am, None) == want
+        assert lib.mtp_layernorm_bwd_sum(d, parts, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                         FAKE, 0, FAKE, 1 << 30, am, None) == want

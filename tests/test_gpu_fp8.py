@@ -133,6 +133,81 @@ def test_fp8_quantize_shards_both_layouts(fmt, rows, cols, n_shards, std):
         assert np.array_equal(qt.cpu().numpy(), ref.T), f"shard {i}: transposed codes differ"
 
 
+# h, T, n: the fused paths (LayerNorm grid within the 1024 parts, one-pass
+# sum + LayerNorm, fused backward), a LayerNorm grid of 1025 workgroups, and
+# widths that take the separate kernels (then the parts come from a pass of
+# their own over the output).
+AMAX_LN_CASES = [(4096, 2048, 2), (4096, 4100, 2), (768, 77, 2), (12288, 9, 4), (512, 5, 1)]
+
+
+@pytest.mark.parametrize("h,T,n", AMAX_LN_CASES)
+def test_amax_parts_from_layernorm_kernels(h, T, n):
+    """The amax parts that the LayerNorm forward, the partial sum + LayerNorm
+    and the LayerNorm backward of summed partials write beside their bf16
+    output: the maximum over the 1024 parts is the largest |value| stored,
+    every slot is written (the buffer starts at 1e30), the codes and scale
+    made from them equal those made from a separate amax pass bit for bit,
+    and the outputs equal those of the calls without parts."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    d = mtp.make_desc(h, h // 64, 4 * h, 1, 0, T, 1, mtp.MTP_BF16)
+    g = torch.Generator().manual_seed(700 + h + T)
+    R = lambda *sh, std=1.0: (torch.randn(*sh, generator=g) * std).to(torch.bfloat16).cuda()
+    x, res = R(T, h), R(T, h)
+    parts = [R(T, h) for _ in range(n)]
+    dys = [R(T, h, std=0.01) for _ in range(n)]
+    gm, bt, bias = (1 + R(h, std=0.1).float()).to(torch.bfloat16), R(h, std=0.1), R(h, std=0.1)
+    x[T // 2, 7] = 40.0   # a row whose LayerNorm output has one clear maximum
+    E = lambda: torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
+    F = lambda k=T: torch.empty(k, dtype=torch.float32, device="cuda")
+    P = lambda: torch.full((mtp.FP8_AMAX_PARTS,), 1e30, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(mtp.mtp_workspace_size(d, mtp.MTP_OP_LAYERNORM_BWD), 256),
+                     dtype=torch.uint8, device="cuda")
+
+    def outputs():
+        """(name, output, parts) of the three producers with amax parts, and
+        the same outputs of the calls without them."""
+        res_ = []
+        y0, y1, mu, rs = E(), E(), F(), F()
+        mtp.mtp_layernorm(d, x, gm, bt, y0, mu, rs)
+        p = P()
+        mtp.mtp_layernorm(d, x, gm, bt, y1, mu, rs, amax_parts=p)
+        res_.append(("layernorm", y1, y0, p))
+        o0, o1, l0, l1 = E(), E(), E(), E()
+        mtp.mtp_partial_sum_layernorm(d, parts, bias, res, o0, gm, bt, l0, mu, rs)
+        p = P()
+        mtp.mtp_partial_sum_layernorm(d, parts, bias, res, o1, gm, bt, l1, mu, rs, amax_parts=p)
+        assert torch.equal(o0, o1)
+        res_.append(("sum_layernorm", l1, l0, p))
+        dx0, dx1, dg, db = E(), E(), F(h), F(h)
+        mtp.mtp_layernorm_bwd_sum(d, dys, o0, gm, mu, rs, res, dx0, dg, db, 0, ws, ws.numel())
+        p = P()
+        mtp.mtp_layernorm_bwd_sum(d, dys, o0, gm, mu, rs, res, dx1, dg, db, 0, ws, ws.numel(),
+                                  amax_parts=p)
+        res_.append(("layernorm_bwd_sum", dx1, dx0, p))
+        return res_
+
+    for name, y, y_plain, p in outputs():
+        assert torch.equal(y, y_plain), f"{name}: output changed by writing amax parts"
+        ref = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_amax(d, y, y.numel(), ref)
+        torch.cuda.synchronize()
+        want = float(y.float().abs().max())
+        log(f"amax parts {name} h={h} T={T}: fused {float(p.max())!r} separate "
+            f"{float(ref.max())!r} max|y| {want!r}")
+        assert float(p.max()) == want == float(ref.max())
+        assert float(p.min()) >= 0.0
+        for fmt in (mtp.MTP_FP8_E4M3, mtp.MTP_FP8_E5M2):
+            codes = []
+            for pp in (p, ref):
+                q = torch.empty(T, h, dtype=torch.uint8, device="cuda")
+                s = torch.empty(1, dtype=torch.float32, device="cuda")
+                mtp.mtp_fp8_quantize(d, fmt, y, T, h, [pp], q, None, s)
+                codes.append((q, s))
+            torch.cuda.synchronize()
+            assert torch.equal(codes[0][0], codes[1][0]) and torch.equal(codes[0][1], codes[1][1])
+
+
 @pytest.mark.parametrize("T", [2048, 304])
 def test_fp8_backward_gemms_7b_shard(T):
     """Data and weight gradients of the four linear maps from FP8 codes (E5M2
