@@ -539,6 +539,38 @@ __global__ void __launch_bounds__(256) fp8_amax_parts_kernel(const bf16_t* __res
 
 struct AmaxParts { const float* p[kMaxPartials]; int n; };
 
+// x / s rounded to fp32 (the quotient the codes are defined on).  FAST: x * r
+// corrected by one residual step, r = fl32(1 / s), the residual x - q0 s
+// exact in an FMA, with the sign of x (the final sum would turn -0 into +0).
+// Over every pair of bf16 values |x| <= amax with s = fl32(amax / fmax) in
+// [2^-60, inf) this has the sign of the IEEE quotient and equals it wherever
+// either magnitude reaches 2^-18; below that both round to the code of a
+// signed zero in either format (checked exhaustively on the host).  Other
+// scales divide.
+template <bool FAST>
+__device__ __forceinline__ float fp8_quotient(float x, float s, float r) {
+  if constexpr (FAST) {
+    const float q0 = __fmul_rn(x, r);
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0), x);
+  } else {
+    return x / s;
+  }
+}
+
+// Codes of four fp32 values (|v| <= fmax) packed little-endian into a word:
+// the conversion instruction rounds to nearest, ties to even, and keeps the
+// subnormals of the format (E4M3: MANT 3; E5M2: MANT 2).
+template <int MANT>
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+  if constexpr (MANT == 3) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+  } else {
+    const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true));
+  }
+}
+
 // Codes of x [rows, cols] (row-major bf16, cols % 8 == 0) with the scale
 // s = amax / fmax, amax the maximum over the n arrays of kAmaxParts partial
 // maxima (one array per shard of the tensor).  Each workgroup converts a
@@ -548,7 +580,42 @@ struct AmaxParts { const float* p[kMaxPartials]; int n; };
 // its columns into one 4-byte LDS word; the transposed tile's rows are
 // padded to 33 words, which puts the 64 lanes' words in 64 distinct banks.
 constexpr int kQRows = 128, kQCols = 64, kQPitch = kQRows + 4;
-template <int MANT, int BIAS>
+
+// The codes of a lane's 4 rows x 8 columns: row-major words rw[i][0..1]
+// (columns 0-3, 4-7 of row i) and, per column, the word of its 4 rows.
+template <bool FAST, int MANT>
+__device__ __forceinline__ void fp8_codes_4x8(const uint4 (&raw)[4], float s, float r, float fmax,
+                                              uint32_t (&rw)[4][2], uint32_t (&col4)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = __builtin_amdgcn_fmed3f(fp8_quotient<FAST>(v[e], s, r), -fmax, fmax);
+    rw[i][0] = fp8_pack4<MANT>(v[0], v[1], v[2], v[3]);
+    rw[i][1] = fp8_pack4<MANT>(v[4], v[5], v[6], v[7]);
+  }
+  // 4x4 byte transposes: column e's word holds rows 0..3 in bytes 0..3
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a01 = __builtin_amdgcn_perm(rw[1][h], rw[0][h], 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+    const uint32_t b01 = __builtin_amdgcn_perm(rw[1][h], rw[0][h], 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+    const uint32_t a23 = __builtin_amdgcn_perm(rw[3][h], rw[2][h], 0x05010400u);
+    const uint32_t b23 = __builtin_amdgcn_perm(rw[3][h], rw[2][h], 0x07030602u);
+    col4[4 * h + 0] = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+    col4[4 * h + 1] = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+    col4[4 * h + 2] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+    col4[4 * h + 3] = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+  }
+}
+
+template <int MANT>
 __global__ void __launch_bounds__(256)
 fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxParts parts,
                    float fmax, uint8_t* __restrict__ q, uint8_t* __restrict__ qt, float* scale) {
@@ -559,7 +626,8 @@ fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxPar
   const int c0 = blockIdx.x * kQCols;
   const int lc = (tid & 7) * 8, lg = tid >> 3;  // columns lc..lc+7, rows 4lg..4lg+3
   const int c = c0 + lc;
-  // every load is issued before the scale is known
+  // every load is issued before the scale is known; rows past the end read
+  // as zeros (their codes are not stored)
   uint4 raw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -577,24 +645,17 @@ fp8_convert_kernel(const bf16_t* __restrict__ x, int64_t rows, int cols, AmaxPar
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / fmax : 1.0f;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) scale[0] = s;
-  uint32_t col4[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // column e: the 4 rows' codes
+  uint32_t rw[4][2], col4[8];
+  if (s >= 0x1p-60f && s < __builtin_huge_valf())
+    fp8_codes_4x8<true, MANT>(raw, s, 1.0f / s, fmax, rw, col4);
+  else
+    fp8_codes_4x8<false, MANT>(raw, s, 1.0f, fmax, rw, col4);
+  if (q && c < cols) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = r0 + 4 * lg + i;
-    if (r >= rows || c >= cols) continue;
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    uint32_t code[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      code[2 * k] = fp8_code<MANT, BIAS>(__uint_as_float(w[k] << 16) / s, fmax);
-      code[2 * k + 1] = fp8_code<MANT, BIAS>(__uint_as_float(w[k] & 0xffff0000u) / s, fmax);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * lg + i;
+      if (r < rows) *reinterpret_cast<uint2*>(q + r * cols + c) = make_uint2(rw[i][0], rw[i][1]);
     }
-    if (q)
-      *reinterpret_cast<uint2*>(q + r * cols + c) =
-          make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                     code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) col4[e] |= code[e] << (8 * i);
   }
   if (!qt) return;
 #pragma unroll
@@ -1434,10 +1495,10 @@ hipError_t fp8_quantize(int fmt, const void* x, int64_t rows, int cols, const fl
   if (rt > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((cols + kQCols - 1) / kQCols), static_cast<unsigned>(rt));
   if (fmt == kFp8E5M2)
-    hipLaunchKernelGGL((fp8_convert_kernel<2, 15>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
+    hipLaunchKernelGGL((fp8_convert_kernel<2>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
                        cols, ap, 57344.0f, q, qt, scale);
   else
-    hipLaunchKernelGGL((fp8_convert_kernel<3, 7>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
+    hipLaunchKernelGGL((fp8_convert_kernel<3>), grid, dim3(256), 0, s, cptr<bf16_t>(x), rows,
                        cols, ap, kE4M3Max, q, qt, scale);
   return hipGetLastError();
 }

@@ -133,6 +133,57 @@ def test_fp8_quantize_shards_both_layouts(fmt, rows, cols, n_shards, std):
         assert np.array_equal(qt.cpu().numpy(), ref.T), f"shard {i}: transposed codes differ"
 
 
+def _bf16_values_upto(amax):
+    """Every bf16 value x with |x| <= amax (amax a positive bf16 value), both
+    signs, as fp32."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    v = v[v <= np.float32(amax)]
+    return np.concatenate([v, -v])
+
+
+# amax per format: plain and all-ones / one-bit significands, the formats'
+# maxima, tiny and huge tensors, and the two bf16 values around the scale
+# 2^-60 where the convert kernel changes from multiplying by 1/s to dividing.
+FP8_AMAX_SWEEP = {
+    "e4m3": [1.0, 3.140625, 1.9921875, 1.0078125, 448.0, 57344.0, 9984.0, 0.0302734375, 2.0 ** -20,
+             2.0 ** -100, 3.3895313892515355e38, 1.75 * 2.0 ** -52, 1.7421875 * 2.0 ** -52],
+    "e5m2": [1.0, 3.140625, 1.9921875, 1.0078125, 448.0, 57344.0, 9984.0, 0.0302734375, 2.0 ** -20,
+             2.0 ** -100, 3.3895313892515355e38, 1.75 * 2.0 ** -45, 1.7421875 * 2.0 ** -45],
+}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_codes_of_every_bf16_value(fmt):
+    """For each amax of the sweep, the tensor of every bf16 value up to it
+    (both signs; 255 rows, a ragged count for the 128-row tiles and for the
+    16-byte transposed stores): row-major and transposed codes and the
+    scale bit for bit against the oracle."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    d = mtp.make_desc(4096, 32, 11008, 2, 0, 2048, 1, mtp.MTP_BF16)
+    code = mtp.MTP_FP8_E4M3 if fmt == "e4m3" else mtp.MTP_FP8_E5M2
+    cols = 256
+    for amax in FP8_AMAX_SWEEP[fmt]:
+        v = _bf16_values_upto(amax)
+        x = np.zeros(((v.size + cols - 1) // cols) * cols, np.float32)
+        x[:v.size] = v
+        x = x.reshape(-1, cols)
+        xt = torch.from_numpy(x).to(torch.bfloat16)
+        assert torch.equal(xt.float(), torch.from_numpy(x)), "sweep values must be bf16"
+        (q, qt, s), = _amax_and_quant(d, code, [xt.cuda()])
+        qo, so = ofp8.quantize_per_tensor(x, fmt)
+        ref = ofp8.fp8_encode(qo, fmt).reshape(x.shape)
+        got, got_t = q.cpu().numpy(), qt.cpu().numpy()
+        bad = np.argwhere(got != ref)
+        log(f"{fmt} amax {amax!r}: {x.shape[0]} rows, scale {float(s[0])!r} / {float(so)!r}, "
+            f"{len(bad)} codes differ" + (f"; first x={x[tuple(bad[0])]!r} got {got[tuple(bad[0])]:#04x} "
+                                          f"want {ref[tuple(bad[0])]:#04x}" if len(bad) else ""))
+        assert float(s[0]) == float(so)
+        assert len(bad) == 0
+        assert np.array_equal(got_t, ref.T)
+
+
 # h, T, n: the fused paths (LayerNorm grid within the 1024 parts, one-pass
 # sum + LayerNorm, fused backward), a LayerNorm grid of 1025 workgroups, and
 # widths that take the separate kernels (then the parts come from a pass of

@@ -1,5 +1,10 @@
-"""Host-side logic of the layer driver (CPU): the SwiGLU weight interleave
-and the sequence-parallel row split checks.  No GPU work."""
+"""Host-side logic of the layer driver (CPU): the SwiGLU weight interleave,
+the sequence-parallel row split checks, and the arithmetic identity the FP8
+convert kernel relies on.  No GPU work."""
+import os
+import shutil
+import subprocess
+
 import pytest
 import torch
 
@@ -99,3 +104,21 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_fp8_division_free_quotient_is_exact_on_every_bf16_pair(tmp_path):
+    """The FP8 convert kernel forms fl32(x / s) as x * fl32(1/s) plus one FMA
+    residual correction, with the sign of x, when s >= 2^-60.
+    tests/host/fp8_quotient_check.c compares that with the IEEE quotient for
+    every pair of bf16 values |x| <= amax and both formats' scales (about
+    2e9 pairs): no pair may differ in a way that can change a code."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this host")
+    src = os.path.join(os.path.dirname(__file__), "host", "fp8_quotient_check.c")
+    exe = str(tmp_path / "fp8_quotient_check")
+    subprocess.run([cc, "-O2", "-fopenmp", "-ffp-contract=off", src, "-o", exe, "-lm"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    print(out.stdout.strip())
+    assert out.returncode == 0, out.stdout
+    assert out.stdout.split()[-1] == "0"
