@@ -294,10 +294,13 @@ int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8
  *   receives u, y GeLU_tanh(u)), MTP_PROJ (x8 [T,h_l], w8 [h,h_l], y the
  *   partial [T,h], b NULL) or MTP_FC2 (x8 [T,f_l], w8 [h,f_l], b NULL).  y
  *   and preact in the shard dtype; the inner width must be a multiple of 16
- *   (else MTP_ERR_UNSUPPORTED).                                              */
+ *   (else MTP_ERR_UNSUPPORTED).  amax_parts: nullable, MTP_FC1 only (else
+ *   MTP_ERR_INVALID_ARG): 1024 fp32 (out) receiving partial maxima of |y| as
+ *   stored in the form mtp_fp8_amax writes, for mtp_fp8_quantize of y
+ *   without a separate amax pass.                                            */
 int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
                        const float* x_scale, const uint8_t* w8, const float* w_scale,
-                       const void* b, void* y, void* preact, void* stream);
+                       const void* b, void* y, void* preact, float* amax_parts, void* stream);
 
 /* FP8 training step: per-tensor scales shared by every shard of a tensor
  * (the ranks of a tensor-parallel group agree on the maximum of their
@@ -329,7 +332,9 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
  *     needs out % 16 == 0;
  *   dw [out, in] fp32 (nullable; += when accumulate) = (dy8_t [out, T] E5M2,
  *     the transposed codes of dy) (x8_t [in, T] E4M3, those of the forward
- *     input)^T * dy_scale * x_scale; needs T % 16 == 0.
+ *     input)^T * dy_scale * x_scale; needs T % 16 == 0;
+ *   dx_amax_parts: nullable, only with dx and preact (FC2's du; else
+ *     MTP_ERR_INVALID_ARG): partial maxima of |dx| as in mtp_linear_fwd_fp8.
  *   Scales are [1] fp32 device values as written by mtp_fp8_quantize.     */
 int mtp_fp8_amax(const mtp_shard_desc* desc, const void* x, int64_t n, float* amax_parts,
                  void* stream);
@@ -339,7 +344,8 @@ int mtp_fp8_quantize(const mtp_shard_desc* desc, int fmt, const void* x, int64_t
 int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
                        const uint8_t* dy8_t, const float* dy_scale, const uint8_t* w8_t,
                        const float* w_scale, const uint8_t* x8_t, const float* x_scale,
-                       const void* preact, void* dx, float* dw, int accumulate, void* stream);
+                       const void* preact, void* dx, float* dw, int accumulate,
+                       float* dx_amax_parts, void* stream);
 
 /* ------------------------------------------ context-parallel attention
  * The sequence split into chunks whose attention runs block pair by block

@@ -485,7 +485,8 @@ int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8
 }
 int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
                        const float* x_scale, const uint8_t* w8, const float* w_scale,
-                       const void* b, void* y, void* preact, void* stream) {
+                       const void* b, void* y, void* preact, float* amax_parts,
+                       void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
@@ -504,6 +505,7 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
     return MTP_ERR_INVALID_ARG;
   if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
   if ((kind == MTP_PROJ || kind == MTP_FC2) && b != nullptr) return MTP_ERR_INVALID_ARG;
+  if (!ok_opt(amax_parts) || (amax_parts && kind != MTP_FC1)) return MTP_ERR_INVALID_ARG;
   if (k % 16 != 0) return MTP_ERR_UNSUPPORTED;
   if (!fits(s.T, k, 1) || !fits(n, k, 1)) return MTP_ERR_UNSUPPORTED;
   GemmDesc g{};
@@ -513,8 +515,8 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
   g.C = y; g.ldc = n; g.bias = b;
   g.aux = preact; g.ld_aux = n;
   g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : mtp::kEpiStore;
- 
   g.fp8 = true; g.scale_a = x_scale; g.scale_b = w_scale;
+  g.amax = amax_parts;
   return hip_status(mtp::gemm_bf16(g, static_cast<hipStream_t>(stream)));
 }
 
@@ -553,7 +555,8 @@ int mtp_fp8_quantize(const mtp_shard_desc* desc, int fmt, const void* x, int64_t
 int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
                        const uint8_t* dy8_t, const float* dy_scale, const uint8_t* w8_t,
                        const float* w_scale, const uint8_t* x8_t, const float* x_scale,
-                       const void* preact, void* dx, float* dw, int accumulate, void* stream) {
+                       const void* preact, void* dx, float* dw, int accumulate,
+                       float* dx_amax_parts, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
@@ -568,6 +571,7 @@ int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
   }
   if (!ok_ptr(dy_scale) || !ok_opt(dx) || !ok_opt(dw) || !ok_opt(preact)) return MTP_ERR_INVALID_ARG;
   if (preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
+  if (!ok_opt(dx_amax_parts) || (dx_amax_parts && (!dx || !preact))) return MTP_ERR_INVALID_ARG;
   if (dx && (!ok_ptr(dy8) || !ok_ptr(w8_t) || !ok_ptr(w_scale))) return MTP_ERR_INVALID_ARG;
   if (dw && (!ok_ptr(dy8_t) || !ok_ptr(x8_t) || !ok_ptr(x_scale))) return MTP_ERR_INVALID_ARG;
   // 16-byte k chunks: the reduction lengths (out for the data gradient, T
@@ -584,6 +588,7 @@ int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
     g.aux = const_cast<void*>(preact); g.ld_aux = in;
     g.epi = preact ? mtp::kEpiDGelu : mtp::kEpiStore;
     g.fp8 = true; g.a_e5m2 = true; g.scale_a = dy_scale; g.scale_b = w_scale;
+    g.amax = dx_amax_parts;
     if (mtp::gemm_bf16(g, str) != hipSuccess) return MTP_ERR_HIP;
   }
   if (dw) {

@@ -66,6 +66,7 @@ struct GemmParams {
   void* aux; int64_t ld_aux;
   int tiles_m, tiles_n;
   uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31)
+  float* amax;  // FP8 GeLU / GeLU' instances: partial maxima of |C| (nullable)
 };
 
 // Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids
@@ -229,8 +230,11 @@ __device__ __forceinline__ bf16x8 frag_m(const char* t, int rb, int kk, int lane
   return cat_bf16x8(lo, hi);
 }
 
-template <int EPI, typename ElemT>
-__device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, float v[4]) {
+// AMAX: mx also takes the largest |value| stored to C (GeLU and GeLU'
+// epilogues).
+template <int EPI, typename ElemT, bool AMAX = false>
+__device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, float v[4],
+                                          float& mx) {
   if (EPI == kEpiStore || EPI == kEpiGelu || EPI == kEpiF32) {
     if (p.bias) {
       float b[4];
@@ -246,12 +250,20 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
     float g[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) g[c] = gelu_tanh(v[c]);
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(g[c]));
+    }
     store4(static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + n, g);
   } else if (EPI == kEpiDGelu) {
     float u[4];
     load4(static_cast<const ElemT*>(p.aux) + static_cast<int64_t>(m) * p.ld_aux + n, u);
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] *= gelu_tanh_grad(u[c]);
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(v[c]));
+    }
     store4(static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + n, v);
   } else if (EPI == kEpiDSwiGLU) {
     // v = dg at columns n..n+3 (n % 4 == 0): gate and up of these columns
@@ -303,9 +315,9 @@ __device__ __forceinline__ void epi_swiglu(const GemmParams& p, int m, int n, co
 // region `stage` (36-float pitch), then reads it back as row segments, so
 // every global store (and every load of C or of the GeLU pre-activation)
 // covers 8 rows x 32 contiguous columns.
-template <int EPI>
+template <int EPI, bool AMAX = false>
 __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, const f32x16& a,
-                                          int mb, int nb, int lane) {
+                                          int mb, int nb, int lane, float& mx) {
   constexpr int kPitch = 36;
   const int lrow = lane & 31, lk = lane >> 5;
   const int sr = lane >> 3, sc = (lane & 7) * 4;
@@ -340,7 +352,7 @@ __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, con
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + 8 * r + sr;
-      if (m < p.M && n < p.N) epi_apply<EPI, bf16_t>(p, m, n, v[r]);
+      if (m < p.M && n < p.N) epi_apply<EPI, bf16_t, AMAX>(p, m, n, v[r], mx);
     }
   }
 }
@@ -599,16 +611,42 @@ gemm_bf16_kernel(GemmParams p) {
                    : (wave / kPerBuf) == 1 ? lds_a1
                    : (wave / kPerBuf) == 2 ? lds_b0 : lds_b1;
   float* stage = reinterpret_cast<float*>(base + (wave % kPerBuf) * kRegion);
+  // FP8 GeLU / GeLU' outputs feed the next quantization: the partial
+  // maximum of what this workgroup stores, in the form of the amax pass
+  // (slot blockIdx.x, unused slots 0; rounded to bf16 like the values,
+  // which keeps the order)
+  constexpr bool kAmax = F8 && (EPI == kEpiGelu || EPI == kEpiDGelu);
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       if constexpr (F8) {
         const f32x16 v = acc[i][j] * (p.scale_a[0] * p.scale_b[0]);
-        epi_block<EPI>(p, stage, v, m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
+        epi_block<EPI, kAmax>(p, stage, v, m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane,
+                              mx);
       } else {
-        epi_block<EPI>(p, stage, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane);
+        epi_block<EPI>(p, stage, acc[i][j], m0 + wm * WTM + i * 32, n0 + wn * WTN + j * 32, lane,
+                       mx);
       }
+  if constexpr (kAmax) {
+    if (p.amax) {
+      mx = warp_max(mx);
+      __syncthreads();  // every wave is done with its staging region
+      float* wmx = reinterpret_cast<float*>(lds_a0);
+      if (lane == 0) wmx[wave] = mx;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float m = wmx[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, wmx[w]);
+        p.amax[blockIdx.x] = lo_bf(pack_bf2(m, 0.0f));
+      }
+      if (blockIdx.x == 0)
+        for (int i = static_cast<int>(gridDim.x) + threadIdx.x; i < kAmaxParts; i += NW * 64)
+          p.amax[i] = 0.0f;
+    }
+  }
 }
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool F8 = false,
@@ -772,7 +810,8 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmParams p, const float
       for (int c = 0; c < 4; ++c) pv[c] = __shfl_xor(acc[i][c], 1);
       if (m < p.M && n < p.N) epi_swiglu<float>(p, m, n, acc[i], pv);
     } else {
-      if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i]);
+      float unused = 0.0f;
+      if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i], unused);
     }
   }
 }
@@ -833,15 +872,32 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     p.a_bytes = static_cast<uint32_t>(ab);
     p.b_bytes = static_cast<uint32_t>(bb);
     const int tile = pick_tile_fp8(g.M, g.N);
-    if (!g.a_e5m2)
-      return g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu, false>(p, tile, s)
-                               : dispatch_fp8<kEpiStore, false>(p, tile, s);
-    switch (g.epi) {
-      case kEpiStore: return dispatch_fp8<kEpiStore, true>(p, tile, s);
-      case kEpiDGelu: return dispatch_fp8<kEpiDGelu, true>(p, tile, s);
-      case kEpiF32: return dispatch_fp8<kEpiF32, true>(p, tile, s);
-      default: return dispatch_fp8<kEpiF32Acc, true>(p, tile, s);
+    // the epilogue writes the amax parts of C when its grid fits them,
+    // otherwise a pass over C does
+    bool amax_pass = false;
+    if (g.amax) {
+      if ((g.epi != kEpiGelu && g.epi != kEpiDGelu) || g.ldc != g.N) return hipErrorInvalidValue;
+      const int bm = tile == kTile256x128 || tile == kTileF8_256x192 ? 256 : 128;
+      const int bn = tile == kTile256x128 || tile == kTile128x128 ? 128
+                     : tile == kTileF8_256x192 ? 192 : 256;
+      const int64_t tiles = static_cast<int64_t>((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+      if (tiles <= kAmaxParts) p.amax = g.amax;
+      else amax_pass = true;
     }
+    hipError_t e;
+    if (!g.a_e5m2) {
+      e = g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu, false>(p, tile, s)
+                            : dispatch_fp8<kEpiStore, false>(p, tile, s);
+    } else {
+      switch (g.epi) {
+        case kEpiStore: e = dispatch_fp8<kEpiStore, true>(p, tile, s); break;
+        case kEpiDGelu: e = dispatch_fp8<kEpiDGelu, true>(p, tile, s); break;
+        case kEpiF32: e = dispatch_fp8<kEpiF32, true>(p, tile, s); break;
+        default: e = dispatch_fp8<kEpiF32Acc, true>(p, tile, s); break;
+      }
+    }
+    if (e != hipSuccess || !amax_pass) return e;
+    return fp8_amax(g.C, static_cast<int64_t>(g.M) * g.N, g.amax, s);
   }
   GemmParams p = to_params(g);
   // Buffer offsets are 32-bit and the edge handling needs every valid byte

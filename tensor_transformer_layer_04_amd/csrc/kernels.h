@@ -39,6 +39,9 @@ struct GemmDesc {
   bool a_e5m2 = false;
   const float* scale_a = nullptr;
   const float* scale_b = nullptr;
+  // FP8 GeLU / GeLU' epilogues (C contiguous, ldc == N): kAmaxParts partial
+  // maxima of |C| as stored, in fp8_amax's form (nullable).
+  float* amax = nullptr;
 };
 
 hipError_t gemm_bf16(const GemmDesc& g, hipStream_t stream);

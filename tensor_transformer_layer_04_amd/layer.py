@@ -304,11 +304,14 @@ class TPLayer(_Probed):
         mtp.mtp_fp8_quantize(self.d0, fmt, x, sl["rows"], sl["cols"], [sl["amax"]], sl["q"],
                              sl["qt"], sl["s"])
 
-    def _quant_split(self, name, xs, fmt, ext):
+    def _quant_split(self, name, xs, fmt, ext, amax_written=False):
         """amax of every computed rank's shard xs[r], then its codes with the
-        scale of the whole tensor (this layer's ranks and ``ext``'s)."""
-        for r in self.ranks:
-            mtp.mtp_fp8_amax(self.descs[r], xs[r], xs[r].numel(), self.r8[r][name]["amax"])
+        scale of the whole tensor (this layer's ranks and ``ext``'s;
+        amax_written: the kernels that produced the shards wrote their amax
+        parts)."""
+        if not amax_written:
+            for r in self.ranks:
+                mtp.mtp_fp8_amax(self.descs[r], xs[r], xs[r].numel(), self.r8[r][name]["amax"])
         parts = [self.r8[r][name]["amax"] for r in self.ranks] + list(ext.get("fp8_" + name, []))
         for r in self.ranks:
             sl = self.r8[r][name]
@@ -555,9 +558,11 @@ class TPLayer(_Probed):
             w, a, c = self.w[r], self.a[r], r8[r]
             with T("fc1_fwd"):
                 mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_FC1, q8["ln2"]["q"], q8["ln2"]["s"],
-                                       c["w1"]["q"], c["w1"]["s"], w["b1"], a["g"], a["u"])
+                                       c["w1"]["q"], c["w1"]["s"], w["b1"], a["g"], a["u"],
+                                       amax_parts=c["g"]["amax"])
         with T("quant"):
-            self._quant_split("g", {r: self.a[r]["g"] for r in self.ranks}, E4, ext)
+            self._quant_split("g", {r: self.a[r]["g"] for r in self.ranks}, E4, ext,
+                              amax_written=True)
         wait_w("w2")
         for r in self.ranks:
             c = r8[r]
@@ -594,7 +599,7 @@ class TPLayer(_Probed):
             with T("fc2_dgrad"):
                 mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, q8["dy"]["q"], None, q8["dy"]["s"],
                                        c["w2"]["qt"], c["w2"]["s"], None, None, a["u"], a["du"],
-                                       None)
+                                       None, dx_amax_parts=c["du"]["amax"])
             with on_side(), T("fc2_wgrad", side):
                 mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, None, q8["dy"]["qt"], q8["dy"]["s"], None,
                                        None, c["g"]["qt"], c["g"]["s"], None, None, g["dw2"])
@@ -604,7 +609,8 @@ class TPLayer(_Probed):
                                            self.rgrads["db2"], 0, wss, wsb)
         # FC1: dln2_r = du_r W1_r; dW1 = du^T ln2
         with T("quant"):
-            self._quant_split("du", {r: self.a[r]["du"] for r in self.ranks}, E5, ext)
+            self._quant_split("du", {r: self.a[r]["du"] for r in self.ranks}, E5, ext,
+                              amax_written=True)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]

@@ -59,11 +59,12 @@ _SIGS = {
     "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "mtp_attn_bwd_noalloc": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP]),
     "mtp_quantize_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
-    "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 7 + [_VP]),
+    "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 8 + [_VP]),
     "mtp_fp8_amax": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP]),
     "mtp_fp8_quantize": (ctypes.c_int, [_VP, ctypes.c_int, _VP, ctypes.c_int64, ctypes.c_int64,
                                         _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
-    "mtp_linear_bwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 10 + [ctypes.c_int, _VP]),
+    "mtp_linear_bwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 10
+                           + [ctypes.c_int, _VP, _VP]),
     "mtp_attn_fwd_block": (ctypes.c_int, [_VP, _VP] + [ctypes.c_int64] * 4
                            + [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "mtp_attn_merge": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int64] * 2 + [_VP]),
@@ -204,9 +205,11 @@ def mtp_quantize_fp8(desc, x, n, q, scale, stream=None):
                  _stream(stream))
 
 
-def mtp_linear_fwd_fp8(desc, kind, x8, x_scale, w8, w_scale, b, y, preact, stream=None):
+def mtp_linear_fwd_fp8(desc, kind, x8, x_scale, w8, w_scale, b, y, preact, amax_parts=None,
+                       stream=None):
     return _call("mtp_linear_fwd_fp8", ctypes.byref(desc), kind, _addr(x8), _addr(x_scale),
-                 _addr(w8), _addr(w_scale), _addr(b), _addr(y), _addr(preact), _stream(stream))
+                 _addr(w8), _addr(w_scale), _addr(b), _addr(y), _addr(preact),
+                 _addr(amax_parts), _stream(stream))
 
 
 def mtp_fp8_amax(desc, x, n, amax_parts, stream=None):
@@ -222,10 +225,11 @@ def mtp_fp8_quantize(desc, fmt, x, rows, cols, amax_parts, q, q_t, scale, stream
 
 
 def mtp_linear_bwd_fp8(desc, kind, dy8, dy8_t, dy_scale, w8_t, w_scale, x8_t, x_scale, preact,
-                       dx, dw, accumulate=0, stream=None):
+                       dx, dw, accumulate=0, dx_amax_parts=None, stream=None):
     return _call("mtp_linear_bwd_fp8", ctypes.byref(desc), kind, _addr(dy8), _addr(dy8_t),
                  _addr(dy_scale), _addr(w8_t), _addr(w_scale), _addr(x8_t), _addr(x_scale),
-                 _addr(preact), _addr(dx), _addr(dw), int(accumulate), _stream(stream))
+                 _addr(preact), _addr(dx), _addr(dw), int(accumulate), _addr(dx_amax_parts),
+                 _stream(stream))
 
 
 def mtp_attn_fwd_block(desc, qkv, q_lo, q_hi, k_lo, k_hi, ctx, lse, cu_seqlens=None, n_seqs=0,

@@ -229,9 +229,9 @@ def test_fp8_entry_points_refuse_bad_arguments():
     assert lib.mtp_fp8_quantize(ctypes.byref(f32), mtp.MTP_FP8_E4M3, FAKE, 8, 64, parts, 1, FAKE,
                                 FAKE, FAKE, None) == U
     assert lib.mtp_linear_fwd_fp8(ctypes.byref(f32), mtp.MTP_QKV, FAKE, FAKE, FAKE, FAKE, None,
-                                  FAKE, None, None) == U
+                                  FAKE, None, None, None) == U
     assert lib.mtp_linear_bwd_fp8(ctypes.byref(f32), mtp.MTP_QKV, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                  FAKE, FAKE, None, FAKE, FAKE, 0, None) == U
+                                  FAKE, FAKE, None, FAKE, FAKE, 0, None, None) == U
     # amax: whole 16-byte vectors only
     assert lib.mtp_fp8_amax(bd, FAKE, 12, FAKE, None) == I
     assert lib.mtp_fp8_amax(bd, FAKE, -8, FAKE, None) == I
@@ -250,20 +250,26 @@ def test_fp8_entry_points_refuse_bad_arguments():
     assert q() == I
     parts[0] = FAKE
     # forward linear maps
-    fwd = lambda kind, b=None, pre=None, dd=bd: lib.mtp_linear_fwd_fp8(
-        dd, kind, FAKE, FAKE, FAKE, FAKE, b, FAKE, pre, None)
+    fwd = lambda kind, b=None, pre=None, dd=bd, am=None: lib.mtp_linear_fwd_fp8(
+        dd, kind, FAKE, FAKE, FAKE, FAKE, b, FAKE, pre, am, None)
     assert fwd(7) == I
     assert fwd(mtp.MTP_PROJ, b=FAKE) == I          # the row-parallel bias comes after the sum
     assert fwd(mtp.MTP_FC1) == I                    # FC1 writes its pre-activation
     assert fwd(mtp.MTP_QKV, pre=FAKE) == I
+    assert fwd(mtp.MTP_QKV, am=FAKE) == I           # amax parts: FC1's GeLU output only
+    assert fwd(mtp.MTP_FC1, pre=FAKE, am=FAKE + 4) == I
     odd = valid(ffn=2000)                            # f_l = 1000: 8 but not 16 bytes of codes
     assert fwd(mtp.MTP_FC2, dd=ctypes.byref(odd)) == U
     # backward: data gradient (dy8, W^T codes) and/or weight gradient (dy^T, x^T codes)
-    bwd = lambda kind, dy8=FAKE, dyt=FAKE, w8t=FAKE, x8t=FAKE, pre=None, dx=FAKE, dw=FAKE, dd=bd: \
-        lib.mtp_linear_bwd_fp8(dd, kind, dy8, dyt, FAKE, w8t, FAKE, x8t, FAKE, pre, dx, dw, 0, None)
+    bwd = lambda kind, dy8=FAKE, dyt=FAKE, w8t=FAKE, x8t=FAKE, pre=None, dx=FAKE, dw=FAKE, dd=bd, \
+        am=None: lib.mtp_linear_bwd_fp8(dd, kind, dy8, dyt, FAKE, w8t, FAKE, x8t, FAKE, pre, dx, dw,
+                                        0, am, None)
     assert bwd(7) == I
     assert bwd(mtp.MTP_PROJ, pre=FAKE) == I         # GeLU' belongs to FC2
     assert bwd(mtp.MTP_FC2, dy8=None) == I
+    assert bwd(mtp.MTP_FC2, am=FAKE) == I           # amax parts: only of du (with preact)
+    assert bwd(mtp.MTP_FC2, pre=FAKE, dx=None, am=FAKE) == I
+    assert bwd(mtp.MTP_FC2, pre=FAKE, am=FAKE + 4) == I
     assert bwd(mtp.MTP_FC2, w8t=None) == I
     assert bwd(mtp.MTP_FC2, dyt=None) == I
     assert bwd(mtp.MTP_FC2, x8t=None) == I

@@ -303,3 +303,54 @@ def test_fp8_backward_gemms_7b_shard(T):
         check(f"{name}.dw", dw.cpu(), ref_dw, 1e-4, report)
         check(f"{name}.dw_acc", dw2.cpu(), ref_dw + 1.0, 1e-4, report)
     log(f"fp8 backward GEMMs T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
+
+
+@pytest.mark.parametrize("T", [2048, 304, 16384])
+def test_amax_parts_from_fp8_gemm_epilogues(T):
+    """The FC1 forward (GeLU output g) and the FC2 data gradient (du, with
+    the GeLU derivative) write the amax parts of their bf16 output when
+    asked: the outputs are those of the calls without parts, the largest
+    part is the largest |value| stored, every slot is written, and the codes
+    made from the parts equal those of a separate amax pass bit for bit.
+    T = 16384 gives the FC1 GEMM more tiles than parts (the pass over the
+    output then writes them)."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    h, a, f, tp = 4096, 32, 11008, 2
+    fl = f // tp
+    d = mtp.make_desc(h, a, f, tp, 0, T, 1, mtp.MTP_BF16)
+    x, w1, b1 = _bf16((T, h), 150), _bf16((fl, h), 151, 0.02), _bf16((fl,), 152, 0.1)
+    dy, w2, u = _bf16((T, h), 153, 1e-3), _bf16((h, fl), 154, 0.02), _bf16((T, fl), 155)
+    (xq, _, xs), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [x.cuda()])
+    (w1q, _, w1s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w1.cuda()])
+    (dq, _, ds), = _amax_and_quant(d, mtp.MTP_FP8_E5M2, [dy.cuda()])
+    (_, w2qt, w2s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w2.cuda()])
+    b1, u = b1.cuda(), u.cuda()
+    P = lambda: torch.full((mtp.FP8_AMAX_PARTS,), 1e30, dtype=torch.float32, device="cuda")
+    E = lambda: torch.empty(T, fl, dtype=torch.bfloat16, device="cuda")
+    g0, g1, u0, u1, p_g = E(), E(), E(), E(), P()
+    mtp.mtp_linear_fwd_fp8(d, mtp.MTP_FC1, xq, xs, w1q, w1s, b1, g0, u0)
+    mtp.mtp_linear_fwd_fp8(d, mtp.MTP_FC1, xq, xs, w1q, w1s, b1, g1, u1, amax_parts=p_g)
+    du0, du1, p_du = E(), E(), P()
+    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, dq, None, ds, w2qt, w2s, None, None, u, du0, None)
+    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, dq, None, ds, w2qt, w2s, None, None, u, du1, None,
+                           dx_amax_parts=p_du)
+    torch.cuda.synchronize()
+    assert torch.equal(g0, g1) and torch.equal(u0, u1) and torch.equal(du0, du1)
+    for name, y, p, fmt in (("g", g1, p_g, mtp.MTP_FP8_E4M3), ("du", du1, p_du, mtp.MTP_FP8_E5M2)):
+        ref = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_amax(d, y, y.numel(), ref)
+        torch.cuda.synchronize()
+        want = float(y.float().abs().max())
+        log(f"fp8 GEMM amax parts {name} T={T}: fused {float(p.max())!r} separate "
+            f"{float(ref.max())!r} max|y| {want!r}")
+        assert float(p.max()) == want == float(ref.max()) and float(p.min()) >= 0.0
+        codes = []
+        for pp in (p, ref):
+            q = torch.empty(T, fl, dtype=torch.uint8, device="cuda")
+            qt = torch.empty(fl, T, dtype=torch.uint8, device="cuda")
+            s = torch.empty(1, dtype=torch.float32, device="cuda")
+            mtp.mtp_fp8_quantize(d, fmt, y, T, fl, [pp], q, qt, s)
+            codes.append((q, qt, s))
+        torch.cuda.synchronize()
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(*codes))
