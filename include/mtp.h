@@ -239,20 +239,25 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy,
  * documents (block-diagonal causal mask); the library trusts its contents
  * (it cannot read device memory before launch).
  *   qkv [T,3h_l] dtype (layout above); ctx [T,h_l] dtype (out);
- *   lse [a_l,T] fp32 (out): natural-log log-sum-exp of each score row.
+ *   lse [a_l,T] fp32 (out): natural-log log-sum-exp of each score row;
+ *   ctx_amax_parts: nullable, bf16 only (else MTP_ERR_UNSUPPORTED): 1024
+ *   fp32 (out) receiving partial maxima of |ctx| as stored in the form
+ *   mtp_fp8_amax writes, for mtp_fp8_quantize of ctx without an amax pass.
  */
 int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* lse,
-                 const int32_t* cu_seqlens, int32_t n_seqs, void* stream);
+                 const int32_t* cu_seqlens, int32_t n_seqs, float* ctx_amax_parts,
+                 void* stream);
 
 /* Attention backward: given qkv, ctx and lse from mtp_attn_fwd and dctx
  * [T,h_l], writes dqkv [T,3h_l] dtype = [dq | dk | dv] in the qkv layout.
  * Needs ws_bytes >= mtp_workspace_size(desc, MTP_OP_ATTN_BWD, 0) (= two fp32
  * values per local head and token: D = rowsum(dctx * ctx) and the
- * log-sum-exp in base 2).                                                    */
+ * log-sum-exp in base 2).  dqkv_amax_parts: nullable, bf16 only, as
+ * ctx_amax_parts of mtp_attn_fwd, of dqkv.                                  */
 int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                  const float* lse, const void* dctx, void* dqkv,
                  const int32_t* cu_seqlens, int32_t n_seqs, void* ws, size_t ws_bytes,
-                 void* stream);
+                 float* dqkv_amax_parts, void* stream);
 
 /* The same attention backward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
@@ -266,7 +271,8 @@ int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
  * contents (nothing in it needs clearing: the call writes every row it
  * reads), so calls that overlap in time on one GPU, on different streams or
  * from different host threads, race; serialise them.  Results are
- * bit-identical to mtp_attn_bwd's.                                           */
+ * bit-identical to mtp_attn_bwd's (which alone offers the optional amax
+ * parts of dqkv).                                                            */
 int mtp_attn_bwd_noalloc(const mtp_shard_desc* desc, const void* qkv, const void* ctx,
                          const float* lse, const void* dctx, void* dqkv,
                          const int32_t* cu_seqlens, int32_t n_seqs, void* stream);

@@ -323,15 +323,18 @@ int mtp_row_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
 }
 
 int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* lse,
-                 const int32_t* cu_seqlens, int32_t n_seqs, void* stream) {
+                 const int32_t* cu_seqlens, int32_t n_seqs, float* ctx_amax_parts,
+                 void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
-  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse)) return MTP_ERR_INVALID_ARG;
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_opt(ctx_amax_parts))
+    return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (ctx_amax_parts && !s.bf16) return MTP_ERR_UNSUPPORTED;
   if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   mtp::AttnDesc a{};
-  a.qkv = qkv; a.ctx = ctx; a.lse = lse;
+  a.qkv = qkv; a.ctx = ctx; a.lse = lse; a.amax = ctx_amax_parts;
   a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
   return hip_status(mtp::attn_fwd(s.bf16, a, static_cast<hipStream_t>(stream)));
@@ -339,19 +342,21 @@ int mtp_attn_fwd(const mtp_shard_desc* desc, const void* qkv, void* ctx, float* 
 
 int mtp_attn_bwd(const mtp_shard_desc* desc, const void* qkv, const void* ctx, const float* lse,
                  const void* dctx, void* dqkv, const int32_t* cu_seqlens, int32_t n_seqs,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 void* ws, size_t ws_bytes, float* dqkv_amax_parts, void* stream) {
   Shard s;
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
-  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv))
+  if (!ok_ptr(qkv) || !ok_ptr(ctx) || !ok_ptr(lse) || !ok_ptr(dctx) || !ok_ptr(dqkv) ||
+      !ok_opt(dqkv_amax_parts))
     return MTP_ERR_INVALID_ARG;
   if (cu_seqlens && n_seqs < 1) return MTP_ERR_INVALID_ARG;
+  if (dqkv_amax_parts && !s.bf16) return MTP_ERR_UNSUPPORTED;
   if (!attn_fits(s)) return MTP_ERR_UNSUPPORTED;
   const size_t need = static_cast<size_t>(s.al) * s.T * sizeof(float) * 2;
   if (need > 0 && (ws == nullptr || !aligned(ws) || ws_bytes < need)) return MTP_ERR_WORKSPACE;
   mtp::AttnDesc a{};
   a.qkv = qkv; a.ctx = const_cast<void*>(ctx); a.lse = const_cast<float*>(lse);
-  a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws);
+  a.dctx = dctx; a.dqkv = dqkv; a.delta = static_cast<float*>(ws); a.amax = dqkv_amax_parts;
   a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs;
   a.T = s.T; a.seq_len = desc->seq_len; a.heads = s.al; a.head_dim = s.d;
   return hip_status(mtp::attn_bwd(s.bf16, a, static_cast<hipStream_t>(stream)));

@@ -27,6 +27,7 @@ struct AttnParams {
   const void* dctx;                 // [T, hl]
   void* dqkv;                       // [T, 3*hl]
   float* delta;                     // [heads, T]
+  float* amax;                      // amax parts of dqkv, zeroed here (nullable)
   const int32_t* cu; int n_seqs;
   int T; int seq_len; int heads; int hl;
   float scale;                      // 1/sqrt(D)
@@ -65,6 +66,10 @@ __global__ void __launch_bounds__(256) attn_delta_kernel(AttnParams p, int D, in
   const int pairs_per_block = 256 / per_row;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * pairs_per_block + threadIdx.x / per_row;
   const int c = threadIdx.x % per_row;
+  // the backward kernel that follows raises these slots to the partial
+  // maxima of |dqkv|
+  if (p.amax && blockIdx.x == 0)
+    for (int k = threadIdx.x; k < kAmaxParts; k += 256) p.amax[k] = 0.0f;
   float acc = 0.0f;
   int64_t i = 0;
   int n = 0;
@@ -257,6 +262,7 @@ AttnParams make_params(const AttnDesc& a) {
   AttnParams p{};
   p.qkv = a.qkv; p.ld = 3LL * a.heads * a.head_dim;
   p.ctx = a.ctx; p.lse = a.lse; p.dctx = a.dctx; p.dqkv = a.dqkv; p.delta = a.delta;
+  p.amax = a.amax;
   p.cu = a.cu_seqlens; p.n_seqs = a.n_seqs;
   p.T = static_cast<int>(a.T); p.seq_len = a.seq_len; p.heads = a.heads;
   p.hl = a.heads * a.head_dim;
@@ -268,7 +274,8 @@ AttnParams make_params(const AttnDesc& a) {
 }  // namespace
 
 hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t s) {
-  if (a.T == 0 || a.heads == 0) return hipSuccess;
+  if (a.amax && !bf16) return hipErrorInvalidValue;
+  if (a.T == 0 || a.heads == 0) return a.amax ? fp8_amax(a.ctx, 0, a.amax, s) : hipSuccess;
   const AttnParams p = make_params(a);
   if (bf16) {
     return attn_fwd_bf16_mfma(a, s);
@@ -293,13 +300,14 @@ hipError_t attn_merge(const AttnDesc& a, const void* ctx_part, const float* lse_
 }
 
 hipError_t attn_bwd(bool bf16, const AttnDesc& a, hipStream_t s) {
-  if (a.T == 0 || a.heads == 0) return hipSuccess;
+  if (a.amax && (!bf16 || a.accumulate)) return hipErrorInvalidValue;
+  if (a.T == 0 || a.heads == 0) return a.amax ? fp8_amax(a.dqkv, 0, a.amax, s) : hipSuccess;
   const AttnParams p = make_params(a);
   const int per_row = a.head_dim / 8;
   // D and lse*log2(e) are read only at the query rows of the range
   const int row_lo = static_cast<int>(a.q_lo);
   const int rows = static_cast<int>((a.q_hi < 0 ? a.T : a.q_hi) - a.q_lo);
-  if (rows <= 0) return hipSuccess;
+  if (rows <= 0) return a.amax ? fp8_amax(a.dqkv, 0, a.amax, s) : hipSuccess;
   const int64_t pairs = static_cast<int64_t>(rows) * a.heads;
   const int pairs_per_block = 256 / per_row;
   const dim3 dgrid(static_cast<unsigned>((pairs + pairs_per_block - 1) / pairs_per_block));

@@ -50,6 +50,7 @@ struct BwdParams {
   int accumulate;              // add into dqkv instead of storing
   float scale, scale_log2;
   uint32_t qkv_bytes, dctx_bytes, stat_bytes;
+  float* amax;  // partial maxima of |dqkv|, zeroed by the preprocess (nullable)
 };
 
 __device__ __forceinline__ int seq_index(const BwdParams& p, int i) {
@@ -179,7 +180,7 @@ __device__ __forceinline__ void ranked_blocks(const BwdParams& p, int r, int& kb
 template <int D, bool want_dk>
 __device__ __forceinline__ void dkv_block(const BwdParams& p, int kblk, int head,
                                           char* sq0, char* sq1, char* so0, char* so1, char* st0,
-                                          char* st1) {
+                                          char* st1, float& mx) {
   constexpr int KS = D / 16, DB = D / 32;
   const int T = p.T;
   const int k0 = p.k_lo + kblk * kBT;
@@ -364,6 +365,8 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, int kblk, int head
 #pragma unroll
           for (int c = 0; c < 4; ++c) w[c] += o[c];
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(w[c]));
         store4(out + 32 * d + 8 * a + 4 * g, w);
       }
   }
@@ -372,7 +375,7 @@ __device__ __forceinline__ void dkv_block(const BwdParams& p, int kblk, int head
 // ---------------------------------------------------------------------- dQ
 template <int D>
 __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head, char* sk0,
-                                         char* sk1, char* sv0, char* sv1) {
+                                         char* sk1, char* sv0, char* sv1, float& mx) {
   constexpr int KS = D / 16, DB = D / 32;
   const int T = p.T;
   const int q0 = p.q_lo + qblk * kBT;
@@ -513,6 +516,8 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, int qblk, int head,
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] += o[c];
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(v[c]));
         store4(out + 32 * d + 8 * a + 4 * g, v);
       }
   }
@@ -540,12 +545,29 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_mfma(BwdParams p) {
   const int role = j / p.heads, head = j % p.heads;
   int kblk, qblk;
   ranked_blocks(p, r, kblk, qblk);
+  float mx = 0.0f;  // largest |dqkv| this lane stores
   if (role == 1)
-    dq_block<D>(p, qblk, head, t0, t1, t2, t3);
+    dq_block<D>(p, qblk, head, t0, t1, t2, t3, mx);
   else if (role == 0)
-    dkv_block<D, true>(p, kblk, head, t0, t1, t2, t3, st0, st1);
+    dkv_block<D, true>(p, kblk, head, t0, t1, t2, t3, st0, st1, mx);
   else
-    dkv_block<D, false>(p, kblk, head, t0, t1, t2, t3, st0, st1);
+    dkv_block<D, false>(p, kblk, head, t0, t1, t2, t3, st0, st1, mx);
+  // The partial maximum of what this workgroup stored (rounded to bf16 like
+  // the values) raises slot blockIdx.x mod kAmaxParts, which the preprocess
+  // zeroed: the grid has more workgroups than slots, and the maximum does
+  // not depend on the order of the atomic updates.
+  if (p.amax) {
+    mx = warp_max(mx);
+    __syncthreads();
+    float* wm = reinterpret_cast<float*>(st0);
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float m = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+      atomicMax(reinterpret_cast<unsigned int*>(p.amax + blockIdx.x % kAmaxParts),
+                __float_as_uint(lo_bf(pack_bf2(m, 0.0f))));
+    }
+  }
 }
 
 }  // namespace
@@ -569,6 +591,7 @@ hipError_t attn_bwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.k_lo = static_cast<int>(a.k_lo);
   p.k_hi = static_cast<int>(a.k_hi < 0 ? a.T : a.k_hi);
   p.accumulate = a.accumulate ? 1 : 0;
+  p.amax = a.amax;
   // one rank (and so one dK/dV and one dQ block) per 64 rows; the two
   // ranges have equal lengths (whole sequence, or equal chunks)
   p.nblk = (p.q_hi - p.q_lo + kBT - 1) / kBT;

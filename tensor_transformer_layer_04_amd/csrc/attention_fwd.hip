@@ -57,6 +57,7 @@ struct FwdParams {
   int q_lo, q_hi, k_lo, k_hi;  // query and key row ranges (absolute)
   float scale_log2;
   uint32_t qkv_bytes;
+  float* amax;  // partial maxima of |ctx|, one per workgroup (nullable)
 };
 
 __device__ __forceinline__ int seq_start(const FwdParams& p, int i) {
@@ -321,6 +322,7 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
     park_ml[kh * 128 + 64 + lane] = l;
   }
   __syncthreads();
+  float mx = 0.0f;  // largest |ctx| this lane stores
   if (kh == 0) {
     float mk[kKH], lk[kKH];
     mk[0] = m;
@@ -357,6 +359,7 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
 #pragma unroll
             for (int k = 1; k < kKH; ++k) acc += slot_o(k)[idx] * ak[k];
             v[c] = acc * inv;
+            mx = fmaxf(mx, fabsf(v[c]));
           }
           store4(out + 32 * d + 8 * a + 4 * g, v);
         }
@@ -364,6 +367,24 @@ __global__ void __launch_bounds__(64 * kFW, (8 + kFW - 1) / kFW) attn_fwd_mfma(F
         p.lse[static_cast<int64_t>(head) * T + qi] =
             lt > 0.0f ? (mf + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
+  }
+  // The partial maximum of this workgroup's ctx for an FP8 scale (slot
+  // blockIdx.x, rounded to bf16 like the values; workgroup 0 zeroes the
+  // slots no workgroup owns).
+  if (p.amax) {
+    mx = warp_max(mx);
+    __syncthreads();
+    if (lane == 0) park_mls[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mw = park_mls[0];
+#pragma unroll
+      for (int w = 1; w < kFW; ++w) mw = fmaxf(mw, park_mls[w]);
+      p.amax[blockIdx.x] = lo_bf(pack_bf2(mw, 0.0f));
+    }
+    if (blockIdx.x == 0)
+      for (int i = static_cast<int>(gridDim.x) + threadIdx.x; i < kAmaxParts; i += 64 * kFW)
+        p.amax[i] = 0.0f;
   }
 }
 
@@ -386,15 +407,18 @@ hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t s) {
   p.k_lo = static_cast<int>(a.k_lo);
   p.k_hi = static_cast<int>(a.k_hi < 0 ? a.T : a.k_hi);
   p.nqb = (p.q_hi - p.q_lo + kFQ - 1) / kFQ;
-  if (p.nqb <= 0) return hipSuccess;
+  if (p.nqb <= 0) return a.amax ? fp8_amax(a.ctx, 0, a.amax, s) : hipSuccess;
   p.scale_log2 = kLog2e / sqrtf(static_cast<float>(a.head_dim));
   const int64_t bytes = a.T * p.ld * 2;
   if (bytes >= static_cast<int64_t>(kOOB)) return hipErrorInvalidValue;
   p.qkv_bytes = static_cast<uint32_t>(bytes);
   const dim3 grid(static_cast<unsigned>(p.nqb * a.heads));
+  // the kernel writes the amax parts of ctx when its grid fits them
+  p.amax = grid.x <= static_cast<unsigned>(kAmaxParts) ? a.amax : nullptr;
   if (a.head_dim == 128) hipLaunchKernelGGL(attn_fwd_mfma<128>, grid, dim3(64 * kFW), 0, s, p);
   else if (a.head_dim == 64) hipLaunchKernelGGL(attn_fwd_mfma<64>, grid, dim3(64 * kFW), 0, s, p);
   else return hipErrorInvalidValue;
+  if (a.amax && !p.amax) return fp8_amax(a.ctx, a.T * p.hl, a.amax, s);
   return hipGetLastError();
 }
 

@@ -107,6 +107,9 @@ struct AttnDesc {
   // both.  With accumulate, the backward adds into dqkv instead of storing.
   int64_t q_lo = 0, q_hi = -1, k_lo = 0, k_hi = -1;
   bool accumulate = false;
+  // bf16 whole-range calls: kAmaxParts partial maxima of |ctx| (forward) or
+  // |dqkv| (backward) as stored, in fp8_amax's form (nullable).
+  float* amax = nullptr;
 };
 hipError_t attn_fwd(bool bf16, const AttnDesc& a, hipStream_t stream);
 hipError_t attn_fwd_bf16_mfma(const AttnDesc& a, hipStream_t stream);

@@ -537,9 +537,11 @@ class TPLayer(_Probed):
         for r in self.ranks:
             a = self.a[r]
             with T("attn_fwd"):
-                mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs)
+                mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs,
+                                 ctx_amax_parts=r8[r]["ctx"]["amax"])
         with T("quant"):
-            self._quant_split("ctx", {r: self.a[r]["ctx"] for r in self.ranks}, E4, ext)
+            self._quant_split("ctx", {r: self.a[r]["ctx"] for r in self.ranks}, E4, ext,
+                              amax_written=True)
         wait_w("wo")
         for r in self.ranks:
             c = r8[r]
@@ -647,10 +649,11 @@ class TPLayer(_Probed):
                                            None, None, self.rgrads["dbo"], 0, wss, wsb)
             with T("attn_bwd"):
                 mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
-                                 self.n_seqs, ws, wsb)
+                                 self.n_seqs, ws, wsb, dqkv_amax_parts=c["dqkv"]["amax"])
         # QKV: dln1_r = dqkv_r Wqkv_r; dWqkv_r = dqkv_r^T ln1
         with T("quant"):
-            self._quant_split("dqkv", {r: self.a[r]["dqkv"] for r in self.ranks}, E5, ext)
+            self._quant_split("dqkv", {r: self.a[r]["dqkv"] for r in self.ranks}, E5, ext,
+                              amax_written=True)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]

@@ -55,8 +55,9 @@ _SIGS = {
     "mtp_row_linear_fwd": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 3 + [_VP]),
     "mtp_row_linear_bwd": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 7
                            + [ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
-    "mtp_attn_fwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int32, _VP]),
-    "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
+    "mtp_attn_fwd": (ctypes.c_int, [_VP] + [_VP] * 4 + [ctypes.c_int32, _VP, _VP]),
+    "mtp_attn_bwd": (ctypes.c_int, [_VP] + [_VP] * 6
+                     + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP, _VP]),
     "mtp_attn_bwd_noalloc": (ctypes.c_int, [_VP] + [_VP] * 6 + [ctypes.c_int32, _VP]),
     "mtp_quantize_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "mtp_linear_fwd_fp8": (ctypes.c_int, [_VP, ctypes.c_int] + [_VP] * 8 + [_VP]),
@@ -184,15 +185,17 @@ def mtp_row_linear_bwd(desc, kind, dy, x_local, w, gelu_preact, dx_local, dw, db
                  int(accumulate), _addr(ws), ws_bytes, _stream(stream))
 
 
-def mtp_attn_fwd(desc, qkv, ctx, lse, cu_seqlens=None, n_seqs=0, stream=None):
+def mtp_attn_fwd(desc, qkv, ctx, lse, cu_seqlens=None, n_seqs=0, ctx_amax_parts=None,
+                 stream=None):
     return _call("mtp_attn_fwd", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
-                 _addr(cu_seqlens), int(n_seqs), _stream(stream))
+                 _addr(cu_seqlens), int(n_seqs), _addr(ctx_amax_parts), _stream(stream))
 
 
-def mtp_attn_bwd(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, ws, ws_bytes, stream=None):
+def mtp_attn_bwd(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, ws, ws_bytes,
+                 dqkv_amax_parts=None, stream=None):
     return _call("mtp_attn_bwd", ctypes.byref(desc), _addr(qkv), _addr(ctx), _addr(lse),
                  _addr(dctx), _addr(dqkv), _addr(cu_seqlens), int(n_seqs), _addr(ws), ws_bytes,
-                 _stream(stream))
+                 _addr(dqkv_amax_parts), _stream(stream))
 
 
 def mtp_attn_bwd_noalloc(desc, qkv, ctx, lse, dctx, dqkv, cu_seqlens, n_seqs, stream=None):

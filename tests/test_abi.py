@@ -104,9 +104,9 @@ def test_kind_and_workspace_errors():
     need = mtp.mtp_workspace_size(d, mtp.MTP_OP_ATTN_BWD)
     assert need == 2 * 16 * 2048 * 4  # two fp32 rows per local head: D and lse*log2(e)
     assert lib.mtp_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
-                            need - 1, None) == mtp.MTP_ERR_WORKSPACE
+                            need - 1, None, None) == mtp.MTP_ERR_WORKSPACE
     assert lib.mtp_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
-                            need, None) == mtp.MTP_ERR_WORKSPACE
+                            need, None, None) == mtp.MTP_ERR_WORKSPACE
     # a bias gradient needs the workspace
     need = mtp.mtp_workspace_size(d, mtp.MTP_OP_COL_LINEAR_BWD, mtp.MTP_QKV)
     assert need > 0
@@ -119,7 +119,8 @@ def test_kind_and_workspace_errors():
     arr[3] = FAKE + 4
     assert lib.mtp_partial_sum(ctypes.byref(d), arr, 4, None, None, FAKE, None) == mtp.MTP_ERR_INVALID_ARG
     # cu_seqlens given with no sequences
-    assert lib.mtp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None) == mtp.MTP_ERR_INVALID_ARG
+    assert lib.mtp_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None,
+                            None) == mtp.MTP_ERR_INVALID_ARG
     # vocab entry points need a vocabulary
     assert lib.mtp_vocab_ce_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
                                   None) == mtp.MTP_ERR_INVALID_ARG
@@ -192,9 +193,9 @@ def test_oversize_operands_refused_before_any_launch():
                                   None) == mtp.MTP_ERR_INVALID_ARG  # reaches the pointer check
     # attention: qkv [T, 3 h_l] at T = 2^20, h_l = 2048 spans 12 GiB
     da = valid(seq_len=1 << 20)
-    assert lib.mtp_attn_fwd(ctypes.byref(da), FAKE, FAKE, FAKE, None, 0, None) == U
+    assert lib.mtp_attn_fwd(ctypes.byref(da), FAKE, FAKE, FAKE, None, 0, None, None) == U
     assert lib.mtp_attn_bwd(ctypes.byref(da), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
-                            1 << 40, None) == U
+                            1 << 40, None, None) == U
     assert lib.mtp_attn_fwd_block(ctypes.byref(da), FAKE, 0, 1024, 0, 1024, FAKE, FAKE, None,
                                   0, None) == U
 
@@ -279,9 +280,9 @@ def test_fp8_entry_points_refuse_bad_arguments():
 
 
 def test_layernorm_amax_parts_arguments():
-    """The FP8 amax parts of the LayerNorm entry points: refused for an fp32
-    shard (there is no FP8 path for it) and when misaligned, before any
-    launch."""
+    """The FP8 amax parts of the LayerNorm and attention entry points:
+    refused for an fp32 shard (there is no FP8 path for it) and when
+    misaligned, before any launch."""
     lib = mtp.lib()
     f32 = ctypes.byref(valid(dtype=mtp.MTP_F32))
     bd = ctypes.byref(valid())
@@ -293,3 +294,6 @@ def test_layernorm_amax_parts_arguments():
                                              FAKE, FAKE, am, None) == want
         assert lib.mtp_layernorm_bwd_sum(d, parts, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                          FAKE, 0, FAKE, 1 << 30, am, None) == want
+        assert lib.mtp_attn_fwd(d, FAKE, FAKE, FAKE, None, 0, am, None) == want
+        assert lib.mtp_attn_bwd(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 30, am,
+                                None) == want

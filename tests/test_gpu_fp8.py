@@ -354,3 +354,56 @@ def test_amax_parts_from_fp8_gemm_epilogues(T):
             codes.append((q, qt, s))
         torch.cuda.synchronize()
         assert all(torch.equal(a_, b_) for a_, b_ in zip(*codes))
+
+
+@pytest.mark.parametrize("T,docs", [(2048, None), (304, None), (8192, None), (2048, [0, 700, 1500, 2048])])
+def test_amax_parts_from_attention(T, docs):
+    """The attention forward (ctx) and backward (dqkv) write the amax parts
+    of their bf16 output when asked: outputs equal those of the calls
+    without parts, the largest part is the largest |value| stored, every slot
+    is written, and the codes made from the parts equal those of a separate
+    amax pass bit for bit.  7B TP=2 shard heads (16 of d = 128); T = 8192
+    gives the forward more workgroups than parts (the pass over ctx then
+    writes them); the backward's 3 x 32 x 16 workgroups at T = 2048 share
+    the 1024 slots; one case packs three documents."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    h, a, f, tp = 4096, 32, 11008, 2
+    hl, al = h // tp, a // tp
+    d = mtp.make_desc(h, a, f, tp, 0, T, 1, mtp.MTP_BF16)
+    qkv = (_bf16((T, 3 * hl), 160 + T) * 2).cuda()
+    dctx = _bf16((T, hl), 161 + T, 0.05).cuda()
+    cu = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    n = 0 if docs is None else len(docs) - 1
+    P = lambda: torch.full((mtp.FP8_AMAX_PARTS,), 1e30, dtype=torch.float32, device="cuda")
+    ctx0, ctx1 = (torch.empty(T, hl, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    lse0, lse1 = (torch.empty(al, T, dtype=torch.float32, device="cuda") for _ in range(2))
+    p_ctx, p_dqkv = P(), P()
+    mtp.mtp_attn_fwd(d, qkv, ctx0, lse0, cu, n)
+    mtp.mtp_attn_fwd(d, qkv, ctx1, lse1, cu, n, ctx_amax_parts=p_ctx)
+    wsb = mtp.mtp_workspace_size(d, mtp.MTP_OP_ATTN_BWD)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    g0, g1 = (torch.empty(T, 3 * hl, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    mtp.mtp_attn_bwd(d, qkv, ctx0, lse0, dctx, g0, cu, n, ws, wsb)
+    mtp.mtp_attn_bwd(d, qkv, ctx0, lse0, dctx, g1, cu, n, ws, wsb, dqkv_amax_parts=p_dqkv)
+    torch.cuda.synchronize()
+    assert torch.equal(ctx0, ctx1) and torch.equal(lse0, lse1) and torch.equal(g0, g1)
+    for name, y, p, fmt in (("ctx", ctx1, p_ctx, mtp.MTP_FP8_E4M3),
+                            ("dqkv", g1, p_dqkv, mtp.MTP_FP8_E5M2)):
+        ref = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_amax(d, y, y.numel(), ref)
+        torch.cuda.synchronize()
+        want = float(y.float().abs().max())
+        log(f"attention amax parts {name} T={T} docs={docs}: fused {float(p.max())!r} separate "
+            f"{float(ref.max())!r} max|y| {want!r}")
+        assert float(p.max()) == want == float(ref.max()) and float(p.min()) >= 0.0
+        rows, cols = y.shape
+        codes = []
+        for pp in (p, ref):
+            q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+            qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+            s = torch.empty(1, dtype=torch.float32, device="cuda")
+            mtp.mtp_fp8_quantize(d, fmt, y, rows, cols, [pp], q, qt, s)
+            codes.append((q, qt, s))
+        torch.cuda.synchronize()
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(*codes))

@@ -417,14 +417,15 @@ def test_zero_tokens_writes_zero_gradients():
     dg2 = torch.full((h,), 7.0, device="cuda")
     dbt2 = torch.full((h,), 7.0, device="cuda")
     # FP8 amax parts of an empty output: every slot zero
-    am = [torch.full((mtp.FP8_AMAX_PARTS,), 7.0, device="cuda") for _ in range(3)]
+    am = [torch.full((mtp.FP8_AMAX_PARTS,), 7.0, device="cuda") for _ in range(5)]
     mtp.mtp_layernorm_bwd_sum(d, [dummy, dummy], dummy, dummy, stat, stat, None, dummy, dg2, dbt2,
                               0, ws, 256, amax_parts=am[0])
     mtp.mtp_partial_sum_layernorm(d, [dummy, dummy], None, None, dummy, dummy, dummy, dummy,
                                   stat, stat, amax_parts=am[1])
     mtp.mtp_layernorm(d, dummy, dummy, dummy, dummy, stat, stat, amax_parts=am[2])
     lse = torch.empty(64, dtype=torch.float32, device="cuda")
-    mtp.mtp_attn_fwd(d, dummy, dummy, lse)
+    mtp.mtp_attn_fwd(d, dummy, dummy, lse, ctx_amax_parts=am[3])
+    mtp.mtp_attn_bwd(d, dummy, dummy, lse, dummy, dummy, None, 0, ws, 256, dqkv_amax_parts=am[4])
     torch.cuda.synchronize()
     assert float(dw.abs().max()) == 0.0 and float(db.abs().max()) == 0.0
     assert float(dg.abs().max()) == 0.0 and float(dbt.abs().max()) == 0.0
