@@ -502,21 +502,18 @@ class TPLayer(_Probed):
         d0, rep, T = self.d0, self.rep, self._timed
         E4, q8, r8 = mtp.MTP_FP8_E4M3, self.q8, self.r8
         self.x = x
-        with T("ln1"):
-            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1,
-                              amax_parts=q8["ln1"]["amax"])
         # The weights' codes (made once per optimizer update; with gradient
-        # accumulation they serve every micro-batch until the next one): the
-        # QKV weight's on the main stream, the other three on the second
-        # stream, which has no other work in the forward; each GEMM waits for
-        # its weight's codes only.
+        # accumulation they serve every micro-batch until the next one), on
+        # the second stream, which has no other work in the forward, beside
+        # LN1 and its codes; each GEMM waits for its weight's codes only.
         side = self.side
-        with T("quant_w"):
-            self._quant_split("wqkv", {r: self.w[r]["wqkv"] for r in self.ranks}, E4, ext)
         ready = {}
         if side is not None:
             side.wait_stream(torch.cuda.current_stream(self.device))
-        for name in ("wo", "w1", "w2"):
+        with T("ln1"):
+            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1,
+                              amax_parts=q8["ln1"]["amax"])
+        for name in ("wqkv", "wo", "w1", "w2"):
             with (torch.cuda.stream(side) if side is not None else contextlib.nullcontext()), \
                     T("quant_w", side):
                 self._quant_split(name, {r: self.w[r][name] for r in self.ranks}, E4, ext)
@@ -529,6 +526,7 @@ class TPLayer(_Probed):
                 torch.cuda.current_stream(self.device).wait_event(ready[name])
         with T("quant"):
             self._quant_shared("ln1", self.ln1, E4, amax_written=True)
+        wait_w("wqkv")
         for r in self.ranks:
             d, w, a, c = self.descs[r], self.w[r], self.a[r], r8[r]
             with T("qkv_fwd"):
