@@ -364,26 +364,12 @@ def main(argv=None) -> int:
     step = step_of(L)
     step1 = step_of(L1)
 
-    # The comparison passes run first and the headline region last: the GPU
+    # The comparison passes (one-stream eager and graph replays, per-call
+    # times) run first and the headline region last: the GPU
     # comes out of the idle of the set-up at low clocks, and its first tens
     # of milliseconds of steps run several % slower than the steady state a
     # training job sees (measured: 30 steps after 5 warm-up steps 1.217 ms
     # per step, the next 30 1.176; after 2 s idle 1.254, then 1.168).
-
-    # Per-call times: a few steps with events around every call.
-    calls = {t: [] for t in CALL_TAGS + HEAD_TAGS}
-    n_call_steps = 5
-    L.probe = calls
-    if H is not None:
-        H.probe = calls
-    for _ in range(n_call_steps):
-        step()
-    torch.cuda.synchronize()
-    L.probe = None
-    if H is not None:
-        H.probe = None
-    call_us = {t: round(1e3 * sum(a.elapsed_time(b) for a, b in calls[t]) / n_call_steps, 1)
-               for t in CALL_TAGS + HEAD_TAGS if calls[t]}
 
     # The same step replayed from a HIP graph (captured once, inputs
     # unchanged): the one-stream step, and the two-stream one beside it.
@@ -431,6 +417,21 @@ def main(argv=None) -> int:
     eager_one_stream_ms = eager_ms(step1)
     graph_ms = graph_replay_ms(step1)
     graph_ms_two_streams = graph_replay_ms(step)
+
+    # Per-call times: a few steps with events around every call.
+    calls = {t: [] for t in CALL_TAGS + HEAD_TAGS}
+    n_call_steps = 5
+    L.probe = calls
+    if H is not None:
+        H.probe = calls
+    for _ in range(n_call_steps):
+        step()
+    torch.cuda.synchronize()
+    L.probe = None
+    if H is not None:
+        H.probe = None
+    call_us = {t: round(1e3 * sum(a.elapsed_time(b) for a, b in calls[t]) / n_call_steps, 1)
+               for t in CALL_TAGS + HEAD_TAGS if calls[t]}
 
     for _ in range(args.warmup):
         step()
