@@ -438,12 +438,13 @@ gemm_bf16_kernel(GemmParams p) {
                      : frag_m<BN>(tb, wn * WTN + j * 32, kk, lane);
     }
   };
-  // The MFMAs of a k-step walk the FM x FN blocks in snake order (odd rows of A fragments take the B fragments backwards), so that
-  // consecutive MFMAs at a row change share their B fragment.  The board
-  // runs these GEMMs at its power limit, where fewer operand bits changing
-  // between instructions buys clock: the 12 shard GEMMs 911.0 / 912.2 ->
-  // 908.3 / 906.9 us, the layer step 1.1733 / 1.1653 -> 1.1695 / 1.1609 ms
-  // (two interleaved rounds, bit-identical results).
+  // The MFMAs of a k-step walk the FM x FN blocks in snake order (odd rows
+  // of A fragments take the B fragments backwards), so that consecutive
+  // MFMAs at a row change share their B fragment.  The board runs these
+  // GEMMs at its power limit, where fewer operand bits changing between
+  // instructions buys clock: the 12 shard GEMMs 911.0 / 912.2 -> 908.3 /
+  // 906.9 us, the layer step 1.1733 / 1.1653 -> 1.1695 / 1.1609 ms (two
+  // interleaved rounds, bit-identical results).
   // LDS reads per k-step (transpose reads come in pairs).
   constexpr int kReads = F8 ? 2 * (FM + FN) : FM * (AK ? 1 : 2) + FN * (BKM ? 1 : 2);
   constexpr int kPerMfma = (kReads + FM * FN - 1) / (FM * FN);
