@@ -48,7 +48,7 @@ FWD_TAGS = ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")
 CALL_TAGS = ("ln1", "qkv_fwd", "attn_fwd", "proj_fwd", "sum_proj_ln2", "fc1_fwd", "fc2_fwd",
              "sum_fc2", "fc2_dgrad", "fc2_wgrad", "fc2_bias", "fc1_dgrad", "fc1_wgrad", "ln2_bwd",
              "proj_dgrad", "proj_wgrad", "proj_bias", "attn_bwd", "qkv_dgrad", "qkv_wgrad",
-             "ln1_bwd", "quant", "quant_w")
+             "ln1_bwd", "qkv_bias", "quant", "quant_w")
 HEAD_TAGS = ("vocab_fwd", "ce_stats", "ce_combine", "ce_bwd", "vocab_bwd", "sum_vocab_dy")
 PROBE_EVERY = 10
 WGRAD_TAGS = ("fc2_wgrad", "fc1_wgrad", "proj_wgrad", "qkv_wgrad")

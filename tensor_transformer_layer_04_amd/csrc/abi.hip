@@ -250,7 +250,6 @@ int mtp_col_linear_bwd(const mtp_shard_desc* desc, int kind, const void* dy, con
     g.B = x; g.ldb = s.h; g.b_kmajor = false;
     g.M = static_cast<int>(n); g.N = s.h; g.K = static_cast<int>(s.T);
     g.C = dw; g.ldc = s.h; g.epi = accumulate ? mtp::kEpiF32Acc : mtp::kEpiF32;
-   
     e = gemm(s, g, str);
     if (e != hipSuccess) return MTP_ERR_HIP;
   }

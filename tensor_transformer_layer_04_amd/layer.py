@@ -477,7 +477,7 @@ class TPLayer(_Probed):
             fork()
             with on_side(), T("qkv_wgrad", side):
                 mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None,
-                                       g["dwqkv"], g["dbqkv"], 0, wss, wsb)
+                                       g["dwqkv"], None, 0, wss, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
         if self.sp:
             for r in self.ranks:
@@ -493,9 +493,21 @@ class TPLayer(_Probed):
                 mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
                                           self.dy1, self.dx, self.rgrads["dln1_g"],
                                           self.rgrads["dln1_b"], 0, ws, wsb)
+        self._qkv_bias_grad()
         if side is not None:
             main.wait_stream(side)
         return self.dx
+
+    def _qkv_bias_grad(self):
+        """QKV bias gradients (column sums of dqkv) on the main stream after the
+        LN1 backward: there they run beside the QKV weight gradient, the last
+        kernel of the second stream, instead of after it at the end of the
+        step."""
+        for r in self.ranks:
+            with self._timed("qkv_bias"):
+                mtp.mtp_col_linear_bwd(self.descs[r], mtp.MTP_QKV, self.a[r]["dqkv"], self.ln1,
+                                       self.w[r]["wqkv"], None, None, self.grads[r]["dbqkv"], 0,
+                                       self.ws, self.ws_bytes)
 
     # ------------------------------------------------------------- FP8 step
     def _forward_fp8(self, x, ext):
@@ -663,13 +675,12 @@ class TPLayer(_Probed):
                 mtp.mtp_linear_bwd_fp8(d, mtp.MTP_QKV, None, c["dqkv"]["qt"], c["dqkv"]["s"],
                                        None, None, q8["ln1"]["qt"], q8["ln1"]["s"], None, None,
                                        g["dwqkv"])
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_QKV, a["dqkv"], self.ln1, w["wqkv"], None, None,
-                                       g["dbqkv"], 0, wss, wsb)
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
         with T("ln1_bwd"):
             mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
                                       self.dy1, self.dx, self.rgrads["dln1_g"],
                                       self.rgrads["dln1_b"], 0, ws, wsb)
+        self._qkv_bias_grad()
         if side is not None:
             main.wait_stream(side)
         return self.dx
