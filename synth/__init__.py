@@ -186,6 +186,10 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_fp8_d64_tp4": LayerConfig(
         "small_fp8_d64_tp4", hidden=512, heads=8, ffn=2176, tp=4, seq_len=208, dtype="bf16",
         fp8=True),
+    # the FP8 step over packed documents (block-diagonal causal attention)
+    "small_fp8_varlen_tp2": LayerConfig(
+        "small_fp8_varlen_tp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        varlen_tokens=304, doc_min=1, doc_max=150, affine_random=True, fp8=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }
