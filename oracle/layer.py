@@ -32,7 +32,11 @@ With ``fp8=True`` the same layer runs its twelve products on FP8 codes with
 per-tensor scales (``oracle.fp8``): each forward map on the E4M3 codes of
 its input and weight, each data and weight gradient on the E5M2 codes of the
 incoming gradient and the forward's E4M3 codes; everything else (LayerNorm,
-attention, GeLU, residuals, bias gradients) stays as above.
+attention, GeLU / SwiGLU, residuals, bias gradients) stays as above.  In the
+SwiGLU variant the gate and up projections are one FFN input map,
+[u | u3] = ln2 [W1; W3]^T, whose weight [W1; W3] is one tensor with one
+scale, and whose incoming gradient [du | du3] is one E5M2 tensor (reading:
+the pages name the flags, not a recipe; one map, one scale each).
 
 Readings where the pages are silent (each is a stated choice, not a fact of the pages):
 pre-LN; LayerNorm with population variance and eps inside the square root;
@@ -286,8 +290,6 @@ def layer_forward(params: Dict, x, heads: int, eps: float, starts,
     x = to64(x)
     h = x.shape[1]
     c: Dict[str, np.ndarray] = {"x": x}
-    if fp8 and "w3" in p:
-        raise ValueError("the FP8 reading covers the GeLU FFN only")
     c["ln1"], c["mu1"], c["rstd1"] = layernorm(x, p["ln1_g"], p["ln1_b"], eps)
     wqkv = np.concatenate([p["wq"], p["wk"], p["wv"]], axis=0)
     c["qkv"] = _fwd_product(c, "qkv", c["ln1"], wqkv, p["bqkv"], fp8)
@@ -295,7 +297,13 @@ def layer_forward(params: Dict, x, heads: int, eps: float, starts,
     c["ctx"], c["lse"] = attention_forward(q, k, v, heads, starts)
     c["y1"] = x + _fwd_product(c, "proj", c["ctx"], p["wo"], p["bo"], fp8)
     c["ln2"], c["mu2"], c["rstd2"] = layernorm(c["y1"], p["ln2_g"], p["ln2_b"], eps)
-    if "w3" in p:
+    if "w3" in p and fp8:
+        f = p["w1"].shape[0]
+        w13 = np.concatenate([p["w1"], p["w3"]], axis=0)
+        u13 = _fwd_product(c, "fc1", c["ln2"], w13, None, fp8)
+        c["u"], c["u3"] = u13[:, :f], u13[:, f:]
+        c["g"] = silu(c["u"]) * c["u3"]
+    elif "w3" in p:
         c["u"] = linear(c["ln2"], p["w1"])
         c["u3"] = linear(c["ln2"], p["w3"])
         c["g"] = silu(c["u"]) * c["u3"]
@@ -335,9 +343,16 @@ def layer_backward(params: Dict, cache: Dict[str, np.ndarray], dy, heads: int,
         du = dg * c["u3"] * silu_grad(c["u"])
         du3 = dg * silu(c["u"])
         gr["du"], gr["du3"] = du, du3
-        gr["dw1"] = du.T @ c["ln2"]
-        gr["dw3"] = du3.T @ c["ln2"]
-        dln2 = du @ p["w1"] + du3 @ p["w3"]
+        if "fp8" in c:
+            f = p["w1"].shape[0]
+            w13 = np.concatenate([p["w1"], p["w3"]], axis=0)
+            dln2, dw13 = _bwd_products(c, gr, "fc1", np.concatenate([du, du3], axis=1),
+                                       c["ln2"], w13)
+            gr["dw1"], gr["dw3"] = dw13[:f], dw13[f:]
+        else:
+            gr["dw1"] = du.T @ c["ln2"]
+            gr["dw3"] = du3.T @ c["ln2"]
+            dln2 = du @ p["w1"] + du3 @ p["w3"]
     else:
         du = dg * gelu_tanh_grad(c["u"])
         gr["du"] = du
@@ -446,12 +461,18 @@ def rank_view(fwd: Dict[str, np.ndarray], grads: Optional[Dict[str, np.ndarray]]
         v["du"] = grads["du"][:, fc]
         v["dw2"] = grads["dw2"][:, fc]
         v["dw1"] = grads["dw1"][fc]
-        v["fc1_dx_partial"] = opnd(grads["du"], "fc1", "qdy")[:, fc] @ opnd(p["w1"], "fc1", "qw")[fc]
         if "w3" in p:
             v["du3"] = grads["du3"][:, fc]
             v["dw3"] = grads["dw3"][fc]
-            v["fc1_dx_partial"] = v["fc1_dx_partial"] + grads["du3"][:, fc] @ p["w3"][fc]
+            # the rank's gate and up rows of the one FFN input map [W1; W3]
+            du13 = np.concatenate([grads["du"], grads["du3"]], axis=1)
+            w13 = np.concatenate([p["w1"], p["w3"]], axis=0)
+            rows = np.r_[r * fl:(r + 1) * fl, f + r * fl:f + (r + 1) * fl]
+            v["fc1_dx_partial"] = (opnd(du13, "fc1", "qdy")[:, rows]
+                                   @ opnd(w13, "fc1", "qw")[rows])
         else:
+            v["fc1_dx_partial"] = (opnd(grads["du"], "fc1", "qdy")[:, fc]
+                                   @ opnd(p["w1"], "fc1", "qw")[fc])
             v["db1"] = grads["db1"][fc]
         v["dctx"] = grads["dctx"][:, hc]
         v["dwo"] = grads["dwo"][:, hc]

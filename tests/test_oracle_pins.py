@@ -537,11 +537,12 @@ class _TorchFP8Linear(torch.autograd.Function):
         return (qg @ qw) * (sg * sw), (qg.T @ qx) * (sg * sx), gy.sum(0)
 
 
-@pytest.mark.parametrize("name", ["tiny_tp2", "small_varlen_tp1"])
+@pytest.mark.parametrize("name", ["tiny_tp2", "small_varlen_tp1", "tiny_swiglu_tp2"])
 def test_fp8_layer_matches_torch_autograd(name):
     """The FP8 layer (forward and backward) against an independent build of
     it from torch library pieces: layer_norm, scaled_dot_product_attention
-    with the same mask, tanh GeLU, autograd for the chain rule, and an FP8
+    with the same mask, tanh GeLU (or SiLU(gate) * up with the gate and up
+    projections as one FP8 map), autograd for the chain rule, and an FP8
     linear function on torch's float8 casts.  Agreement to fp64 rounding."""
     import torch.nn.functional as F
     cfg = synth.get_config(name).replace(affine_random=True, dtype="f32")
@@ -563,7 +564,13 @@ def test_fp8_layer_matches_torch_autograd(name):
     ctx = F.scaled_dot_product_attention(q, k, v, attn_mask=allowed).transpose(0, 1).reshape(T, h)
     y1 = x + _TorchFP8Linear.apply(ctx, P["wo"], P["bo"])
     ln2 = F.layer_norm(y1, (h,), P["ln2_g"], P["ln2_b"], cfg.eps)
-    g = F.gelu(_TorchFP8Linear.apply(ln2, P["w1"], P["b1"]), approximate="tanh")
+    if cfg.swiglu:
+        f = cfg.ffn
+        u13 = _TorchFP8Linear.apply(ln2, torch.cat([P["w1"], P["w3"]]),
+                                    torch.zeros(2 * f, dtype=torch.float64))
+        g = F.silu(u13[:, :f]) * u13[:, f:]
+    else:
+        g = F.gelu(_TorchFP8Linear.apply(ln2, P["w1"], P["b1"]), approximate="tanh")
     y = y1 + _TorchFP8Linear.apply(g, P["w2"], P["b2"])
     (y * dy).sum().backward()
     c = oracle.layer_forward(data, data["x"], a, cfg.eps, starts, fp8=True)
@@ -576,18 +583,24 @@ def test_fp8_layer_matches_torch_autograd(name):
         assert err <= tol, f"{what}: rel {err:.2e}"
     close(y, c["y"], "y")
     close(x.grad, gr["dx"], "dx")
-    for pn, gn in PARAM_GRADS[1:]:
+    for pn, gn in (SWIGLU_PARAM_GRADS if cfg.swiglu else PARAM_GRADS)[1:]:
         close(P[pn].grad, gr[gn], gn)
     # the FP8 layer is not the exact one, but within the formats' error
     e = np.linalg.norm(c["y"] - exact["y"]) / np.linalg.norm(exact["y"])
     assert 1e-4 < e < 5e-2, e
 
 
-@pytest.mark.parametrize("tp", [2, 4])
-def test_fp8_column_row_split_is_exact(tp):
+@pytest.mark.parametrize("tp,swiglu", [(2, False), (4, False), (2, True), (4, True)])
+def test_fp8_column_row_split_is_exact(tp, swiglu):
     """With whole-tensor scales the ranks' FP8 partials still sum to the
-    unsharded FP8 products (forward and backward)."""
-    cfg, data, starts = _tiny(seed=4)
+    unsharded FP8 products (forward and backward), also with the SwiGLU
+    FFN's gate and up rows taken per rank from the one map [W1; W3]."""
+    if swiglu:
+        cfg = synth.get_config("tiny_swiglu_tp2").replace(seed=4)
+        data = synth.generate(cfg)
+        starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
+    else:
+        cfg, data, starts = _tiny(seed=4)
     c = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts, fp8=True)
     g = oracle.layer_backward(data, c, data["dy"], cfg.heads, starts)
     p64 = {k: oracle.to64(v) for k, v in data.items() if k not in ("cu_seqlens",)}
