@@ -297,13 +297,17 @@ int mtp_quantize_fp8(const mtp_shard_desc* desc, const void* x, int64_t n, uint8
  *   w8 the codes and scales of mtp_quantize_fp8 of the layouts of
  *   mtp_col_linear_fwd / mtp_row_linear_fwd: kind MTP_QKV (x8 [T,h], w8
  *   [3h_l,h], b nullable, y [T,3h_l]), MTP_FC1 (w8 [f_l,h]; preact [T,f_l]
- *   receives u, y GeLU_tanh(u)), MTP_PROJ (x8 [T,h_l], w8 [h,h_l], y the
- *   partial [T,h], b NULL) or MTP_FC2 (x8 [T,f_l], w8 [h,f_l], b NULL).  y
- *   and preact in the shard dtype; the inner width must be a multiple of 16
- *   (else MTP_ERR_UNSUPPORTED).  amax_parts: nullable, MTP_FC1 only (else
- *   MTP_ERR_INVALID_ARG): 1024 fp32 (out) receiving partial maxima of |y| as
- *   stored in the form mtp_fp8_amax writes, for mtp_fp8_quantize of y
- *   without a separate amax pass.                                            */
+ *   receives u, y GeLU_tanh(u)), MTP_FC1_SWIGLU (w8 [2f_l,h], the codes of
+ *   the interleaved gate|up rows of mtp_col_linear_fwd(MTP_FC1_SWIGLU) under
+ *   one scale; b NULL; preact [T,2f_l] receives the interleaved gate|up
+ *   product, y [T,f_l] SiLU(gate) * up; f_l % 4 == 0), MTP_PROJ (x8 [T,h_l],
+ *   w8 [h,h_l], y the partial [T,h], b NULL) or MTP_FC2 / MTP_FC2_SWIGLU (x8
+ *   [T,f_l], w8 [h,f_l], b NULL).  y and preact in the shard dtype; the inner
+ *   width must be a multiple of 16 (else MTP_ERR_UNSUPPORTED).  amax_parts:
+ *   nullable, MTP_FC1 and MTP_FC1_SWIGLU only (else MTP_ERR_INVALID_ARG):
+ *   1024 fp32 (out) receiving partial maxima of |y| as stored in the form
+ *   mtp_fp8_amax writes, for mtp_fp8_quantize of y without a separate amax
+ *   pass.                                                                    */
 int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
                        const float* x_scale, const uint8_t* w8, const float* w_scale,
                        const void* b, void* y, void* preact, float* amax_parts, void* stream);
@@ -330,17 +334,23 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
  *   them; scale [1] fp32 (out) receives s.  With n = 0 or rows = 0, x, q
  *   and q_t may be NULL.
  * mtp_linear_bwd_fp8: the gradients of one of the linear maps of kind
- *   (QKV, FC1, PROJ, FC2; out x in = 3h_l x h, f_l x h, h x h_l, h x f_l)
- *   from FP8 codes:
+ *   (QKV, FC1, FC1_SWIGLU, PROJ, FC2, FC2_SWIGLU; out x in = 3h_l x h,
+ *   f_l x h, 2f_l x h (the interleaved gate|up rows), h x h_l, h x f_l,
+ *   h x f_l) from FP8 codes:
  *   dx [T, in] dtype (nullable) = (dy8 [T, out] E5M2) (w8_t [in, out] E4M3,
  *     the transposed codes of W)^T * dy_scale * w_scale, times
  *     GeLU_tanh'(preact) for FC2 with preact = u [T, f_l] (the FFN's du);
+ *     for FC2_SWIGLU with preact = the interleaved gate|up product
+ *     [T, 2f_l], dx [T, 2f_l] instead receives in that order the gradients
+ *     w.r.t. gate and up as mtp_row_linear_bwd(MTP_FC2_SWIGLU) defines
+ *     them, ready for quantization as one E5M2 tensor;
  *     needs out % 16 == 0;
  *   dw [out, in] fp32 (nullable; += when accumulate) = (dy8_t [out, T] E5M2,
  *     the transposed codes of dy) (x8_t [in, T] E4M3, those of the forward
  *     input)^T * dy_scale * x_scale; needs T % 16 == 0;
- *   dx_amax_parts: nullable, only with dx and preact (FC2's du; else
- *     MTP_ERR_INVALID_ARG): partial maxima of |dx| as in mtp_linear_fwd_fp8.
+ *   dx_amax_parts: nullable, only with dx and preact (FC2's du, or the
+ *     interleaved [dgate | dup] of FC2_SWIGLU; else MTP_ERR_INVALID_ARG):
+ *     partial maxima of |dx| as in mtp_linear_fwd_fp8.
  *   Scales are [1] fp32 device values as written by mtp_fp8_quantize.     */
 int mtp_fp8_amax(const mtp_shard_desc* desc, const void* x, int64_t n, float* amax_parts,
                  void* stream);

@@ -116,6 +116,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         fp8=True,
         description="7B-style layer, one TP=2 rank shard, its twelve GEMMs on FP8 codes (E4M3 "
                     "activations and weights, E5M2 gradients, per-tensor scales), bf16 elsewhere"),
+    "7b_tp2_swiglu_fp8": LayerConfig(
+        "7b_tp2_swiglu_fp8", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        swiglu=True, fp8=True,
+        description="7B-style layer with a SwiGLU FFN, one TP=2 rank shard, its twelve GEMMs on "
+                    "FP8 codes (gate and up under one scale), bf16 elsewhere"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -190,6 +195,13 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_fp8_varlen_tp2": LayerConfig(
         "small_fp8_varlen_tp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
         varlen_tokens=304, doc_min=1, doc_max=150, affine_random=True, fp8=True),
+    # the FP8 step with the SwiGLU FFN (gate|up one tensor under one scale)
+    "small_fp8_swiglu_tp2": LayerConfig(
+        "small_fp8_swiglu_tp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        swiglu=True, affine_random=True, fp8=True),
+    "small_fp8_swiglu_d64_tp4": LayerConfig(
+        "small_fp8_swiglu_d64_tp4", hidden=512, heads=8, ffn=2176, tp=4, seq_len=208,
+        dtype="bf16", swiglu=True, fp8=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

@@ -495,30 +495,35 @@ int mtp_linear_fwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* x8,
   int st = check_desc(desc, &s);
   if (st != MTP_OK) return st;
   if (!s.bf16) return MTP_ERR_UNSUPPORTED;
-  // column-parallel QKV / FC1 (GeLU) or row-parallel PROJ / FC2 (partial)
+  // column-parallel QKV / FC1 (GeLU or SwiGLU over the interleaved
+  // gate|up product) or row-parallel PROJ / FC2 (partial)
   int64_t n = 0, k = 0;
   switch (kind) {
     case MTP_QKV: n = 3LL * s.hl; k = s.h; break;
     case MTP_FC1: n = s.fl; k = s.h; break;
+    case MTP_FC1_SWIGLU: n = 2LL * s.fl; k = s.h; break;
     case MTP_PROJ: n = s.h; k = s.hl; break;
-    case MTP_FC2: n = s.h; k = s.fl; break;
+    case MTP_FC2: case MTP_FC2_SWIGLU: n = s.h; k = s.fl; break;
     default: return MTP_ERR_INVALID_ARG;
   }
+  const bool fc1 = kind == MTP_FC1 || kind == MTP_FC1_SWIGLU;
+  const bool swiglu = kind == MTP_FC1_SWIGLU;
   if (!ok_ptr(x8) || !ok_ptr(x_scale) || !ok_ptr(w8) || !ok_ptr(w_scale) || !ok_opt(b) ||
       !ok_ptr(y))
     return MTP_ERR_INVALID_ARG;
-  if (kind == MTP_FC1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
-  if ((kind == MTP_PROJ || kind == MTP_FC2) && b != nullptr) return MTP_ERR_INVALID_ARG;
-  if (!ok_opt(amax_parts) || (amax_parts && kind != MTP_FC1)) return MTP_ERR_INVALID_ARG;
-  if (k % 16 != 0) return MTP_ERR_UNSUPPORTED;
+  if (fc1 ? !ok_ptr(preact) : preact != nullptr) return MTP_ERR_INVALID_ARG;
+  if ((kind == MTP_PROJ || kind == MTP_FC2 || kind == MTP_FC2_SWIGLU || swiglu) && b != nullptr)
+    return MTP_ERR_INVALID_ARG;
+  if (!ok_opt(amax_parts) || (amax_parts && !fc1)) return MTP_ERR_INVALID_ARG;
+  if (k % 16 != 0 || (swiglu && n % 8 != 0)) return MTP_ERR_UNSUPPORTED;
   if (!fits(s.T, k, 1) || !fits(n, k, 1)) return MTP_ERR_UNSUPPORTED;
   GemmDesc g{};
   g.A = x8; g.lda = k; g.a_kmajor = true;
   g.B = w8; g.ldb = k; g.b_kmajor = true;
   g.M = static_cast<int>(s.T); g.N = static_cast<int>(n); g.K = static_cast<int>(k);
-  g.C = y; g.ldc = n; g.bias = b;
+  g.C = y; g.ldc = swiglu ? n / 2 : n; g.bias = b;
   g.aux = preact; g.ld_aux = n;
-  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : mtp::kEpiStore;
+  g.epi = kind == MTP_FC1 ? mtp::kEpiGelu : swiglu ? mtp::kEpiSwiGLU : mtp::kEpiStore;
   g.fp8 = true; g.scale_a = x_scale; g.scale_b = w_scale;
   g.amax = amax_parts;
   return hip_status(mtp::gemm_bf16(g, static_cast<hipStream_t>(stream)));
@@ -569,12 +574,15 @@ int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
   switch (kind) {
     case MTP_QKV: out = 3LL * s.hl; in = s.h; break;
     case MTP_FC1: out = s.fl; in = s.h; break;
+    case MTP_FC1_SWIGLU: out = 2LL * s.fl; in = s.h; break;
     case MTP_PROJ: out = s.h; in = s.hl; break;
-    case MTP_FC2: out = s.h; in = s.fl; break;
+    case MTP_FC2: case MTP_FC2_SWIGLU: out = s.h; in = s.fl; break;
     default: return MTP_ERR_INVALID_ARG;
   }
+  // FC2 after SwiGLU: the data gradient is the interleaved [dgate | dup]
+  const bool dswiglu = kind == MTP_FC2_SWIGLU && preact != nullptr;
   if (!ok_ptr(dy_scale) || !ok_opt(dx) || !ok_opt(dw) || !ok_opt(preact)) return MTP_ERR_INVALID_ARG;
-  if (preact && kind != MTP_FC2) return MTP_ERR_INVALID_ARG;
+  if (preact && kind != MTP_FC2 && kind != MTP_FC2_SWIGLU) return MTP_ERR_INVALID_ARG;
   if (!ok_opt(dx_amax_parts) || (dx_amax_parts && (!dx || !preact))) return MTP_ERR_INVALID_ARG;
   if (dx && (!ok_ptr(dy8) || !ok_ptr(w8_t) || !ok_ptr(w_scale))) return MTP_ERR_INVALID_ARG;
   if (dw && (!ok_ptr(dy8_t) || !ok_ptr(x8_t) || !ok_ptr(x_scale))) return MTP_ERR_INVALID_ARG;
@@ -588,9 +596,9 @@ int mtp_linear_bwd_fp8(const mtp_shard_desc* desc, int kind, const uint8_t* dy8,
     g.A = dy8; g.lda = out; g.a_kmajor = true;
     g.B = w8_t; g.ldb = out; g.b_kmajor = true;
     g.M = static_cast<int>(s.T); g.N = static_cast<int>(in); g.K = static_cast<int>(out);
-    g.C = dx; g.ldc = in;
-    g.aux = const_cast<void*>(preact); g.ld_aux = in;
-    g.epi = preact ? mtp::kEpiDGelu : mtp::kEpiStore;
+    g.C = dx; g.ldc = dswiglu ? 2 * in : in;
+    g.aux = const_cast<void*>(preact); g.ld_aux = dswiglu ? 2 * in : in;
+    g.epi = dswiglu ? mtp::kEpiDSwiGLU : preact ? mtp::kEpiDGelu : mtp::kEpiStore;
     g.fp8 = true; g.a_e5m2 = true; g.scale_a = dy_scale; g.scale_b = w_scale;
     g.amax = dx_amax_parts;
     if (mtp::gemm_bf16(g, str) != hipSuccess) return MTP_ERR_HIP;

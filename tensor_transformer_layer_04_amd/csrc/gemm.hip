@@ -230,8 +230,8 @@ __device__ __forceinline__ bf16x8 frag_m(const char* t, int rb, int kk, int lane
   return cat_bf16x8(lo, hi);
 }
 
-// AMAX: mx also takes the largest |value| stored to C (GeLU and GeLU'
-// epilogues).
+// AMAX: mx also takes the largest |value| stored to C (GeLU, GeLU' and
+// SwiGLU' epilogues).
 template <int EPI, typename ElemT, bool AMAX = false>
 __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, float v[4],
                                           float& mx) {
@@ -278,6 +278,10 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
       dup[c] = v[c] * gt[c] * sg;
       dgate[c] = v[c] * up[c] * sg * fmaf(gt[c], 1.0f - sg, 1.0f);
     }
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fmaxf(fabsf(dgate[c]), fabsf(dup[c])));
+    }
     ElemT* o = static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + 2 * n;
     store4(o, dgate);
     store4(o + 4, dup);
@@ -296,15 +300,20 @@ __device__ __forceinline__ void epi_apply(const GemmParams& p, int m, int n, flo
 // SwiGLU forward epilogue of columns n..n+3 (n % 4 == 0) of the interleaved
 // gate|up product: v holds them, pv the partner group (n ^ 4).  Both lanes
 // store their group as the pre-activation; the gate lane (n % 8 == 0)
-// writes SiLU(gate) * up to output columns n/2 .. n/2+3.
-template <typename ElemT>
+// writes SiLU(gate) * up to output columns n/2 .. n/2+3 (AMAX: and takes
+// their largest |value| into mx).
+template <typename ElemT, bool AMAX = false>
 __device__ __forceinline__ void epi_swiglu(const GemmParams& p, int m, int n, const float v[4],
-                                           const float pv[4]) {
+                                           const float pv[4], float& mx) {
   store4(static_cast<ElemT*>(p.aux) + static_cast<int64_t>(m) * p.ld_aux + n, v);
   if ((n & 4) == 0) {
     float o[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[c] = v[c] * silu_sigmoid(v[c]) * pv[c];
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(o[c]));
+    }
     store4(static_cast<ElemT*>(p.C) + static_cast<int64_t>(m) * p.ldc + n / 2, o);
   }
 }
@@ -346,7 +355,7 @@ __device__ __forceinline__ void epi_block(const GemmParams& p, float* stage, con
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb + 8 * r + sr;
-      if (m < p.M && n < p.N) epi_swiglu<bf16_t>(p, m, n, v[r], pv[r]);
+      if (m < p.M && n < p.N) epi_swiglu<bf16_t, AMAX>(p, m, n, v[r], pv[r], mx);
     }
   } else {
 #pragma unroll
@@ -622,11 +631,12 @@ gemm_bf16_kernel(GemmParams p) {
                    : (wave / kPerBuf) == 1 ? lds_a1
                    : (wave / kPerBuf) == 2 ? lds_b0 : lds_b1;
   float* stage = reinterpret_cast<float*>(base + (wave % kPerBuf) * kRegion);
-  // FP8 GeLU / GeLU' outputs feed the next quantization: the partial
-  // maximum of what this workgroup stores, in the form of the amax pass
-  // (slot blockIdx.x, unused slots 0; rounded to bf16 like the values,
-  // which keeps the order)
-  constexpr bool kAmax = F8 && (EPI == kEpiGelu || EPI == kEpiDGelu);
+  // FP8 GeLU / SwiGLU outputs and their gradients feed the next
+  // quantization: the partial maximum of what this workgroup stores, in
+  // the form of the amax pass (slot blockIdx.x, unused slots 0; rounded to
+  // bf16 like the values, which keeps the order)
+  constexpr bool kAmax = F8 && (EPI == kEpiGelu || EPI == kEpiDGelu || EPI == kEpiSwiGLU ||
+                                EPI == kEpiDSwiGLU);
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -819,7 +829,8 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmParams p, const float
       float pv[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) pv[c] = __shfl_xor(acc[i][c], 1);
-      if (m < p.M && n < p.N) epi_swiglu<float>(p, m, n, acc[i], pv);
+      float unused = 0.0f;
+      if (m < p.M && n < p.N) epi_swiglu<float>(p, m, n, acc[i], pv, unused);
     } else {
       float unused = 0.0f;
       if (m < p.M && n < p.N) epi_apply<EPI, float>(p, m, n, acc[i], unused);
@@ -866,13 +877,16 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.fp8) {
     // bytes staged as bf16 pairs: K and the leading dimensions in 2-byte units
-    // forward (E4M3 A): Store, Gelu; data gradient (E5M2 A): Store, DGelu;
-    // weight gradient (E5M2 A): F32, F32Acc
+    // forward (E4M3 A): Store, Gelu, SwiGLU; data gradient (E5M2 A): Store,
+    // DGelu, DSwiGLU; weight gradient (E5M2 A): F32, F32Acc
     const bool ok_epi = g.a_e5m2 ? (g.epi == kEpiStore || g.epi == kEpiDGelu ||
-                                    g.epi == kEpiF32 || g.epi == kEpiF32Acc)
-                                 : (g.epi == kEpiStore || g.epi == kEpiGelu);
+                                    g.epi == kEpiDSwiGLU || g.epi == kEpiF32 ||
+                                    g.epi == kEpiF32Acc)
+                                 : (g.epi == kEpiStore || g.epi == kEpiGelu ||
+                                    g.epi == kEpiSwiGLU);
+    // SwiGLU pairs the gate and up groups of 4 columns within 8
     if (!g.a_kmajor || !g.b_kmajor || (g.K & 15) || (g.lda & 15) || (g.ldb & 15) || (g.N & 3) ||
-        !g.scale_a || !g.scale_b || !ok_epi)
+        (g.epi == kEpiSwiGLU && (g.N & 7)) || !g.scale_a || !g.scale_b || !ok_epi)
       return hipErrorInvalidValue;
     GemmDesc h = g;
     h.K = g.K / 2; h.lda = g.lda / 2; h.ldb = g.ldb / 2;
@@ -886,8 +900,12 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     // the epilogue writes the amax parts of C when its grid fits them,
     // otherwise a pass over C does
     bool amax_pass = false;
+    // columns of C: SwiGLU halves the product's, SwiGLU' doubles them
+    const int64_t c_cols = g.epi == kEpiSwiGLU ? g.N / 2 : g.epi == kEpiDSwiGLU ? 2LL * g.N : g.N;
     if (g.amax) {
-      if ((g.epi != kEpiGelu && g.epi != kEpiDGelu) || g.ldc != g.N) return hipErrorInvalidValue;
+      if ((g.epi != kEpiGelu && g.epi != kEpiDGelu && g.epi != kEpiSwiGLU &&
+           g.epi != kEpiDSwiGLU) || g.ldc != c_cols)
+        return hipErrorInvalidValue;
       const int bm = tile == kTile256x128 || tile == kTileF8_256x192 ? 256 : 128;
       const int bn = tile == kTile256x128 || tile == kTile128x128 ? 128
                      : tile == kTileF8_256x192 ? 192 : 256;
@@ -897,18 +915,22 @@ hipError_t gemm_bf16(const GemmDesc& g, hipStream_t s) {
     }
     hipError_t e;
     if (!g.a_e5m2) {
-      e = g.epi == kEpiGelu ? dispatch_fp8<kEpiGelu, false>(p, tile, s)
-                            : dispatch_fp8<kEpiStore, false>(p, tile, s);
+      switch (g.epi) {
+        case kEpiGelu: e = dispatch_fp8<kEpiGelu, false>(p, tile, s); break;
+        case kEpiSwiGLU: e = dispatch_fp8<kEpiSwiGLU, false>(p, tile, s); break;
+        default: e = dispatch_fp8<kEpiStore, false>(p, tile, s); break;
+      }
     } else {
       switch (g.epi) {
         case kEpiStore: e = dispatch_fp8<kEpiStore, true>(p, tile, s); break;
         case kEpiDGelu: e = dispatch_fp8<kEpiDGelu, true>(p, tile, s); break;
+        case kEpiDSwiGLU: e = dispatch_fp8<kEpiDSwiGLU, true>(p, tile, s); break;
         case kEpiF32: e = dispatch_fp8<kEpiF32, true>(p, tile, s); break;
         default: e = dispatch_fp8<kEpiF32Acc, true>(p, tile, s); break;
       }
     }
     if (e != hipSuccess || !amax_pass) return e;
-    return fp8_amax(g.C, static_cast<int64_t>(g.M) * g.N, g.amax, s);
+    return fp8_amax(g.C, static_cast<int64_t>(g.M) * c_cols, g.amax, s);
   }
   GemmParams p = to_params(g);
   // Buffer offsets are 32-bit and the edge handling needs every valid byte

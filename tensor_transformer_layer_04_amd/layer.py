@@ -46,7 +46,10 @@ row-major ones).  A tensor split over the ranks (a weight shard, ctx_r, g_r,
 du_r, dqkv_r) is scaled by the maximum over every rank's amax, as the ranks
 of a tensor-parallel group would agree on it; the step therefore runs phase
 by phase over the ranks (all ranks' amax, then their codes), and ranks not
-computed here contribute their amax parts through ``external``.
+computed here contribute their amax parts through ``external``.  With the
+SwiGLU FFN the gate and up rows of W1|W3 are one tensor under one scale, and
+so are their output gradients [du | du3], both in the interleaved order the
+bf16 step uses.
 """
 from __future__ import annotations
 
@@ -219,8 +222,8 @@ class TPLayer(_Probed):
                           for r in range(cfg.tp)}
         self.fp8 = bool(getattr(cfg, "fp8", False))
         if self.fp8:
-            if cfg.dtype != "bf16" or self.swiglu or self.sp or self.cp > 1:
-                raise ValueError("the FP8 step needs a bf16 GeLU layer without sequence or "
+            if cfg.dtype != "bf16" or self.sp or self.cp > 1:
+                raise ValueError("the FP8 step needs a bf16 layer without sequence or "
                                  "context parallelism")
             if self.T % 16:
                 raise ValueError(f"the FP8 step needs T ({self.T}) divisible by 16")
@@ -282,6 +285,9 @@ class TPLayer(_Probed):
         cfg, T, dev = self.cfg, self.T, self.device
         h, t = cfg.hidden, cfg.tp
         hl, fl = h // t, cfg.ffn // t
+        # SwiGLU: gate and up rows (and their output gradients) are one
+        # tensor under one scale, in the interleaved order of the bf16 step
+        ul = 2 * fl if self.swiglu else fl
 
         def slot(rows, cols):
             return {"q": torch.empty(rows, cols, dtype=torch.uint8, device=dev),
@@ -291,8 +297,8 @@ class TPLayer(_Probed):
                     "rows": rows, "cols": cols}
         # replicated inputs (one quantization serves every rank)
         self.q8 = {k: slot(T, h) for k in ("ln1", "ln2", "dy", "dy1")}
-        shapes = {"ctx": (T, hl), "g": (T, fl), "du": (T, fl), "dqkv": (T, 3 * hl),
-                  "wqkv": (3 * hl, h), "wo": (h, hl), "w1": (fl, h), "w2": (h, fl)}
+        shapes = {"ctx": (T, hl), "g": (T, fl), "du": (T, ul), "dqkv": (T, 3 * hl),
+                  "wqkv": (3 * hl, h), "wo": (h, hl), "w1": (ul, h), "w2": (h, fl)}
         self.r8 = {r: {k: slot(*sh) for k, sh in shapes.items()} for r in self.ranks}
 
     def _quant_shared(self, name, x, fmt, amax_written=False):
@@ -569,8 +575,8 @@ class TPLayer(_Probed):
         for r in self.ranks:
             w, a, c = self.w[r], self.a[r], r8[r]
             with T("fc1_fwd"):
-                mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_FC1, q8["ln2"]["q"], q8["ln2"]["s"],
-                                       c["w1"]["q"], c["w1"]["s"], w["b1"], a["g"], a["u"],
+                mtp.mtp_linear_fwd_fp8(self.descs[r], self.k_fc1, q8["ln2"]["q"], q8["ln2"]["s"],
+                                       c["w1"]["q"], c["w1"]["s"], w.get("b1"), a["g"], a["u"],
                                        amax_parts=c["g"]["amax"])
         with T("quant"):
             self._quant_split("g", {r: self.a[r]["g"] for r in self.ranks}, E4, ext,
@@ -579,7 +585,7 @@ class TPLayer(_Probed):
         for r in self.ranks:
             c = r8[r]
             with T("fc2_fwd"):
-                mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_FC2, c["g"]["q"], c["g"]["s"],
+                mtp.mtp_linear_fwd_fp8(self.descs[r], self.k_fc2, c["g"]["q"], c["g"]["s"],
                                        c["w2"]["q"], c["w2"]["s"], None, self.a[r]["q"], None)
         parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
         with T("sum_fc2"):
@@ -602,18 +608,19 @@ class TPLayer(_Probed):
             return torch.cuda.stream(side) if side is not None else contextlib.nullcontext()
 
         self.dy_seen = dy
-        # FC2: du = (dy W2) * GeLU'(u); dW2 = dy^T g
+        # FC2: du = (dy W2) * GeLU'(u) (SwiGLU: the interleaved gate and up
+        # gradients); dW2 = dy^T g
         with T("quant"):
             self._quant_shared("dy", dy, E5)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
             with T("fc2_dgrad"):
-                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, q8["dy"]["q"], None, q8["dy"]["s"],
+                mtp.mtp_linear_bwd_fp8(d, self.k_fc2, q8["dy"]["q"], None, q8["dy"]["s"],
                                        c["w2"]["qt"], c["w2"]["s"], None, None, a["u"], a["du"],
                                        None, dx_amax_parts=c["du"]["amax"])
             with on_side(), T("fc2_wgrad", side):
-                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, None, q8["dy"]["qt"], q8["dy"]["s"], None,
+                mtp.mtp_linear_bwd_fp8(d, self.k_fc2, None, q8["dy"]["qt"], q8["dy"]["s"], None,
                                        None, c["g"]["qt"], c["g"]["s"], None, None, g["dw2"])
             if r == self.owns_bias:
                 with on_side(), T("fc2_bias", side):
@@ -627,12 +634,13 @@ class TPLayer(_Probed):
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
             with on_side(), T("fc1_wgrad", side):
-                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC1, None, c["du"]["qt"], c["du"]["s"], None,
+                mtp.mtp_linear_bwd_fp8(d, self.k_fc1, None, c["du"]["qt"], c["du"]["s"], None,
                                        None, q8["ln2"]["qt"], q8["ln2"]["s"], None, None, g["dw1"])
-                mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, None,
-                                       g["db1"], 0, wss, wsb)
+                if not self.swiglu:
+                    mtp.mtp_col_linear_bwd(d, mtp.MTP_FC1, a["du"], self.ln2, w["w1"], None, None,
+                                           g["db1"], 0, wss, wsb)
             with T("fc1_dgrad"):
-                mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC1, c["du"]["q"], None, c["du"]["s"],
+                mtp.mtp_linear_bwd_fp8(d, self.k_fc1, c["du"]["q"], None, c["du"]["s"],
                                        c["w1"]["qt"], c["w1"]["s"], None, None, None, a["dln2"],
                                        None)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))

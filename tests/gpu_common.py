@@ -259,11 +259,24 @@ def compare_fp8_components(cfg, L, report):
         u = oracle.to64(cpu(a["u"]))
         check(f"r{r}.fp8_qkv", cpu(a["qkv"]), f8.fp8_linear(*ln1, qwqkv, swqkv, oracle.to64(w["bqkv"].cpu())), tol, report)
         check(f"r{r}.fp8_proj", cpu(a["p"]), f8.fp8_linear(qctx, sctx, qwo, swo), tol, report)
-        uref = f8.fp8_linear(*ln2, qw1, sw1, oracle.to64(w["b1"].cpu()))
-        check(f"r{r}.fp8_u", cpu(a["u"]), uref, tol, report)
-        check(f"r{r}.fp8_g", cpu(a["g"]), oracle.gelu_tanh(uref), tol, report)
+        if getattr(cfg, "swiglu", False):
+            # gate|up interleaved in groups of 4 columns (rows of W1|W3)
+            from tensor_transformer_layer_04_amd.layer import swiglu_split
+            uref = f8.fp8_linear(*ln2, qw1, sw1)
+            check(f"r{r}.fp8_u", cpu(a["u"]), uref, tol, report)
+            gt, up = (oracle.to64(t) for t in swiglu_split(torch.from_numpy(u), 1))
+            gr_, ur_ = (t.numpy() for t in swiglu_split(torch.from_numpy(uref), 1))
+            check(f"r{r}.fp8_g", cpu(a["g"]), oracle.silu(gr_) * ur_, tol, report)
+            dg = f8.fp8_dgrad(*dy, qw2, sw2)
+            dgate, dup = (t.float() for t in swiglu_split(cpu(a["du"]), 1))
+            check(f"r{r}.fp8_dgate", dgate, dg * up * oracle.silu_grad(gt), tol, report)
+            check(f"r{r}.fp8_dup", dup, dg * oracle.silu(gt), tol, report)
+        else:
+            uref = f8.fp8_linear(*ln2, qw1, sw1, oracle.to64(w["b1"].cpu()))
+            check(f"r{r}.fp8_u", cpu(a["u"]), uref, tol, report)
+            check(f"r{r}.fp8_g", cpu(a["g"]), oracle.gelu_tanh(uref), tol, report)
+            check(f"r{r}.fp8_du", cpu(a["du"]), f8.fp8_dgrad(*dy, qw2, sw2) * oracle.gelu_tanh_grad(u), tol, report)
         check(f"r{r}.fp8_fc2", cpu(a["q"]), f8.fp8_linear(qg, sg, qw2, sw2), tol, report)
-        check(f"r{r}.fp8_du", cpu(a["du"]), f8.fp8_dgrad(*dy, qw2, sw2) * oracle.gelu_tanh_grad(u), tol, report)
         check(f"r{r}.fp8_dw2", cpu(gr["dw2"]), f8.fp8_wgrad(*dy, qg, sg), tol, report)
         check(f"r{r}.fp8_dln2", cpu(a["dln2"]), f8.fp8_dgrad(qdu, sdu, qw1, sw1), tol, report)
         check(f"r{r}.fp8_dw1", cpu(gr["dw1"]), f8.fp8_wgrad(qdu, sdu, *ln2), tol, report)

@@ -217,8 +217,8 @@ def test_fp8_entry_points_refuse_bad_arguments():
     contract excludes with the documented status, before any launch: fp32
     shards, formats and kinds outside the enums, widths that are not whole
     16-byte chunks, reduction lengths that are not multiples of 16, missing
-    operands of a requested product, a bias on a row-parallel map, and the
-    GeLU derivative on anything but FC2."""
+    operands of a requested product, a bias on a row-parallel or SwiGLU map,
+    and the activation derivative on anything but FC2 / FC2_SWIGLU."""
     lib = mtp.lib()
     d = valid()
     bd = ctypes.byref(d)
@@ -261,6 +261,16 @@ def test_fp8_entry_points_refuse_bad_arguments():
     assert fwd(mtp.MTP_FC1, pre=FAKE, am=FAKE + 4) == I
     odd = valid(ffn=2000)                            # f_l = 1000: 8 but not 16 bytes of codes
     assert fwd(mtp.MTP_FC2, dd=ctypes.byref(odd)) == U
+    assert fwd(mtp.MTP_FC2_SWIGLU, dd=ctypes.byref(odd)) == U
+    # SwiGLU: the interleaved gate|up product is written, there is no bias,
+    # and gate and up pair up in groups of 4 columns
+    assert fwd(mtp.MTP_FC1_SWIGLU) == I
+    assert fwd(mtp.MTP_FC1_SWIGLU, pre=FAKE, b=FAKE) == I
+    assert fwd(mtp.MTP_FC2_SWIGLU, b=FAKE) == I
+    assert fwd(mtp.MTP_FC2_SWIGLU, am=FAKE) == I
+    assert fwd(mtp.MTP_FC1_SWIGLU, pre=FAKE, am=FAKE + 4) == I
+    unpaired = valid(ffn=2004)                       # f_l = 1002: 2 f_l = 2004 not a multiple of 8
+    assert fwd(mtp.MTP_FC1_SWIGLU, pre=FAKE, dd=ctypes.byref(unpaired)) == U
     # backward: data gradient (dy8, W^T codes) and/or weight gradient (dy^T, x^T codes)
     bwd = lambda kind, dy8=FAKE, dyt=FAKE, w8t=FAKE, x8t=FAKE, pre=None, dx=FAKE, dw=FAKE, dd=bd, \
         am=None: lib.mtp_linear_bwd_fp8(dd, kind, dy8, dyt, FAKE, w8t, FAKE, x8t, FAKE, pre, dx, dw,
@@ -275,6 +285,11 @@ def test_fp8_entry_points_refuse_bad_arguments():
     assert bwd(mtp.MTP_FC2, dyt=None) == I
     assert bwd(mtp.MTP_FC2, x8t=None) == I
     assert bwd(mtp.MTP_FC1, dd=ctypes.byref(odd), dw=None) == U   # data gradient reduces over f_l
+    assert bwd(mtp.MTP_FC1_SWIGLU, pre=FAKE) == I    # SwiGLU' belongs to FC2_SWIGLU
+    assert bwd(mtp.MTP_FC2_SWIGLU, am=FAKE) == I
+    assert bwd(mtp.MTP_FC2_SWIGLU, pre=FAKE, am=FAKE + 4) == I
+    # the SwiGLU data gradient reduces over 2 f_l = 2004
+    assert bwd(mtp.MTP_FC1_SWIGLU, dd=ctypes.byref(unpaired), dw=None) == U
     ragged = valid(seq_len=2004)                     # weight gradient reduces over T
     assert bwd(mtp.MTP_QKV, dd=ctypes.byref(ragged), dx=None) == U
 

@@ -305,55 +305,132 @@ def test_fp8_backward_gemms_7b_shard(T):
     log(f"fp8 backward GEMMs T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
 @pytest.mark.parametrize("T", [2048, 304, 16384])
-def test_amax_parts_from_fp8_gemm_epilogues(T):
-    """The FC1 forward (GeLU output g) and the FC2 data gradient (du, with
-    the GeLU derivative) write the amax parts of their bf16 output when
-    asked: the outputs are those of the calls without parts, the largest
-    part is the largest |value| stored, every slot is written, and the codes
-    made from the parts equal those of a separate amax pass bit for bit.
-    T = 16384 gives the FC1 GEMM more tiles than parts (the pass over the
-    output then writes them)."""
+def test_amax_parts_from_fp8_gemm_epilogues(T, act):
+    """The FC1 forward (GeLU output g, or SiLU(gate) * up of the interleaved
+    gate|up product) and the FC2 data gradient (du with the GeLU derivative,
+    or the interleaved gate and up gradients) write the amax parts of their
+    bf16 output when asked: the outputs are those of the calls without
+    parts, the largest part is the largest |value| stored, every slot is
+    written, and the codes made from the parts equal those of a separate
+    amax pass bit for bit.  T = 16384 gives the FC1 GEMM more tiles than
+    parts (the pass over the output then writes them)."""
+    require_gpu()
+    from tensor_transformer_layer_04_amd import mtp
+    h, a, f, tp = 4096, 32, 11008, 2
+    fl = f // tp
+    sw = act == "swiglu"
+    ul = 2 * fl if sw else fl    # width of the FC1 product and of its gradient
+    k_fc1, k_fc2 = ((mtp.MTP_FC1_SWIGLU, mtp.MTP_FC2_SWIGLU) if sw else
+                    (mtp.MTP_FC1, mtp.MTP_FC2))
+    d = mtp.make_desc(h, a, f, tp, 0, T, 1, mtp.MTP_BF16)
+    x, w1 = _bf16((T, h), 150), _bf16((ul, h), 151, 0.02)
+    b1 = None if sw else _bf16((fl,), 152, 0.1).cuda()
+    dy, w2, u = _bf16((T, h), 153, 1e-3), _bf16((h, fl), 154, 0.02), _bf16((T, ul), 155)
+    (xq, _, xs), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [x.cuda()])
+    (w1q, _, w1s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w1.cuda()])
+    (dq, _, ds), = _amax_and_quant(d, mtp.MTP_FP8_E5M2, [dy.cuda()])
+    (_, w2qt, w2s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w2.cuda()])
+    u = u.cuda()
+    P = lambda: torch.full((mtp.FP8_AMAX_PARTS,), 1e30, dtype=torch.float32, device="cuda")
+    E = lambda c: torch.empty(T, c, dtype=torch.bfloat16, device="cuda")
+    g0, g1, u0, u1, p_g = E(fl), E(fl), E(ul), E(ul), P()
+    mtp.mtp_linear_fwd_fp8(d, k_fc1, xq, xs, w1q, w1s, b1, g0, u0)
+    mtp.mtp_linear_fwd_fp8(d, k_fc1, xq, xs, w1q, w1s, b1, g1, u1, amax_parts=p_g)
+    du0, du1, p_du = E(ul), E(ul), P()
+    mtp.mtp_linear_bwd_fp8(d, k_fc2, dq, None, ds, w2qt, w2s, None, None, u, du0, None)
+    mtp.mtp_linear_bwd_fp8(d, k_fc2, dq, None, ds, w2qt, w2s, None, None, u, du1, None,
+                           dx_amax_parts=p_du)
+    torch.cuda.synchronize()
+    assert torch.equal(g0, g1) and torch.equal(u0, u1) and torch.equal(du0, du1)
+    for name, y, p, fmt in (("g", g1, p_g, mtp.MTP_FP8_E4M3), ("du", du1, p_du, mtp.MTP_FP8_E5M2)):
+        cols = y.shape[1]
+        ref = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
+        mtp.mtp_fp8_amax(d, y, y.numel(), ref)
+        torch.cuda.synchronize()
+        want = float(y.float().abs().max())
+        log(f"fp8 GEMM amax parts {act} {name} T={T}: fused {float(p.max())!r} separate "
+            f"{float(ref.max())!r} max|y| {want!r}")
+        assert float(p.max()) == want == float(ref.max()) and float(p.min()) >= 0.0
+        codes = []
+        for pp in (p, ref):
+            q = torch.empty(T, cols, dtype=torch.uint8, device="cuda")
+            qt = torch.empty(cols, T, dtype=torch.uint8, device="cuda")
+            s = torch.empty(1, dtype=torch.float32, device="cuda")
+            mtp.mtp_fp8_quantize(d, fmt, y, T, cols, [pp], q, qt, s)
+            codes.append((q, qt, s))
+        torch.cuda.synchronize()
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(*codes))
+
+
+def _gate_up(z):
+    """(gate, up) halves of columns interleaved in groups of 4."""
+    r = z.shape[0]
+    v = z.reshape(r, -1, 2, 4)
+    return v[:, :, 0].reshape(r, -1), v[:, :, 1].reshape(r, -1)
+
+
+def _interleave(gate, up):
+    r = gate.shape[0]
+    return np.stack([gate.reshape(r, -1, 4), up.reshape(r, -1, 4)], 2).reshape(r, -1)
+
+
+@pytest.mark.parametrize("T", [2048, 304])
+def test_fp8_swiglu_maps_7b_shard(T):
+    """The SwiGLU FFN on FP8 codes at the 7B TP=2 shard shapes (f_l = 5504;
+    gate and up rows interleaved in groups of 4 under one scale), against
+    the oracle's FP8 products of the same codes: the forward's interleaved
+    pre-activation and SiLU(gate) * up, the FC2 data gradient's interleaved
+    gate and up gradients (sampled rows), and the FC1 data gradient (sampled
+    rows) and weight gradient (every element) over the interleaved width."""
     require_gpu()
     from tensor_transformer_layer_04_amd import mtp
     h, a, f, tp = 4096, 32, 11008, 2
     fl = f // tp
     d = mtp.make_desc(h, a, f, tp, 0, T, 1, mtp.MTP_BF16)
-    x, w1, b1 = _bf16((T, h), 150), _bf16((fl, h), 151, 0.02), _bf16((fl,), 152, 0.1)
-    dy, w2, u = _bf16((T, h), 153, 1e-3), _bf16((h, fl), 154, 0.02), _bf16((T, fl), 155)
-    (xq, _, xs), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [x.cuda()])
-    (w1q, _, w1s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w1.cuda()])
+    tol = TOL["bf16"]
+    rows = np.unique(np.concatenate([np.random.default_rng(T + 7).choice(T, 24, replace=False),
+                                     [0, T - 1]]))
+    report = {}
+    x, w13 = _bf16((T, h), 170), _bf16((2 * fl, h), 171, 0.02)
+    dy, w2 = _bf16((T, h), 172, 1e-3), _bf16((h, fl), 173, 0.02)
+    (xq, xqt, xs), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [x.cuda()])
+    (wq, wqt, wsc), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w13.cuda()])
     (dq, _, ds), = _amax_and_quant(d, mtp.MTP_FP8_E5M2, [dy.cuda()])
     (_, w2qt, w2s), = _amax_and_quant(d, mtp.MTP_FP8_E4M3, [w2.cuda()])
-    b1, u = b1.cuda(), u.cuda()
-    P = lambda: torch.full((mtp.FP8_AMAX_PARTS,), 1e30, dtype=torch.float32, device="cuda")
-    E = lambda: torch.empty(T, fl, dtype=torch.bfloat16, device="cuda")
-    g0, g1, u0, u1, p_g = E(), E(), E(), E(), P()
-    mtp.mtp_linear_fwd_fp8(d, mtp.MTP_FC1, xq, xs, w1q, w1s, b1, g0, u0)
-    mtp.mtp_linear_fwd_fp8(d, mtp.MTP_FC1, xq, xs, w1q, w1s, b1, g1, u1, amax_parts=p_g)
-    du0, du1, p_du = E(), E(), P()
-    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, dq, None, ds, w2qt, w2s, None, None, u, du0, None)
-    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2, dq, None, ds, w2qt, w2s, None, None, u, du1, None,
-                           dx_amax_parts=p_du)
+    u = torch.empty(T, 2 * fl, dtype=torch.bfloat16, device="cuda")
+    g = torch.empty(T, fl, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_linear_fwd_fp8(d, mtp.MTP_FC1_SWIGLU, xq, xs, wq, wsc, None, g, u)
+    du = torch.empty(T, 2 * fl, dtype=torch.bfloat16, device="cuda")
+    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC2_SWIGLU, dq, None, ds, w2qt, w2s, None, None, u, du,
+                           None)
     torch.cuda.synchronize()
-    assert torch.equal(g0, g1) and torch.equal(u0, u1) and torch.equal(du0, du1)
-    for name, y, p, fmt in (("g", g1, p_g, mtp.MTP_FP8_E4M3), ("du", du1, p_du, mtp.MTP_FP8_E5M2)):
-        ref = torch.empty(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device="cuda")
-        mtp.mtp_fp8_amax(d, y, y.numel(), ref)
-        torch.cuda.synchronize()
-        want = float(y.float().abs().max())
-        log(f"fp8 GEMM amax parts {name} T={T}: fused {float(p.max())!r} separate "
-            f"{float(ref.max())!r} max|y| {want!r}")
-        assert float(p.max()) == want == float(ref.max()) and float(p.min()) >= 0.0
-        codes = []
-        for pp in (p, ref):
-            q = torch.empty(T, fl, dtype=torch.uint8, device="cuda")
-            qt = torch.empty(fl, T, dtype=torch.uint8, device="cuda")
-            s = torch.empty(1, dtype=torch.float32, device="cuda")
-            mtp.mtp_fp8_quantize(d, fmt, y, T, fl, [pp], q, qt, s)
-            codes.append((q, qt, s))
-        torch.cuda.synchronize()
-        assert all(torch.equal(a_, b_) for a_, b_ in zip(*codes))
+    q_x, s_x = ofp8.quantize_per_tensor(x.float().numpy(), "e4m3")
+    q_w, s_w = ofp8.quantize_per_tensor(w13.float().numpy(), "e4m3")
+    q_dy, s_dy = ofp8.quantize_per_tensor(dy.float().numpy(), "e5m2")
+    q_w2, s_w2 = ofp8.quantize_per_tensor(w2.float().numpy(), "e4m3")
+    uref = ofp8.fp8_linear(q_x[rows], s_x, q_w, s_w)
+    check("fc1_swiglu.u", u[rows].float().cpu(), uref, tol, report)
+    gt, up = _gate_up(uref)
+    check("fc1_swiglu.g", g[rows].float().cpu(), oracle.silu(gt) * up, tol, report)
+    # the derivative at the pre-activation the GPU stored (bf16)
+    gt, up = _gate_up(oracle.to64(u[rows].cpu()))
+    dg = ofp8.fp8_dgrad(q_dy[rows], s_dy, q_w2, s_w2)
+    ref_du = _interleave(dg * up * oracle.silu_grad(gt), dg * oracle.silu(gt))
+    check("fc2_swiglu.du", du[rows].float().cpu(), ref_du, tol, report)
+    # FC1 backward over the interleaved width, from the codes of du
+    (dq13, dqt13, ds13), = _amax_and_quant(d, mtp.MTP_FP8_E5M2, [du])
+    dx = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(2 * fl, h, dtype=torch.float32, device="cuda")
+    mtp.mtp_linear_bwd_fp8(d, mtp.MTP_FC1_SWIGLU, dq13, dqt13, ds13, wqt, wsc, xqt, xs, None, dx,
+                           dw)
+    torch.cuda.synchronize()
+    q_du, s_du = ofp8.quantize_per_tensor(du.float().cpu().numpy(), "e5m2")
+    check("fc1_swiglu.dx", dx[rows].float().cpu(), ofp8.fp8_dgrad(q_du[rows], s_du, q_w, s_w), tol,
+          report)
+    check("fc1_swiglu.dw", dw.cpu(), ofp8.fp8_wgrad(q_du, s_du, q_x, s_x), 1e-4, report)
+    log(f"fp8 SwiGLU maps T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
 
 @pytest.mark.parametrize("T,docs", [(2048, None), (304, None), (8192, None), (2048, [0, 700, 1500, 2048])])
