@@ -94,19 +94,20 @@ def source_digest() -> str:
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch from the committed counter runs, if they were
-    taken on the current kernel source (null otherwise)."""
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch of a GEMM family in a workload from the committed
+    counter runs, if they were taken on the current kernel source and on
+    that workload (null otherwise)."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if t.get("gemm_source_sha") != source_digest():
         return None
-    return t.get("bytes_per_launch", {}).get(kernel)
+    return t.get("workloads", {}).get(workload, {}).get("bytes_per_launch", {}).get(kernel)
 
 
-def roofline(kernel, tags, probes, flops, ms, steps, peak=None) -> dict:
+def roofline(kernel, tags, probes, flops, ms, steps, workload, peak=None) -> dict:
     """Roofline entry of one GEMM family: model flops of its probed launches
     over their summed HIP-event durations (``steps``: the probed steps)."""
     dur_ms = sum(a.elapsed_time(b) for t in tags for a, b in probes[t])
@@ -121,7 +122,7 @@ def roofline(kernel, tags, probes, flops, ms, steps, peak=None) -> dict:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": traffic_for(kernel),
+        "traffic": traffic_for(kernel, workload),
         "launches_per_step": launches // max(steps, 1),
         "avg_launch_us": round(1e3 * dur_ms / max(launches, 1), 2),
         "share_of_step": round(dur_ms / (ms * steps), 4),
@@ -268,7 +269,8 @@ def fp8_gemm_probe(cfg, L, reps: int = 20) -> dict:
             "roofline": {"kernel": FP8_KERNEL,
                          "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
-                         "traffic": traffic_for(FP8_KERNEL)}}
+                         # the same four GEMMs as the FP8 step of this shard
+                         "traffic": traffic_for(FP8_KERNEL, cfg.name + "_fp8")}}
 
 
 def main(argv=None) -> int:
@@ -517,10 +519,10 @@ def main(argv=None) -> int:
             round(ms - 1e-3 * (call_us["sum_fc2"] + call_us["sum_proj_ln2"] - call_us["ln1"]), 4)
             if all(k in call_us for k in ("sum_fc2", "sum_proj_ln2", "ln1")) else None),
         "roofline": roofline(FP8_KERNEL if L.fp8 else FWD_KERNEL, FWD_TAGS, probes, fl["call"], ms,
-                             len(probed), PEAK_FP8_TFLOPS if L.fp8 else None),
+                             len(probed), cfg.name, PEAK_FP8_TFLOPS if L.fp8 else None),
         "roofline_wgrad_overlapped": roofline(FP8_WGRAD_KERNEL if L.fp8 else WGRAD_KERNEL,
                                               WGRAD_TAGS, probes, fl["call"], ms, len(probed),
-                                              PEAK_FP8_TFLOPS if L.fp8 else None),
+                                              cfg.name, PEAK_FP8_TFLOPS if L.fp8 else None),
     }
     if cfg.dtype == "bf16" and not cfg.swiglu and not L.fp8 and cfg.tokens % 8 == 0:
         # the same shard's forward GEMMs on the FP8 matrix cores (not part of the step)
