@@ -106,6 +106,51 @@ def test_bench_refuses_several_gpus():
     assert "one GPU" in (r.stdout + r.stderr)
 
 
+def test_bench_model_flops_closed_forms():
+    """The model FLOPs bench.py divides by: 2MNK per linear map and 4 d
+    flops per visible (query, key) pair and local head, forward; the
+    backward twice the forward.  At the 7B TP=2 shard (T = 2048, causal)
+    that is 322.1 GFLOP of forward GEMMs, 17.2 GFLOP of forward attention
+    and 1017.9 GFLOP per step; the SwiGLU FFN adds a third FFN matrix
+    (another 2 T h f_l per direction)."""
+    import bench
+    import synth
+    cfg = synth.get_config("7b_tp2")
+    T, h, hl, fl = 2048, 4096, 2048, 5504
+    cu = [0, T]
+    f = bench.shard_flops(cfg, cu)
+    gemm_fwd = 2 * T * hl * h * 3 + 2 * T * h * hl + 2 * 2 * T * h * fl
+    attn_fwd = 4 * 128 * 16 * (T * (T + 1) // 2)
+    assert f["gemm"] == 3 * gemm_fwd and round(gemm_fwd / 1e9, 1) == 322.1
+    assert f["attn"] == 3 * attn_fwd and round(attn_fwd / 1e9, 1) == 17.2
+    assert f["total"] == 3 * (gemm_fwd + attn_fwd) and round(f["total"] / 1e9, 1) == 1017.9
+    assert sum(f["call"][k] for k in ("qkv_fwd", "proj_fwd", "fc1_fwd", "fc2_fwd")) == gemm_fwd
+    sw = bench.shard_flops(synth.get_config("7b_tp2_swiglu_fp8"), cu)
+    assert sw["total"] - f["total"] == 3 * 2 * T * h * fl
+    assert sw["call"]["fc1_fwd"] == 2 * f["call"]["fc1_fwd"]
+    # a document split adds no pair across documents
+    assert bench.seq_pairs([0, 100, 300]) == 100 * 101 // 2 + 200 * 201 // 2
+
+
+def test_bench_traffic_only_for_measured_workloads(monkeypatch):
+    """The counter traffic bench.py reports is that of the workload and GEMM
+    family the committed counter runs measured, and null for any other
+    workload or once the GEMM source has changed."""
+    import json
+    import bench
+    t = json.load(open(bench.TRAFFIC_FILE))
+    assert t["gemm_source_sha"] == bench.source_digest(), "counter figures are stale"
+    for w, e in t["workloads"].items():
+        for k, v in e["bytes_per_launch"].items():
+            assert bench.traffic_for(k, w) == v
+            assert v >= e["algorithmic_bytes_per_launch"][k] > 0
+    assert bench.traffic_for(bench.FWD_KERNEL, "7b_tp2") is not None
+    assert bench.traffic_for(bench.FWD_KERNEL, "wide_tp8") is None
+    assert bench.traffic_for(bench.FP8_KERNEL, "7b_tp2") is None
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
+    assert bench.traffic_for(bench.FWD_KERNEL, "7b_tp2") is None
+
+
 def test_fp8_division_free_quotient_is_exact_on_every_bf16_pair(tmp_path):
     """The FP8 convert kernel forms fl32(x / s) as x * fl32(1/s) plus one FMA
     residual correction, with the sign of x, when s >= 2^-60.
