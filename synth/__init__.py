@@ -121,6 +121,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         swiglu=True, fp8=True,
         description="7B-style layer with a SwiGLU FFN, one TP=2 rank shard, its twelve GEMMs on "
                     "FP8 codes (gate and up under one scale), bf16 elsewhere"),
+    "7b_tp2_cp2_fp8": LayerConfig(
+        "7b_tp2_cp2_fp8", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        context_parallel=2, fp8=True,
+        description="7B-style layer, one TP=2 rank shard, 2-chunk context-parallel attention, its "
+                    "twelve GEMMs on FP8 codes, bf16 elsewhere"),
     "varlen_tp1": LayerConfig(
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
@@ -202,6 +207,14 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_fp8_swiglu_d64_tp4": LayerConfig(
         "small_fp8_swiglu_d64_tp4", hidden=512, heads=8, ffn=2176, tp=4, seq_len=208,
         dtype="bf16", swiglu=True, fp8=True),
+    # the FP8 step with context-parallel attention (chunks of 152 and 208
+    # tokens; packed documents cross the chunk edges in the second case)
+    "small_fp8_tp2_cp2": LayerConfig(
+        "small_fp8_tp2_cp2", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        affine_random=True, fp8=True, context_parallel=2),
+    "small_fp8_varlen_d64_cp3": LayerConfig(
+        "small_fp8_varlen_d64_cp3", hidden=512, heads=8, ffn=1376, tp=2, seq_len=624,
+        dtype="bf16", varlen_tokens=624, doc_min=1, doc_max=300, fp8=True, context_parallel=3),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

@@ -49,7 +49,8 @@ by phase over the ranks (all ranks' amax, then their codes), and ranks not
 computed here contribute their amax parts through ``external``.  With the
 SwiGLU FFN the gate and up rows of W1|W3 are one tensor under one scale, and
 so are their output gradients [du | du3], both in the interleaved order the
-bf16 step uses.
+bf16 step uses.  With context-parallel attention, ctx and dqkv come out of
+the chunks' block pairs and merges and take the amax pass.
 """
 from __future__ import annotations
 
@@ -222,9 +223,8 @@ class TPLayer(_Probed):
                           for r in range(cfg.tp)}
         self.fp8 = bool(getattr(cfg, "fp8", False))
         if self.fp8:
-            if cfg.dtype != "bf16" or self.sp or self.cp > 1:
-                raise ValueError("the FP8 step needs a bf16 layer without sequence or "
-                                 "context parallelism")
+            if cfg.dtype != "bf16" or self.sp:
+                raise ValueError("the FP8 step needs a bf16 layer without sequence parallelism")
             if self.T % 16:
                 raise ValueError(f"the FP8 step needs T ({self.T}) divisible by 16")
         self._alloc()
@@ -553,11 +553,15 @@ class TPLayer(_Probed):
         for r in self.ranks:
             a = self.a[r]
             with T("attn_fwd"):
-                mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu, self.n_seqs,
-                                 ctx_amax_parts=r8[r]["ctx"]["amax"])
+                if self.cp > 1:
+                    # the chunks' block pairs and merges: ctx's amax in a pass of its own
+                    self._attn_fwd_cp(self.descs[r], a)
+                else:
+                    mtp.mtp_attn_fwd(self.descs[r], a["qkv"], a["ctx"], a["lse"], self.cu,
+                                     self.n_seqs, ctx_amax_parts=r8[r]["ctx"]["amax"])
         with T("quant"):
             self._quant_split("ctx", {r: self.a[r]["ctx"] for r in self.ranks}, E4, ext,
-                              amax_written=True)
+                              amax_written=self.cp == 1)
         wait_w("wo")
         for r in self.ranks:
             c = r8[r]
@@ -666,12 +670,16 @@ class TPLayer(_Probed):
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
                                            None, None, self.rgrads["dbo"], 0, wss, wsb)
             with T("attn_bwd"):
-                mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"], self.cu,
-                                 self.n_seqs, ws, wsb, dqkv_amax_parts=c["dqkv"]["amax"])
+                if self.cp > 1:
+                    self._attn_bwd_cp(d, a, ws, wsb)
+                else:
+                    mtp.mtp_attn_bwd(d, a["qkv"], a["ctx"], a["lse"], a["dctx"], a["dqkv"],
+                                     self.cu, self.n_seqs, ws, wsb,
+                                     dqkv_amax_parts=c["dqkv"]["amax"])
         # QKV: dln1_r = dqkv_r Wqkv_r; dWqkv_r = dqkv_r^T ln1
         with T("quant"):
             self._quant_split("dqkv", {r: self.a[r]["dqkv"] for r in self.ranks}, E5, ext,
-                              amax_written=True)
+                              amax_written=self.cp == 1)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
