@@ -121,6 +121,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         swiglu=True, fp8=True,
         description="7B-style layer with a SwiGLU FFN, one TP=2 rank shard, its twelve GEMMs on "
                     "FP8 codes (gate and up under one scale), bf16 elsewhere"),
+    "7b_tp2_sp_fp8": LayerConfig(
+        "7b_tp2_sp_fp8", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
+        sequence_parallel=True, fp8=True,
+        description="7B-style layer, one TP=2 rank shard with sequence parallelism, its twelve "
+                    "GEMMs on FP8 codes, bf16 elsewhere"),
     "7b_tp2_cp2_fp8": LayerConfig(
         "7b_tp2_cp2_fp8", hidden=4096, heads=32, ffn=11008, tp=2, seq_len=2048, dtype="bf16",
         context_parallel=2, fp8=True,
@@ -215,6 +220,14 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_fp8_varlen_d64_cp3": LayerConfig(
         "small_fp8_varlen_d64_cp3", hidden=512, heads=8, ffn=1376, tp=2, seq_len=624,
         dtype="bf16", varlen_tokens=624, doc_min=1, doc_max=300, fp8=True, context_parallel=3),
+    # the FP8 step with sequence parallelism (LayerNorm and the sums on row
+    # blocks of 152 and 52 tokens)
+    "small_fp8_tp2_sp": LayerConfig(
+        "small_fp8_tp2_sp", hidden=512, heads=4, ffn=1376, tp=2, seq_len=304, dtype="bf16",
+        affine_random=True, sequence_parallel=True, fp8=True),
+    "small_fp8_swiglu_sp_tp4": LayerConfig(
+        "small_fp8_swiglu_sp_tp4", hidden=512, heads=8, ffn=2176, tp=4, seq_len=208,
+        dtype="bf16", swiglu=True, sequence_parallel=True, fp8=True),
     "one_token_bf16": LayerConfig(
         "one_token_bf16", hidden=256, heads=2, ffn=512, tp=2, seq_len=1, dtype="bf16"),
 }

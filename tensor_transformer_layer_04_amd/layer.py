@@ -50,7 +50,11 @@ computed here contribute their amax parts through ``external``.  With the
 SwiGLU FFN the gate and up rows of W1|W3 are one tensor under one scale, and
 so are their output gradients [du | du3], both in the interleaved order the
 bf16 step uses.  With context-parallel attention, ctx and dqkv come out of
-the chunks' block pairs and merges and take the amax pass.
+the chunks' block pairs and merges and take the amax pass.  With sequence
+parallelism, ln1, ln2 and dy1 are written rank by rank on their row blocks;
+each block's kernel writes amax parts of its own and the whole tensor is
+scaled by the maximum over all blocks' parts (the other ranks' through
+``external``).
 """
 from __future__ import annotations
 
@@ -223,8 +227,8 @@ class TPLayer(_Probed):
                           for r in range(cfg.tp)}
         self.fp8 = bool(getattr(cfg, "fp8", False))
         if self.fp8:
-            if cfg.dtype != "bf16" or self.sp:
-                raise ValueError("the FP8 step needs a bf16 layer without sequence parallelism")
+            if cfg.dtype != "bf16":
+                raise ValueError("the FP8 step needs a bf16 layer")
             if self.T % 16:
                 raise ValueError(f"the FP8 step needs T ({self.T}) divisible by 16")
         self._alloc()
@@ -300,6 +304,11 @@ class TPLayer(_Probed):
         shapes = {"ctx": (T, hl), "g": (T, fl), "du": (T, ul), "dqkv": (T, 3 * hl),
                   "wqkv": (3 * hl, h), "wo": (h, hl), "w1": (ul, h), "w2": (h, fl)}
         self.r8 = {r: {k: slot(*sh) for k, sh in shapes.items()} for r in self.ranks}
+        # sequence parallelism: ln1, ln2 and dy1 are written rank by rank on
+        # their row blocks, each block with amax parts of its own
+        if self.sp:
+            self.p8 = {k: {r: torch.zeros(mtp.FP8_AMAX_PARTS, dtype=torch.float32, device=dev)
+                           for r in self.ranks} for k in ("ln1", "ln2", "dy1")}
 
     def _quant_shared(self, name, x, fmt, amax_written=False):
         """amax and codes of a tensor every rank holds whole (amax_written:
@@ -309,6 +318,15 @@ class TPLayer(_Probed):
             mtp.mtp_fp8_amax(self.d0, x, x.numel(), sl["amax"])
         mtp.mtp_fp8_quantize(self.d0, fmt, x, sl["rows"], sl["cols"], [sl["amax"]], sl["q"],
                              sl["qt"], sl["s"])
+
+    def _quant_rows(self, name, x, fmt, ext):
+        """Codes of a tensor that every rank holds whole but whose row blocks
+        the ranks produced (sequence parallelism), scaled by the maximum over
+        the blocks' amax parts (this layer's ranks and ``ext``'s)."""
+        sl = self.q8[name]
+        parts = [self.p8[name][r] for r in self.ranks] + list(ext.get("fp8_" + name, []))
+        mtp.mtp_fp8_quantize(self.d0, fmt, x, sl["rows"], sl["cols"], parts, sl["q"], sl["qt"],
+                             sl["s"])
 
     def _quant_split(self, name, xs, fmt, ext, amax_written=False):
         """amax of every computed rank's shard xs[r], then its codes with the
@@ -528,9 +546,16 @@ class TPLayer(_Probed):
         ready = {}
         if side is not None:
             side.wait_stream(torch.cuda.current_stream(self.device))
-        with T("ln1"):
-            mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1,
-                              amax_parts=q8["ln1"]["amax"])
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln1"):
+                    mtp.mtp_layernorm(self.rdesc[r], x[s], rep["ln1_g"], rep["ln1_b"], self.ln1[s],
+                                      self.mu1[s], self.rs1[s], amax_parts=self.p8["ln1"][r])
+        else:
+            with T("ln1"):
+                mtp.mtp_layernorm(d0, x, rep["ln1_g"], rep["ln1_b"], self.ln1, self.mu1, self.rs1,
+                                  amax_parts=q8["ln1"]["amax"])
         for name in ("wqkv", "wo", "w1", "w2"):
             with (torch.cuda.stream(side) if side is not None else contextlib.nullcontext()), \
                     T("quant_w", side):
@@ -543,7 +568,10 @@ class TPLayer(_Probed):
             if name in ready:
                 torch.cuda.current_stream(self.device).wait_event(ready[name])
         with T("quant"):
-            self._quant_shared("ln1", self.ln1, E4, amax_written=True)
+            if self.sp:
+                self._quant_rows("ln1", self.ln1, E4, ext)
+            else:
+                self._quant_shared("ln1", self.ln1, E4, amax_written=True)
         wait_w("wqkv")
         for r in self.ranks:
             d, w, a, c = self.descs[r], self.w[r], self.a[r], r8[r]
@@ -569,12 +597,23 @@ class TPLayer(_Probed):
                 mtp.mtp_linear_fwd_fp8(self.descs[r], mtp.MTP_PROJ, c["ctx"]["q"], c["ctx"]["s"],
                                        c["wo"]["q"], c["wo"]["s"], None, self.a[r]["p"], None)
         parts = [self.a[r]["p"] for r in self.ranks] + list(ext.get("proj", []))
-        with T("sum_proj_ln2"):
-            mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
-                                          rep["ln2_b"], self.ln2, self.mu2, self.rs2,
-                                          amax_parts=q8["ln2"]["amax"])
-        with T("quant"):
-            self._quant_shared("ln2", self.ln2, E4, amax_written=True)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("sum_proj_ln2"):
+                    mtp.mtp_partial_sum_layernorm(self.rdesc[r], [q[s] for q in parts], rep["bo"],
+                                                  x[s], self.y1[s], rep["ln2_g"], rep["ln2_b"],
+                                                  self.ln2[s], self.mu2[s], self.rs2[s],
+                                                  amax_parts=self.p8["ln2"][r])
+            with T("quant"):
+                self._quant_rows("ln2", self.ln2, E4, ext)
+        else:
+            with T("sum_proj_ln2"):
+                mtp.mtp_partial_sum_layernorm(d0, parts, rep["bo"], x, self.y1, rep["ln2_g"],
+                                              rep["ln2_b"], self.ln2, self.mu2, self.rs2,
+                                              amax_parts=q8["ln2"]["amax"])
+            with T("quant"):
+                self._quant_shared("ln2", self.ln2, E4, amax_written=True)
         wait_w("w1")
         for r in self.ranks:
             w, a, c = self.w[r], self.a[r], r8[r]
@@ -592,8 +631,15 @@ class TPLayer(_Probed):
                 mtp.mtp_linear_fwd_fp8(self.descs[r], self.k_fc2, c["g"]["q"], c["g"]["s"],
                                        c["w2"]["q"], c["w2"]["s"], None, self.a[r]["q"], None)
         parts = [self.a[r]["q"] for r in self.ranks] + list(ext.get("fc2", []))
-        with T("sum_fc2"):
-            mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("sum_fc2"):
+                    mtp.mtp_partial_sum(self.rdesc[r], [q[s] for q in parts], rep["b2"],
+                                        self.y1[s], self.y[s])
+        else:
+            with T("sum_fc2"):
+                mtp.mtp_partial_sum(d0, parts, rep["b2"], self.y1, self.y)
         return self.y
 
     def _backward_fp8(self, dy, ext):
@@ -626,7 +672,14 @@ class TPLayer(_Probed):
             with on_side(), T("fc2_wgrad", side):
                 mtp.mtp_linear_bwd_fp8(d, self.k_fc2, None, q8["dy"]["qt"], q8["dy"]["s"], None,
                                        None, c["g"]["qt"], c["g"]["s"], None, None, g["dw2"])
-            if r == self.owns_bias:
+            if self.sp:
+                # row-parallel bias: this rank's column sums of dy over its rows
+                s = self.rows[r]
+                with on_side(), T("fc2_bias", side):
+                    mtp.mtp_row_linear_bwd(self.rdesc[r], mtp.MTP_FC2, dy[s], a["g"][s], w["w2"],
+                                           None, None, None, self.rgrads["db2"],
+                                           int(r != self.ranks[0]), wss, wsb)
+            elif r == self.owns_bias:
                 with on_side(), T("fc2_bias", side):
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_FC2, dy, a["g"], w["w2"], None, None, None,
                                            self.rgrads["db2"], 0, wss, wsb)
@@ -648,13 +701,27 @@ class TPLayer(_Probed):
                                        c["w1"]["qt"], c["w1"]["s"], None, None, None, a["dln2"],
                                        None)
         parts = [self.a[r]["dln2"] for r in self.ranks] + list(ext.get("fc1_dx", []))
-        with T("ln2_bwd"):
-            mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2, dy,
-                                      self.dy1, self.rgrads["dln2_g"], self.rgrads["dln2_b"], 0,
-                                      ws, wsb, amax_parts=q8["dy1"]["amax"])
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln2_bwd"):
+                    mtp.mtp_layernorm_bwd_sum(self.rdesc[r], [q[s] for q in parts], self.y1[s],
+                                              rep["ln2_g"], self.mu2[s], self.rs2[s], dy[s],
+                                              self.dy1[s], self.rgrads["dln2_g"],
+                                              self.rgrads["dln2_b"], int(r != self.ranks[0]), ws,
+                                              wsb, amax_parts=self.p8["dy1"][r])
+        else:
+            with T("ln2_bwd"):
+                mtp.mtp_layernorm_bwd_sum(d0, parts, self.y1, rep["ln2_g"], self.mu2, self.rs2,
+                                          dy, self.dy1, self.rgrads["dln2_g"],
+                                          self.rgrads["dln2_b"], 0, ws, wsb,
+                                          amax_parts=q8["dy1"]["amax"])
         # PROJ: dctx_r = dy1 Wo_r; dWo_r = dy1^T ctx_r; then attention
         with T("quant"):
-            self._quant_shared("dy1", self.dy1, E5, amax_written=True)
+            if self.sp:
+                self._quant_rows("dy1", self.dy1, E5, ext)
+            else:
+                self._quant_shared("dy1", self.dy1, E5, amax_written=True)
         fork()
         for r in self.ranks:
             d, w, a, g, c = self.descs[r], self.w[r], self.a[r], self.grads[r], r8[r]
@@ -666,7 +733,12 @@ class TPLayer(_Probed):
                 mtp.mtp_linear_bwd_fp8(d, mtp.MTP_PROJ, None, q8["dy1"]["qt"], q8["dy1"]["s"],
                                        None, None, c["ctx"]["qt"], c["ctx"]["s"], None, None,
                                        g["dwo"])
-                if r == self.owns_bias:
+                if self.sp:
+                    s = self.rows[r]
+                    mtp.mtp_row_linear_bwd(self.rdesc[r], mtp.MTP_PROJ, self.dy1[s], a["ctx"][s],
+                                           w["wo"], None, None, None, self.rgrads["dbo"],
+                                           int(r != self.ranks[0]), wss, wsb)
+                elif r == self.owns_bias:
                     mtp.mtp_row_linear_bwd(d, mtp.MTP_PROJ, self.dy1, a["ctx"], w["wo"], None,
                                            None, None, self.rgrads["dbo"], 0, wss, wsb)
             with T("attn_bwd"):
@@ -692,10 +764,20 @@ class TPLayer(_Probed):
                                        None, None, q8["ln1"]["qt"], q8["ln1"]["s"], None, None,
                                        g["dwqkv"])
         parts = [self.a[r]["dln1"] for r in self.ranks] + list(ext.get("qkv_dx", []))
-        with T("ln1_bwd"):
-            mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
-                                      self.dy1, self.dx, self.rgrads["dln1_g"],
-                                      self.rgrads["dln1_b"], 0, ws, wsb)
+        if self.sp:
+            for r in self.ranks:
+                s = self.rows[r]
+                with T("ln1_bwd"):
+                    mtp.mtp_layernorm_bwd_sum(self.rdesc[r], [q[s] for q in parts], self.x[s],
+                                              rep["ln1_g"], self.mu1[s], self.rs1[s], self.dy1[s],
+                                              self.dx[s], self.rgrads["dln1_g"],
+                                              self.rgrads["dln1_b"], int(r != self.ranks[0]), ws,
+                                              wsb)
+        else:
+            with T("ln1_bwd"):
+                mtp.mtp_layernorm_bwd_sum(d0, parts, self.x, rep["ln1_g"], self.mu1, self.rs1,
+                                          self.dy1, self.dx, self.rgrads["dln1_g"],
+                                          self.rgrads["dln1_b"], 0, ws, wsb)
         self._qkv_bias_grad()
         if side is not None:
             main.wait_stream(side)
@@ -749,6 +831,9 @@ class TPLayer(_Probed):
         if self.fp8:  # the amax parts of the tensors split over the ranks
             for k in ("ctx", "g", "du", "dqkv", "wqkv", "wo", "w1", "w2"):
                 out["fp8_" + k] = [self.r8[r][k]["amax"].clone() for r in self.ranks]
+            if self.sp:  # and of the row blocks each rank wrote
+                for k in ("ln1", "ln2", "dy1"):
+                    out["fp8_" + k] = [self.p8[k][r].clone() for r in self.ranks]
         return out
 
 

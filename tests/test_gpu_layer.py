@@ -279,13 +279,16 @@ def test_sequence_parallel_matches_replicated(name):
         assert err <= 1e-5, f"{name}: {k} rel diff {err}"
 
 
-def test_sequence_parallel_one_rank_with_resident_rows():
+@pytest.mark.parametrize("name", ["small_bf16_tp2_sp", "small_fp8_tp2_sp"])
+def test_sequence_parallel_one_rank_with_resident_rows(name):
     """The timed shard of the sequence-parallel workload: rank 0 alone, the
     other rank's partials and row blocks resident from a full run, gives
-    rank 0's rows of every row-wise output bit-identically."""
+    rank 0's rows of every row-wise output bit-identically (FP8: and the
+    codes of the row-block tensors, whose scale takes the other rank's amax
+    parts through the external partials)."""
     require_gpu()
     from tensor_transformer_layer_04_amd.layer import TPLayer
-    cfg = synth.get_config("small_bf16_tp2_sp")
+    cfg = synth.get_config(name)
     data = synth.generate(cfg)
     full = run_gpu_layer(cfg, data)
     ref = {k: getattr(full, k).clone() for k in ("y1", "y", "dy1", "dx", "ln1", "ln2")}
@@ -302,13 +305,19 @@ def test_sequence_parallel_one_rank_with_resident_rows():
     torch.cuda.synchronize()
     for k, v in ref.items():
         assert torch.equal(getattr(L, k)[rows], v[rows]), f"rank-0 rows of {k} differ"
+    if cfg.fp8:
+        for k in ("ln1", "ln2", "dy1"):
+            assert torch.equal(L.q8[k]["s"][:1], full.q8[k]["s"][:1]), f"scale of {k} differs"
+            assert torch.equal(L.q8[k]["q"], full.q8[k]["q"]), f"codes of {k} differ"
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["small_fp8_tp2", "small_fp8_d64_tp4", "small_fp8_varlen_tp2",
                                   "small_fp8_swiglu_tp2", "small_fp8_swiglu_d64_tp4",
                                   "small_fp8_tp2_cp2", "small_fp8_varlen_d64_cp3",
-                                  "7b_tp2_fp8", "7b_tp2_swiglu_fp8", "7b_tp2_cp2_fp8"])
+                                  "small_fp8_tp2_sp", "small_fp8_swiglu_sp_tp4",
+                                  "7b_tp2_fp8", "7b_tp2_swiglu_fp8", "7b_tp2_cp2_fp8",
+                                  "7b_tp2_sp_fp8"])
 def test_layer_fp8_parity(name):
     """The FP8 layer step (twelve GEMMs on FP8 codes, whole-tensor scales
     shared by the ranks), all ranks, forward and backward: (a) every code and
