@@ -315,7 +315,7 @@ def test_sequence_parallel_one_rank_with_resident_rows(name):
 @pytest.mark.parametrize("name", ["small_fp8_tp2", "small_fp8_d64_tp4", "small_fp8_varlen_tp2",
                                   "small_fp8_swiglu_tp2", "small_fp8_swiglu_d64_tp4",
                                   "small_fp8_tp2_cp2", "small_fp8_varlen_d64_cp3",
-                                  "small_fp8_tp2_sp", "small_fp8_swiglu_sp_tp4",
+                                  "small_fp8_tp2_sp", "small_fp8_swiglu_sp_tp4", "small_fp8_mb2",
                                   "7b_tp2_fp8", "7b_tp2_swiglu_fp8", "7b_tp2_cp2_fp8",
                                   "7b_tp2_sp_fp8"])
 def test_layer_fp8_parity(name):
