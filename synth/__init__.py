@@ -135,6 +135,11 @@ CONFIGS: Dict[str, LayerConfig] = {
         "varlen_tp1", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096,
         description="packed variable-length batch, TP=1, bf16"),
+    "varlen_tp1_fp8": LayerConfig(
+        "varlen_tp1_fp8", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
+        varlen_tokens=16384, doc_min=256, doc_max=4096, fp8=True,
+        description="packed variable-length batch, TP=1, its twelve GEMMs on FP8 codes, bf16 "
+                    "elsewhere"),
     "varlen_tp1_cp4": LayerConfig(
         "varlen_tp1_cp4", hidden=4096, heads=32, ffn=11008, tp=1, seq_len=16384, dtype="bf16",
         varlen_tokens=16384, doc_min=256, doc_max=4096, context_parallel=4,

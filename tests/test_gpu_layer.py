@@ -317,7 +317,7 @@ def test_sequence_parallel_one_rank_with_resident_rows(name):
                                   "small_fp8_tp2_cp2", "small_fp8_varlen_d64_cp3",
                                   "small_fp8_tp2_sp", "small_fp8_swiglu_sp_tp4", "small_fp8_mb2",
                                   "7b_tp2_fp8", "7b_tp2_swiglu_fp8", "7b_tp2_cp2_fp8",
-                                  "7b_tp2_sp_fp8"])
+                                  "7b_tp2_sp_fp8", "varlen_tp1_fp8"])
 def test_layer_fp8_parity(name):
     """The FP8 layer step (twelve GEMMs on FP8 codes, whole-tensor scales
     shared by the ranks), all ranks, forward and backward: (a) every code and
