@@ -311,6 +311,15 @@ def test_sequence_parallel_one_rank_with_resident_rows(name):
             assert torch.equal(L.q8[k]["q"], full.q8[k]["q"]), f"codes of {k} differ"
 
 
+# The 16384-token packed batch is checked component by component only:
+# every code and scale bit for bit (which covers the amax passes that stand
+# in for the producing kernels' parts once a grid has more workgroups than
+# parts) and every product against the oracle's product of the same codes.
+# The oracle's whole layer at that length takes about 90 s on the host; the
+# end-to-end comparison runs at the other sizes.
+FP8_COMPONENTS_ONLY = {"varlen_tp1_fp8"}
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["small_fp8_tp2", "small_fp8_d64_tp4", "small_fp8_varlen_tp2",
                                   "small_fp8_swiglu_tp2", "small_fp8_swiglu_d64_tp4",
@@ -323,7 +332,8 @@ def test_layer_fp8_parity(name):
     shared by the ranks), all ranks, forward and backward: (a) every code and
     scale bit for bit and (b) every FP8 product at the bf16 tolerance, both
     against the oracle applied to the GPU's own tensors; (c) every per-rank
-    and summed tensor against the oracle's FP8 layer end to end."""
+    and summed tensor against the oracle's FP8 layer end to end (not for
+    FP8_COMPONENTS_ONLY)."""
     require_gpu()
     cfg = synth.get_config(name)
     log(f"FP8 layer parity {name}: T={cfg.tokens} h={cfg.hidden} tp={cfg.tp}")
@@ -333,6 +343,8 @@ def test_layer_fp8_parity(name):
     report = {}
     compare_fp8_components(cfg, L, report)
     log(f"  components worst: {fmt_report(report)}")
+    if name in FP8_COMPONENTS_ONLY:
+        return
     starts = oracle.doc_starts(data["cu_seqlens"], cfg.tokens)
     c = oracle.layer_forward(data, data["x"], cfg.heads, cfg.eps, starts, fp8=True)
     g = oracle.layer_backward(data, c, data["dy"], cfg.heads, starts)
