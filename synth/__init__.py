@@ -225,6 +225,11 @@ PARITY_CASES: Dict[str, LayerConfig] = {
     "small_fp8_varlen_d64_cp3": LayerConfig(
         "small_fp8_varlen_d64_cp3", hidden=512, heads=8, ffn=1376, tp=2, seq_len=624,
         dtype="bf16", varlen_tokens=624, doc_min=1, doc_max=300, fp8=True, context_parallel=3),
+    # the FP8 step over eight tensor-parallel shards (every split tensor's
+    # scale merges eight ranks' amax parts)
+    "small_fp8_tp8": LayerConfig(
+        "small_fp8_tp8", hidden=1024, heads=8, ffn=4096, tp=8, seq_len=208, dtype="bf16",
+        affine_random=True, fp8=True),
     # the FP8 step over two micro-batch sequences of 136 tokens (T = 272)
     "small_fp8_mb2": LayerConfig(
         "small_fp8_mb2", hidden=256, heads=2, ffn=768, tp=2, seq_len=136, micro_batch=2,

@@ -325,6 +325,7 @@ FP8_COMPONENTS_ONLY = {"varlen_tp1_fp8"}
                                   "small_fp8_swiglu_tp2", "small_fp8_swiglu_d64_tp4",
                                   "small_fp8_tp2_cp2", "small_fp8_varlen_d64_cp3",
                                   "small_fp8_tp2_sp", "small_fp8_swiglu_sp_tp4", "small_fp8_mb2",
+                                  "small_fp8_tp8",
                                   "7b_tp2_fp8", "7b_tp2_swiglu_fp8", "7b_tp2_cp2_fp8",
                                   "7b_tp2_sp_fp8", "varlen_tp1_fp8"])
 def test_layer_fp8_parity(name):
